@@ -1,0 +1,378 @@
+"""Pins for the fp64 oracle: checks against what the definition and the
+mathematics fix, never against the oracle itself.
+
+Each pin is a function of an ``oracle.Oracle`` instance that raises
+AssertionError when the oracle is wrong. ``test_oracle_pins.py`` runs them on
+the real oracle; ``test_oracle_mutants.py`` runs them on oracle builds with a
+planted mistake and requires that some pin fails for every mistake.
+
+The pages print no worked numeric example (no tensor, output or LSE value),
+so the pins are: bit-level agreement of the storage-format routines with
+torch/numpy, RoPE invariants (position 0 is the identity, pair norms are
+kept, dot products depend only on the position difference, rotations
+compose), an independent complex-number form of RoPE, a D = 2 closed form,
+explicit N x N brute force and torch's fp64 scaled_dot_product_attention for
+attention, and special cases with closed forms (row 0 returns v_0, zero
+queries average the visible values, softmax rows sum to one).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.special
+import torch
+
+RNG_SEED = 1234
+
+
+def _rng(*key):
+    return np.random.default_rng(np.random.SeedSequence([RNG_SEED, *key]))
+
+
+# --------------------------------------------------------------------------
+# storage formats
+# --------------------------------------------------------------------------
+
+def pin_decode_bf16_all_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_decode_fp16_all_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode(bits, "fp16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _wide_fp32_sample(rng, n):
+    mant = rng.uniform(1.0, 2.0, n)
+    expo = rng.integers(-140, 128, n)
+    sign = rng.choice([-1.0, 1.0], n)
+    x = (sign * np.ldexp(mant, expo)).astype(np.float32)
+    # exact ties: one bit past the bf16 grid, for both parities of the last kept bit
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3 * 2 ** -9 + 2 ** -16,
+                     2 ** -130 + 2 ** -134], dtype=np.float32)
+    return np.concatenate([x, ties, np.array([0.0, -0.0, np.inf, -np.inf], np.float32)])
+
+
+def pin_encode_bf16_matches_torch(orc):
+    x = _wide_fp32_sample(_rng(1), 200000)
+    got = orc.encode(x.astype(np.float64), "bf16")
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def pin_encode_fp16_matches_numpy(orc):
+    rng = _rng(2)
+    n = 200000
+    x = rng.uniform(1.0, 2.0, n) * np.exp2(rng.integers(-27, 18, n)) * rng.choice([-1, 1], n)
+    ties = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 65504.0, 65519.99, 65520.0, 2 ** -25,
+                     3 * 2 ** -26, 2 ** -24 * 1.5, 2 ** -14 - 2 ** -25, 0.0, -0.0])
+    x = np.concatenate([x, ties, -ties])
+    got = orc.encode(x, "fp16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def pin_encode_decode_roundtrip(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt in ("bf16", "fp16"):
+        vals = orc.decode(bits, dt)
+        keep = ~np.isnan(vals)
+        assert np.array_equal(orc.encode(vals[keep], dt), bits[keep])
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+
+def _rope_complex(x, pos, base):
+    """RoPE written as complex multiplication: pair (x_2i, x_2i+1) is the
+    complex number x_2i + 1j*x_2i+1, multiplied by exp(1j * p * base**(-2i/D))."""
+    D = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    freq = np.power(float(base), -np.arange(0, D, 2, dtype=np.float64) / D)
+    z = z * np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * freq)
+    out = np.empty_like(x)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def pin_rope_position_zero_identity(orc):
+    x = _rng(3).standard_normal((7, 128))
+    assert np.array_equal(orc.rope(x, np.zeros(7, np.int64), 500000.0), x)
+
+
+def pin_rope_preserves_pair_norms(orc):
+    rng = _rng(4)
+    x = rng.standard_normal((64, 128))
+    pos = rng.integers(0, 32768, 64)
+    y = orc.rope(x, pos, 10000.0)
+    nx = np.hypot(x[:, 0::2], x[:, 1::2])
+    ny = np.hypot(y[:, 0::2], y[:, 1::2])
+    assert np.max(np.abs(ny - nx) / nx) < 1e-14
+
+
+def pin_rope_complex_form(orc):
+    rng = _rng(5)
+    for D in (2, 8, 64, 128):
+        for base in (10000.0, 500000.0):
+            x = rng.standard_normal((50, D))
+            pos = np.concatenate([np.arange(10), rng.integers(0, 32768, 40)])
+            got = orc.rope(x, pos, base)
+            ref = _rope_complex(x, pos, base)
+            assert np.max(np.abs(got - ref)) < 1e-10, (D, base)
+
+
+def pin_rope_d2_rotates_by_position_radians(orc):
+    # D = 2: the only frequency is base**0 = 1, so position p turns the pair by
+    # p radians, counter-clockwise, whatever the base.
+    pos = np.arange(0, 40, dtype=np.int64)
+    x = np.tile(np.array([[1.0, 0.0]]), (40, 1))
+    for base in (10000.0, 3.0):
+        y = orc.rope(x, pos, base)
+        assert np.allclose(y[:, 0], np.cos(pos), atol=1e-15, rtol=0)
+        assert np.allclose(y[:, 1], np.sin(pos), atol=1e-15, rtol=0)
+
+
+def pin_rope_first_and_last_frequency(orc):
+    # unit vector on pair i at position 1 turns by exactly theta_i: theta_0 = 1
+    # and theta_{D/2-1} = base**(-(D-2)/D).
+    D, base = 64, 10000.0
+    x = np.zeros((2, D))
+    x[0, 0] = 1.0
+    x[1, D - 2] = 1.0
+    y = orc.rope(x, np.array([1, 1]), base)
+    assert abs(math.atan2(y[0, 1], y[0, 0]) - 1.0) < 1e-15
+    assert abs(math.atan2(y[1, D - 1], y[1, D - 2]) - base ** (-(D - 2) / D)) < 1e-15
+
+
+def pin_rope_pairs_are_adjacent(orc):
+    # a unit vector on coordinate c only ever mixes with its partner c ^ 1
+    D = 16
+    x = np.eye(D)
+    y = orc.rope(x, np.full(D, 5), 100.0)
+    for c in range(D):
+        support = set(np.nonzero(np.abs(y[c]) > 1e-300)[0].tolist())
+        assert support <= {c, c ^ 1}, (c, support)
+        assert len(support) == 2
+
+
+def pin_rope_shift_invariance(orc):
+    # (R(m) q) . (R(n) k) depends only on m - n
+    rng = _rng(6)
+    for D, base in ((64, 10000.0), (128, 500000.0)):
+        q = rng.standard_normal((30, D))
+        k = rng.standard_normal((30, D))
+        m = rng.integers(0, 16384, 30)
+        n = rng.integers(0, 16384, 30)
+        t = rng.integers(0, 16384, 30)
+        d0 = np.sum(orc.rope(q, m, base) * orc.rope(k, n, base), axis=1)
+        d1 = np.sum(orc.rope(q, m + t, base) * orc.rope(k, n + t, base), axis=1)
+        scale = np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1)
+        assert np.max(np.abs(d0 - d1) / scale) < 1e-11
+
+
+def pin_rope_composition(orc):
+    rng = _rng(7)
+    x = rng.standard_normal((40, 64))
+    a = rng.integers(0, 16384, 40)
+    b = rng.integers(0, 16384, 40)
+    y = orc.rope(orc.rope(x, a, 10000.0), b, 10000.0)
+    z = orc.rope(x, a + b, 10000.0)
+    assert np.max(np.abs(y - z)) < 1e-10
+
+
+# --------------------------------------------------------------------------
+# causal attention
+# --------------------------------------------------------------------------
+
+def _brute_attention(q, k, v):
+    """Explicit N x N score matrix, -inf above the diagonal, scipy softmax."""
+    B, Hq, N, D = q.shape
+    rep = Hq // k.shape[1]
+    kk = np.repeat(k, rep, axis=1)
+    vv = np.repeat(v, rep, axis=1)
+    S = np.matmul(q, np.swapaxes(kk, -1, -2)) / np.sqrt(D)
+    S[..., np.triu(np.ones((N, N), dtype=bool), 1)] = -np.inf
+    lse = scipy.special.logsumexp(S, axis=-1)
+    P = scipy.special.softmax(S, axis=-1)
+    return np.matmul(P, vv), lse
+
+
+def _qkv(rng, B, Hq, Hkv, N, D, sigma=1.0):
+    return (sigma * rng.standard_normal((B, Hq, N, D)), sigma * rng.standard_normal((B, Hkv, N, D)),
+            rng.standard_normal((B, Hkv, N, D)))
+
+
+def pin_attention_bruteforce(orc):
+    rng = _rng(8)
+    for (B, Hq, Hkv, N, D) in ((1, 1, 1, 1, 2), (1, 2, 2, 5, 8), (2, 4, 1, 17, 16),
+                               (1, 8, 2, 64, 64), (1, 6, 3, 33, 128)):
+        q, k, v = _qkv(rng, B, Hq, Hkv, N, D, sigma=2.0)
+        o, lse = orc.attention(q, k, v)
+        ro, rlse = _brute_attention(q, k, v)
+        assert np.max(np.abs(o - ro)) < 1e-12
+        assert np.max(np.abs(lse - rlse)) < 1e-12
+
+
+def pin_attention_torch_sdpa(orc):
+    rng = _rng(9)
+    B, Hq, Hkv, N, D = 2, 8, 2, 48, 32
+    q, k, v = _qkv(rng, B, Hq, Hkv, N, D)
+    o, _ = orc.attention(q, k, v)
+    rep = Hq // Hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(rep, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(rep, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy()
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def pin_attention_row0_is_v0(orc):
+    rng = _rng(10)
+    q, k, v = _qkv(rng, 1, 4, 2, 9, 64, sigma=3.0)
+    o, lse = orc.attention(q, k, v)
+    for h in range(4):
+        g = h // 2
+        assert np.array_equal(o[0, h, 0], v[0, g, 0])
+        s00 = float(np.dot(q[0, h, 0], k[0, g, 0])) / 8.0
+        assert abs(lse[0, h, 0] - s00) < 1e-13 * max(1.0, abs(s00))
+
+
+def pin_attention_zero_query_mean(orc):
+    rng = _rng(11)
+    B, H, N, D = 1, 2, 40, 16
+    q = np.zeros((B, H, N, D))
+    _, k, v = _qkv(rng, B, H, H, N, D)
+    o, lse = orc.attention(q, k, v)
+    mean = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.max(np.abs(o - mean)) < 1e-14
+    assert np.max(np.abs(lse - np.log(np.arange(1, N + 1))[None, None, :])) < 1e-14
+
+
+def pin_attention_probabilities(orc):
+    # with v_j = e_j the output row i is the probability row P_i.
+    rng = _rng(12)
+    N, D = 24, 32
+    q = 2.0 * rng.standard_normal((1, 1, N, D))
+    k = 2.0 * rng.standard_normal((1, 1, N, D))
+    v = np.zeros((1, 1, N, D))
+    v[0, 0, np.arange(N), np.arange(N)] = 1.0
+    o, lse = orc.attention(q, k, v)
+    P = o[0, 0, :, :N]
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) < 1e-14
+    assert np.all(P[np.triu(np.ones((N, N), dtype=bool), 1)] == 0.0)
+    assert np.all(P[np.tril(np.ones((N, N), dtype=bool))] > 0.0)
+    S = (q[0, 0] @ k[0, 0].T) / np.sqrt(D)
+    for i in range(N):
+        # log P_ij = s_ij - L_i on the visible keys
+        assert np.max(np.abs(np.log(P[i, :i + 1]) - (S[i, :i + 1] - lse[0, 0, i]))) < 1e-12
+
+
+def pin_attention_prefix_invariance(orc):
+    rng = _rng(13)
+    q, k, v = _qkv(rng, 1, 4, 4, 50, 16)
+    o, lse = orc.attention(q, k, v)
+    n2 = 21
+    o2, lse2 = orc.attention(q[:, :, :n2], k[:, :, :n2], v[:, :, :n2])
+    assert np.array_equal(o[:, :, :n2], o2)
+    assert np.array_equal(lse[:, :, :n2], lse2)
+
+
+def pin_attention_gqa_equals_repeated_mha(orc):
+    rng = _rng(14)
+    q, k, v = _qkv(rng, 2, 8, 2, 20, 16)
+    o, lse = orc.attention(q, k, v)
+    o2, lse2 = orc.attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1))
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def pin_attention_rows_subset(orc):
+    rng = _rng(15)
+    q, k, v = _qkv(rng, 2, 4, 2, 30, 16)
+    o, lse = orc.attention(q, k, v)
+    rows = rng.choice(2 * 4 * 30, 37, replace=False)
+    o2, lse2 = orc.attention(q, k, v, rows=rows)
+    assert np.array_equal(o.reshape(-1, 16)[rows], o2)
+    assert np.array_equal(lse.reshape(-1)[rows], lse2)
+
+
+def pin_attention_large_sigma_finite(orc):
+    rng = _rng(16)
+    q, k, v = _qkv(rng, 1, 2, 2, 64, 64, sigma=8.0)
+    o, lse = orc.attention(q, k, v)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    # each output row is a convex combination of the visible values
+    vmax = np.maximum.accumulate(np.max(np.abs(v), axis=-1), axis=-1)
+    assert np.all(np.max(np.abs(o), axis=-1) <= vmax + 1e-12)
+
+
+# --------------------------------------------------------------------------
+# RoPE then attention
+# --------------------------------------------------------------------------
+
+def pin_rope_attention_relative_position(orc):
+    # rotating every query and key by position + t leaves attention unchanged
+    rng = _rng(17)
+    B, Hq, Hkv, N, D = 1, 4, 2, 32, 64
+    q, k, v = _qkv(rng, B, Hq, Hkv, N, D)
+    pos = np.arange(N)
+    o1, l1 = orc.attention(orc.rope(q, pos, 10000.0), orc.rope(k, pos, 10000.0), v)
+    o2, l2 = orc.attention(orc.rope(q, pos + 9000, 10000.0), orc.rope(k, pos + 9000, 10000.0), v)
+    assert np.max(np.abs(o1 - o2)) < 1e-10 and np.max(np.abs(l1 - l2)) < 1e-10
+
+
+def pin_rope_attention_closed_form_d2(orc):
+    # D = 2, every q and k equal to (1, 0): after RoPE q_i = (cos i, sin i) and
+    # k_j = (cos j, sin j), so s_ij = cos(i - j) / sqrt(2); v_j = (j, 1).
+    N = 5
+    one = np.array([[1.0, 0.0]] * N)
+    bits = orc.encode(one, "bf16")[None, None]
+    v = np.stack([np.arange(N, dtype=np.float64), np.ones(N)], axis=1)[None, None]
+    o, lse, _, _ = orc.rope_attention(bits, bits, orc.encode(v, "bf16"), "bf16", 10000.0,
+                                      variant="exact")
+    for i in range(N):
+        w = [math.exp(math.cos(i - j) / math.sqrt(2.0)) for j in range(i + 1)]
+        z = math.fsum(w)
+        assert abs(o[0, 0, i, 0] - math.fsum(j * w[j] for j in range(i + 1)) / z) < 1e-14
+        assert abs(o[0, 0, i, 1] - 1.0) < 1e-15
+        assert abs(lse[0, 0, i] - math.log(z)) < 1e-14
+
+
+def pin_rope_attention_variants(orc):
+    rng = _rng(18)
+    B, Hq, Hkv, N, D = 1, 2, 1, 40, 64
+    q = torch.from_numpy(rng.standard_normal((B, Hq, N, D)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, N, D)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, N, D)).astype(np.float32)).to(torch.bfloat16)
+
+    def b(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    oe, le, qe, ke = orc.rope_attention(b(q), b(k), b(v), "bf16", 10000.0, variant="exact")
+    orr, lr, qr, kr = orc.rope_attention(b(q), b(k), b(v), "bf16", 10000.0, variant="rounded")
+    # the rounded operands are the exact ones rounded to bf16 (torch rounding
+    # from fp64 via fp32 agrees except on double-rounding ties, absent here)
+    ref_q = torch.from_numpy(qe).float().to(torch.bfloat16).double().numpy()
+    assert np.mean(qr == ref_q) > 0.999
+    assert np.max(np.abs(qr - qe) / np.maximum(np.abs(qe), 1e-30)) <= 2.0 ** -8 + 1e-12
+    # rounding the operands perturbs the result only slightly
+    assert np.max(np.abs(oe - orr)) < 2e-2 and np.max(np.abs(le - lr)) < 2e-2
+    # the first row is exact in both: rotation by 0 is the identity
+    assert np.array_equal(qe[:, :, 0], qr[:, :, 0])
+
+
+ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

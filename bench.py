@@ -1,0 +1,279 @@
+"""Benchmark: causal RoPE attention forward on one MI355X, fused vs pre-rotated.
+
+One step = the whole hot path over one batch of the Llama-3-8B-shaped GQA
+attention layer (B=1, Hq=32, Hkv=8, N=2048, D=128, bf16, RoPE base 500000):
+  * the fused path: attn_rope_causal_fwd (one kernel), and
+  * the pre-rotation path: rope_prerotate then attn_causal_fwd.
+`value` = causal attention FLOPs of both paths (2 * 2*B*Hq*N^2*D per step)
+divided by the measured step time, in TFLOP/s. Inputs are resident in HBM
+before timing starts; steps run back to back on torch's current stream.
+
+Also printed in the same JSON line:
+  * roofline: the fused attention kernel (the dominant kernel), achieved
+    TFLOP/s from HIP events around each of its launches in the timed region,
+    against the dense bf16 MFMA peak;
+  * paths: per-path and per-kernel times (warm, and cold after a 512 MiB
+    cache flush), TFLOP/s, % of MFMA peak, rope_prerotate GB/s vs 8 TB/s;
+  * crossover: fused vs pre-rotation times over the D=64 fp16 MHA sweep
+    (N = 2048 .. 32768) and the GQA shapes, with the measured crossover N*;
+  * cpu_baseline: the fp64 CPU oracle timed on this host over the full
+    workload (rotation + causal attention), in the same unit.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+       [--no-cpu] [--only fused|prerotate|rope|attn] [--copy-calib]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}  # MI355X dense, published
+HBM_PEAK_GBS = 8000.0
+MAIN = "llama3_8b_gqa_n2048"
+METRIC = "causal RoPE-attn fwd TFLOP/s (fused & pre-rotate) + % of MFMA peak; N*"
+
+
+def attn_flops(w):
+    return 2.0 * w["B"] * w["Hq"] * w["N"] ** 2 * w["D"]
+
+
+def prerot_bytes(w):
+    return 2.0 * w["B"] * (w["Hq"] + w["Hkv"]) * w["N"] * w["D"] * 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["fused", "prerotate", "rope", "attn"], default=None,
+                    help="time one kernel/path alone (for profiler runs)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run a plain 256 MiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rotary_position_embedding_causal_amd as rac
+    from rotary_position_embedding_causal_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rac.lib()
+
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": 256 << 20, "launches": 5}))
+        return
+
+    w = inputs.WORKLOADS[MAIN]
+    B, Hq, Hkv, N, D, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["base"]
+    q, k, v = inputs.workload_qkv(MAIN)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out_f = torch.empty_like(qd)
+    out_p = torch.empty_like(qd)
+    lse_f = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    lse_p = torch.empty_like(lse_f)
+    qr = torch.empty_like(qd)
+    kr = torch.empty_like(kd)
+
+    def fused():
+        rac.attn_rope_causal_fwd(qd, kd, vd, base, out=out_f, lse=lse_f)
+
+    def rope():
+        rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr)
+
+    def attn():
+        rac.attn_causal_fwd(qr, kr, vd, out=out_p, lse=lse_p)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    if args.only:
+        fn = {"fused": fused, "rope": rope, "attn": attn,
+              "prerotate": lambda: (rope(), attn())}[args.only]
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"only": args.only, "workload": MAIN, "ms_per_call": dt * 1e3}))
+        return
+
+    # ---- the timed region: K steps of the whole hot path ----
+    for _ in range(args.warmup):
+        fused(); rope(); attn()
+    torch.cuda.synchronize()
+    fused_ev = [(ev(), ev()) for _ in range(args.steps)]
+    rope_ev = [(ev(), ev()) for _ in range(args.steps)]
+    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused_ev[i][0].record(); fused(); fused_ev[i][1].record()
+        rope_ev[i][0].record(); rope(); rope_ev[i][1].record()
+        attn_ev[i][0].record(); attn(); attn_ev[i][1].record()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+
+    def avg_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    fl = attn_flops(w)
+    t_fused = avg_ms(fused_ev)
+    t_rope = avg_ms(rope_ev)
+    t_attn = avg_ms(attn_ev)
+    value = 2 * fl / step_s / 1e12
+    peak = MFMA_PEAK_TFLOPS[w["dtype"]]
+    achieved = fl / (t_fused * 1e-3) / 1e12
+
+    # ---- cold-cache kernel times (512 MiB flush before each rep) ----
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def cold(fn, reps=20):
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            a, b = ev(), ev()
+            a.record(); fn(); b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    c_fused, c_rope, c_attn = cold(fused), cold(rope), cold(attn)
+    pb = prerot_bytes(w)
+    paths = {
+        "fused": {"ms": t_fused, "tflops": fl / t_fused / 1e9, "mfma_frac": fl / t_fused / 1e9 / peak,
+                  "cold_ms": c_fused, "cold_tflops": fl / c_fused / 1e9},
+        "prerotate": {"ms": t_rope + t_attn, "tflops": fl / (t_rope + t_attn) / 1e9,
+                      "mfma_frac": fl / (t_rope + t_attn) / 1e9 / peak,
+                      "cold_ms": c_rope + c_attn},
+        "attn_causal_fwd": {"ms": t_attn, "tflops": fl / t_attn / 1e9,
+                            "mfma_frac": fl / t_attn / 1e9 / peak, "cold_ms": c_attn},
+        "rope_prerotate": {"ms": t_rope, "gbs": pb / t_rope / 1e6,
+                           "hbm_frac": pb / t_rope / 1e6 / HBM_PEAK_GBS, "cold_ms": c_rope,
+                           "cold_gbs": pb / c_rope / 1e6,
+                           "cold_hbm_frac": pb / c_rope / 1e6 / HBM_PEAK_GBS, "bytes": pb},
+    }
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": MAIN, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D,
+                   "rope_base": base, "causal": True,
+                   "step": "attn_rope_causal_fwd + (rope_prerotate -> attn_causal_fwd)",
+                   "flops_per_path": fl},
+        "roofline": {"kernel": "attn_fwd_kernel<bf16,128,rope>", "bound": "mfma",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None},
+        "paths": paths,
+    }
+
+    if not args.no_sweep:
+        result["crossover"] = crossover(torch, rac, inputs, dev, ev)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(inputs, w)
+    print(json.dumps(result), flush=True)
+
+
+def crossover(torch, rac, inputs, dev, ev, reps=10):
+    """Fused vs pre-rotation path time per shape; N* where their order flips."""
+    rows = []
+    names = ["mha_d64_fp16_n%d" % n for n in inputs.SWEEP_NS] + [
+        "llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192"]
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        q, k, v = inputs.workload_qkv(name)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        base = w["base"]
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
+        qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+        fns = {
+            "fused": lambda: rac.attn_rope_causal_fwd(qd, kd, vd, base, out=o, lse=lse),
+            "prerotate": lambda: (rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
+                                  rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse)),
+            "attn": lambda: rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse),
+        }
+        t = {}
+        for key, fn in fns.items():
+            for _ in range(3):
+                fn()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t[key] = a.elapsed_time(b) / reps
+        fl = attn_flops(w)
+        rows.append({"workload": name, "N": w["N"], "fused_ms": t["fused"],
+                     "prerotate_ms": t["prerotate"], "attn_only_ms": t["attn"],
+                     "fused_tflops": fl / t["fused"] / 1e9,
+                     "prerotate_tflops": fl / t["prerotate"] / 1e9,
+                     "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0})
+        del qd, kd, vd, o, lse, qr, kr
+        torch.cuda.empty_cache()
+    sweep = [r for r in rows if r["workload"].startswith("mha_d64")]
+    n_star = None
+    bracket = None
+    for a, b in zip(sweep, sweep[1:]):
+        da = a["fused_ms"] - a["prerotate_ms"]
+        db = b["fused_ms"] - b["prerotate_ms"]
+        if (da < 0) != (db < 0):
+            # log-linear interpolation of the sign change of the relative gap
+            ga, gb = da / a["prerotate_ms"], db / b["prerotate_ms"]
+            x = ga / (ga - gb)
+            n_star = math.exp(math.log(a["N"]) + x * (math.log(b["N"]) - math.log(a["N"])))
+            bracket = [a["N"], b["N"]]
+            break
+    winner = None
+    if n_star is None and sweep:
+        winner = "fused" if all(r["fused_ms"] < r["prerotate_ms"] for r in sweep) else (
+            "prerotate" if all(r["fused_ms"] > r["prerotate_ms"] for r in sweep) else "mixed")
+    return {"n_star": n_star, "bracket": bracket, "winner_if_no_crossing": winner,
+            "sweep": "mha_d64_fp16 N=2048..32768 (B=1, H=16)", "rows": rows}
+
+
+def cpu_baseline(inputs, w, min_seconds=10.0):
+    """The fp64 oracle on this host over the full workload (one pass)."""
+    import oracle
+    q, k, v = inputs.workload_qkv(MAIN)
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:  # whole passes until at least min_seconds of CPU work
+        oracle.rope_attention(qb, kb, vb, w["dtype"], w["base"], variant="rounded")
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 200:
+            break
+    return {"value": passes * attn_flops(w) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "seconds": dt, "passes": passes,
+            "sample": "the full %s workload, %d pass(es): fp64 RoPE of Q and K, then "
+                      "two-pass causal attention over every query row; FLOPs counted as "
+                      "2*B*Hq*N^2*D per pass, as for the GPU" % (MAIN, passes)}
+
+
+if __name__ == "__main__":
+    main()

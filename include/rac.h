@@ -1,0 +1,123 @@
+/*
+ * rac.h -- RoPE + causal attention forward on AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Three operations:
+ *
+ *   attn_rope_causal_fwd  one kernel: rotary position embedding applied to the
+ *                         query and key tiles inside a causal attention
+ *                         forward ("in-kernel rotation").
+ *   rope_prerotate        a separate streaming pass writing rotated copies of
+ *                         Q and K ("pre-rotation").
+ *   attn_causal_fwd       causal attention forward on already-rotated inputs;
+ *                         with rope_prerotate it forms the pre-rotation path.
+ *
+ * The two paths and the choice between them are the subject of "AttnFuse Makes
+ * RoPE a First-Class Attention Compilation Operation" (tdteach paper-news,
+ * 2026-09-13), paragraphs 3 and 4, and of the AttnFuse abstract (arxivdaily
+ * 2609.13612): pre-rotation costs memory bandwidth, in-kernel rotation costs
+ * compute and tiling, and which wins depends on the GPU and the shape.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are contiguous row-major [B, H, N, D]: batch, head, token, head dim.
+ *   q, out          [B, Hq,  N, D]
+ *   k, v            [B, Hkv, N, D]
+ *   lse             [B, Hq,  N]     fp32
+ * Every tensor pointer is a DEVICE pointer on the current HIP device, owned by
+ * the caller, who keeps it alive until the enqueued work completes. Element
+ * type is `dtype` (RAC_BF16 or RAC_FP16) for q, k, v, out, q_rot and k_rot.
+ * Pointers must be 16-byte aligned.
+ *
+ * RoPE (rotary position embedding; "Fast and Exact Relative-Position Attention
+ * via Structure-Aware Kernels", rainbus digest, background "RoPE and
+ * parameter-free position encodings": each query and key is rotated by an
+ * angle set by its absolute position). Readings where the pages are silent:
+ * token n of every (b, h) sits at position n; coordinates (2i, 2i+1) form a
+ * pair turned counter-clockwise by n * theta_i, theta_i = rope_base^(-2i/D);
+ * values are not rotated. Angles and their cos/sin are formed in fp64 on the
+ * host, stored as fp32, and the rotation runs in fp32 on the device, rounded
+ * once to `dtype` (round to nearest even). Both paths feed the same rotated
+ * operands to the matrix cores.
+ *
+ * Causal attention (same digest, "FlashAttention and online softmax" and its
+ * forward Algorithm 1; MHA/GQA per the AttnFuse report, paragraph 4): query
+ * head h reads key/value head h / (Hq / Hkv); query n attends to keys j <= n;
+ * scores are scaled by 1/sqrt(D); softmax statistics are kept in fp32 with a
+ * base-2 exponent; out = softmax(scores) V rounded to `dtype`;
+ * lse[n] = natural log of sum_j exp(score_nj), fp32.
+ *
+ * Supported: D in {64, 128}; Hq % Hkv == 0; 1 <= Hq, Hkv <= 65535;
+ * 0 <= B <= 65535; 0 <= N <= RAC_MAX_N. B == 0 or N == 0 is a no-op that
+ * returns RAC_OK without touching any pointer.
+ *
+ * Errors: arguments are validated before anything is enqueued; a non-zero
+ * return means nothing was launched, and rac_last_error() gives the reason
+ * (per calling thread). Calls enqueue on `stream` (NULL = the null stream)
+ * and return without synchronising; a fault inside a kernel surfaces at the
+ * caller's next synchronisation. No C++ exception crosses this boundary.
+ *
+ * Library-owned memory: the cos/sin table for each (device, D, rope_base),
+ * fp32 [capacity, D], grown on demand. The first call that needs a new or
+ * larger table allocates it and uploads it synchronously (so warm up before
+ * timing). rac_release_tables() frees every table.
+ */
+#ifndef RAC_H
+#define RAC_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { RAC_BF16 = 0, RAC_FP16 = 1 };
+
+enum {
+    RAC_OK = 0,
+    RAC_ERR_ARG = -1,          /* bad size, null pointer, overlap, bad rope_base or dtype */
+    RAC_ERR_ALIGN = -2,        /* a pointer is not 16-byte aligned */
+    RAC_ERR_UNSUPPORTED = -3,  /* valid but not implemented: D not in {64, 128} */
+    RAC_ERR_HIP = -4           /* a HIP runtime call failed (no device, out of memory, launch) */
+};
+
+#define RAC_MAX_N (1 << 22)
+
+/*
+ * Fused path: one kernel applies RoPE to each query tile once and to every key
+ * tile it visits, then runs causal attention on the rotated operands.
+ * q, k, v: inputs as above (not rotated). out: [B,Hq,N,D], must not overlap
+ * q, k or v. lse: [B,Hq,N] fp32, or NULL to skip it. rope_base > 0, finite.
+ */
+int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int N, int D, double rope_base,
+                         int dtype, void* stream);
+
+/*
+ * Pre-rotation pass: q_rot = RoPE(q), k_rot = RoPE(k), each element rounded
+ * once to `dtype`. Memory-bound streaming kernel. q_rot may equal q and k_rot
+ * may equal k (in place); any other overlap between the four buffers is an
+ * error.
+ */
+int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
+                   int B, int Hq, int Hkv, int N, int D, double rope_base,
+                   int dtype, void* stream);
+
+/*
+ * Causal attention forward on inputs that already carry their rotation (for
+ * example the output of rope_prerotate). Same layouts and rules as
+ * attn_rope_causal_fwd, without rope_base.
+ */
+int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int Hq, int Hkv, int N, int D,
+                    int dtype, void* stream);
+
+/* Text for the last non-zero return on the calling thread ("" if none). */
+const char* rac_last_error(void);
+
+/* Synchronises every device holding a table, then frees all cos/sin tables.
+ * Returns RAC_OK or RAC_ERR_HIP. */
+int rac_release_tables(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAC_H */

@@ -1,0 +1,170 @@
+"""RoPE + causal attention forward for AMD MI355X (gfx950).
+
+Thin Python binding over ``librac.so`` (C ABI in ``include/rac.h``): it only
+checks and marshals torch tensors into pointers and sizes, passes torch's
+current HIP stream, and turns error codes into exceptions. Every step of the
+computation runs in the library's HIP kernels; there is no CPU fallback, and
+calling any operation without the built library raises.
+
+Operations (names as in the C ABI):
+  attn_rope_causal_fwd(q, k, v, rope_base)  -> (out, lse)   fused RoPE + attention
+  rope_prerotate(q, k, rope_base)           -> (q_rot, k_rot)
+  attn_causal_fwd(q, k, v)                  -> (out, lse)   on pre-rotated inputs
+Tensors are contiguous [B, H, N, D] bf16/fp16 on one HIP device; lse is fp32
+[B, Hq, N] (natural log).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librac.so")
+
+RAC_BF16, RAC_FP16 = 0, 1
+RAC_OK, RAC_ERR_ARG, RAC_ERR_ALIGN, RAC_ERR_UNSUPPORTED, RAC_ERR_HIP = 0, -1, -2, -3, -4
+RAC_MAX_N = 1 << 22
+EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rac_last_error",
+            "rac_release_tables")
+
+_DTYPES = {torch.bfloat16: RAC_BF16, torch.float16: RAC_FP16}
+
+_lib = None
+
+
+class RacError(RuntimeError):
+    """A HIP runtime failure reported by the library."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librac.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("librac.so is missing at %s: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, d, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+    L.attn_rope_causal_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, vp]
+    L.attn_rope_causal_fwd.restype = i
+    L.rope_prerotate.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp]
+    L.rope_prerotate.restype = i
+    L.attn_causal_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, vp]
+    L.attn_causal_fwd.restype = i
+    L.rac_last_error.argtypes = []
+    L.rac_last_error.restype = ctypes.c_char_p
+    L.rac_release_tables.argtypes = []
+    L.rac_release_tables.restype = i
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().rac_last_error().decode()
+
+
+def check(rc: int, what: str) -> None:
+    """Raise for a non-zero return code of the C ABI."""
+    if rc == RAC_OK:
+        return
+    msg = "%s: %s (code %d)" % (what, last_error(), rc)
+    if rc == RAC_ERR_HIP:
+        raise RacError(msg)
+    if rc == RAC_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise ValueError(msg)
+
+
+def release_tables() -> None:
+    check(lib().rac_release_tables(), "rac_release_tables")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or (v is not None and v.dim() != 4):
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, D) or (v is not None and v.shape != k.shape):
+        raise ValueError("k and v must be [B, Hkv, N, D] matching q %s" % (tuple(q.shape),))
+    for t in (q, k) + ((v,) if v is not None else ()):
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on a HIP device")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, D]")
+    if q.dtype not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float16, got %s" % q.dtype)
+    return B, Hq, Hkv, N, D, _DTYPES[q.dtype]
+
+
+def _outputs(q, out, lse, want_lse):
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != q.shape[:-1] or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, N]")
+    return out, lse
+
+
+def attn_rope_causal_fwd(q, k, v, rope_base: float, out=None, lse=None, want_lse: bool = True):
+    """Fused path: RoPE on Q/K inside the causal attention kernel. Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        B, Hq, Hkv, N, D, float(rope_base), dt,
+                                        _stream(q.device))
+    check(rc, "attn_rope_causal_fwd")
+    return out, lse
+
+
+def rope_prerotate(q, k, rope_base: float, q_rot=None, k_rot=None):
+    """Pre-rotation pass. Returns (q_rot, k_rot); pass q_rot=q, k_rot=k for in place."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, None)
+    q_rot = torch.empty_like(q) if q_rot is None else q_rot
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    for src, dst in ((q, q_rot), (k, k_rot)):
+        if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous() \
+                or dst.device != src.device:
+            raise ValueError("q_rot/k_rot must be contiguous tensors like q/k")
+    with torch.cuda.device(q.device):
+        rc = lib().rope_prerotate(_ptr(q), _ptr(k), _ptr(q_rot), _ptr(k_rot), B, Hq, Hkv, N, D,
+                                  float(rope_base), dt, _stream(q.device))
+    check(rc, "rope_prerotate")
+    return q_rot, k_rot
+
+
+def attn_causal_fwd(q, k, v, out=None, lse=None, want_lse: bool = True):
+    """Causal attention on already-rotated inputs. Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_causal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                   B, Hq, Hkv, N, D, dt, _stream(q.device))
+    check(rc, "attn_causal_fwd")
+    return out, lse
+
+
+def prerotate_path(q, k, v, rope_base: float, want_lse: bool = True):
+    """The pre-rotation path: rope_prerotate then attn_causal_fwd. Returns (out, lse)."""
+    q_rot, k_rot = rope_prerotate(q, k, rope_base)
+    return attn_causal_fwd(q_rot, k_rot, v, want_lse=want_lse)

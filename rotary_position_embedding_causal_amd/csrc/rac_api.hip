@@ -1,0 +1,241 @@
+// rac_api.hip -- the C ABI declared in include/rac.h: argument validation,
+// the per-device cos/sin table cache, and kernel dispatch. Host code only.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/rac.h"
+#include "rac_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return RAC_OK;
+}
+
+// ---- cos/sin tables --------------------------------------------------------
+//
+// Entry [p][2i] = cos(p * theta_i), [p][2i+1] = sin(p * theta_i), with
+// theta_i = base^(-2i/D) and the angle formed in fp64 (p up to millions times
+// theta would lose the low bits of the angle in fp32), rounded once to fp32.
+
+struct Table {
+    float* dev = nullptr;
+    int64_t capacity = 0;  // positions held
+};
+
+std::mutex g_mutex;
+std::map<std::tuple<int, int, uint64_t>, Table> g_tables;  // (device, D, base bits)
+std::vector<std::pair<int, float*>> g_retired;             // outgrown tables, freed on release
+
+uint64_t bits_of(double x) {
+    uint64_t u;
+    memcpy(&u, &x, sizeof u);
+    return u;
+}
+
+int get_table(int D, double base, int N, const float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(RAC_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Table& t = g_tables[std::make_tuple(dev, D, bits_of(base))];
+    if (t.capacity >= N) {
+        *out = t.dev;
+        return RAC_OK;
+    }
+    int64_t cap = 4096;
+    while (cap < N) cap *= 2;
+    std::vector<float> host((size_t)cap * D);
+    std::vector<double> theta(D / 2);
+    for (int i = 0; i < D / 2; ++i) theta[i] = pow(base, -(2.0 * i) / (double)D);
+    for (int64_t p = 0; p < cap; ++p)
+        for (int i = 0; i < D / 2; ++i) {
+            const double ang = (double)p * theta[i];
+            host[(size_t)p * D + 2 * i] = (float)cos(ang);
+            host[(size_t)p * D + 2 * i + 1] = (float)sin(ang);
+        }
+    float* d = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&d), host.size() * sizeof(float)) != hipSuccess)
+        return fail(RAC_ERR_HIP, "hipMalloc of a %lld-position RoPE table failed", (long long)cap);
+    if (hipMemcpy(d, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(d);
+        return fail(RAC_ERR_HIP, "upload of the RoPE table failed");
+    }
+    // in-flight kernels may still read the old table: keep it until release
+    if (t.dev) g_retired.emplace_back(dev, t.dev);
+    t.dev = d;
+    t.capacity = cap;
+    *out = d;
+    return RAC_OK;
+}
+
+// ---- validation --------------------------------------------------------------
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Checks shared by every entry point. Returns RAC_OK, or an error code with
+// the message set. Sets *empty when there is nothing to compute.
+int check_shape(int B, int Hq, int Hkv, int N, int D, int dtype, bool* empty) {
+    if (dtype != RAC_BF16 && dtype != RAC_FP16)
+        return fail(RAC_ERR_ARG, "dtype must be RAC_BF16 (0) or RAC_FP16 (1), got %d", dtype);
+    if (B < 0 || N < 0) return fail(RAC_ERR_ARG, "B and N must be >= 0 (B=%d, N=%d)", B, N);
+    if (Hq < 1 || Hkv < 1) return fail(RAC_ERR_ARG, "Hq and Hkv must be >= 1 (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(RAC_ERR_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (Hq > 65535 || B > 65535)
+        return fail(RAC_ERR_ARG, "Hq and B must be <= 65535 (Hq=%d, B=%d)", Hq, B);
+    if (N > RAC_MAX_N) return fail(RAC_ERR_ARG, "N=%d exceeds RAC_MAX_N=%d", N, RAC_MAX_N);
+    if (D != 64 && D != 128)
+        return fail(RAC_ERR_UNSUPPORTED, "head dim D=%d is not supported (64 or 128)", D);
+    *empty = (B == 0 || N == 0);
+    return RAC_OK;
+}
+
+int check_base(double base) {
+    if (!(base > 0.0) || !isfinite(base))
+        return fail(RAC_ERR_ARG, "rope_base must be finite and > 0");
+    return RAC_OK;
+}
+
+int check_attn_ptrs(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    int B, int Hq, int Hkv, int N, int D) {
+    if (!q || !k || !v || !out) return fail(RAC_ERR_ARG, "q, k, v and out must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
+    const int64_t kvbytes = (int64_t)B * Hkv * N * D * 2;
+    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) ||
+        overlap(out, qbytes, v, kvbytes))
+        return fail(RAC_ERR_ARG, "out must not overlap q, k or v");
+    if (lse) {
+        const int64_t lbytes = (int64_t)B * Hq * N * 4;
+        if (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kvbytes) ||
+            overlap(lse, lbytes, v, kvbytes) || overlap(lse, lbytes, out, qbytes))
+            return fail(RAC_ERR_ARG, "lse must not overlap q, k, v or out");
+    }
+    return RAC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(RAC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
+                         void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    const float* table = nullptr;
+    if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype};
+    return hip_status(rac::launch_attn_fwd(a, true, static_cast<hipStream_t>(stream)),
+                      "attn_rope_causal_fwd launch");
+}
+
+int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int Hq, int Hkv, int N, int D, int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    rac::AttnArgs a{q, k, v, out, lse, nullptr, B, Hq, Hkv, N, D, dtype};
+    return hip_status(rac::launch_attn_fwd(a, false, static_cast<hipStream_t>(stream)),
+                      "attn_causal_fwd launch");
+}
+
+int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B, int Hq,
+                   int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)
+        return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280");
+    if (empty) return ok();
+    if (!q || !k || !q_rot || !k_rot)
+        return fail(RAC_ERR_ARG, "q, k, q_rot and k_rot must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_rot) || !aligned16(k_rot))
+        return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
+    const int64_t kbytes = (int64_t)B * Hkv * N * D * 2;
+    // exact in-place use is allowed; any other overlap is not
+    if ((q_rot != q && overlap(q_rot, qbytes, q, qbytes)) || overlap(q_rot, qbytes, k, kbytes) ||
+        (k_rot != k && overlap(k_rot, kbytes, k, kbytes)) || overlap(k_rot, kbytes, q, qbytes) ||
+        overlap(q_rot, qbytes, k_rot, kbytes))
+        return fail(RAC_ERR_ARG, "q_rot/k_rot may alias q/k exactly, and must not overlap otherwise");
+    const float* table = nullptr;
+    if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    return hip_status(rac::launch_rope_prerotate(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D,
+                                                 dtype, static_cast<hipStream_t>(stream)),
+                      "rope_prerotate launch");
+}
+
+const char* rac_last_error(void) { return g_last_error.c_str(); }
+
+int rac_release_tables(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int prev = 0;
+    bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    bool failed = false;
+    std::map<int, bool> synced;
+    auto sync_dev = [&](int dev) {
+        if (synced.count(dev)) return;
+        synced[dev] = true;
+        if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess) failed = true;
+    };
+    for (auto& kv : g_tables) {
+        const int dev = std::get<0>(kv.first);
+        if (!kv.second.dev) continue;
+        sync_dev(dev);
+        if (hipFree(kv.second.dev) != hipSuccess) failed = true;
+    }
+    for (auto& r : g_retired) {
+        sync_dev(r.first);
+        if (hipFree(r.second) != hipSuccess) failed = true;
+    }
+    g_tables.clear();
+    g_retired.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+    if (failed) return fail(RAC_ERR_HIP, "freeing the RoPE tables failed");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// rac_device.h -- device-side building blocks shared by the gfx950 kernels:
+// storage formats, the 32x32x16 MFMA wrappers and the one RoPE rotation
+// routine that both the pre-rotation pass and the fused attention kernel use,
+// so that both paths hand bit-identical rotated operands to the matrix cores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rac {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_BF16 = 0, DT_FP16 = 1 };
+
+// Storage format traits: 16-bit element <-> fp32, packed 8-element operand
+// vectors and the matching 32x32x16 MFMA (fp32 accumulate).
+template <int DT> struct Fmt;
+
+template <> struct Fmt<DT_BF16> {
+    typedef bf16x8 vec8;
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        __bf16 x = (__bf16)a, y = (__bf16)b;
+        return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    }
+    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Fmt<DT_FP16> {
+    typedef f16x8 vec8;
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+    // round to nearest even (v_cvt_f16_f32 in the default rounding mode)
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        _Float16 x = (_Float16)a, y = (_Float16)b;
+        return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    }
+    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ typename Fmt<DT>::vec8 as_vec8(u32x4 w) {
+    return __builtin_bit_cast(typename Fmt<DT>::vec8, w);
+}
+
+// RoPE on 8 consecutive elements (4 adjacent pairs) of one row.
+// x: the 8 elements as 4 packed words; cs: the row's table entries for these
+// pairs, (cos, sin) interleaved. Pair (x0, x1) turns counter-clockwise:
+//   x0' = x0*c - x1*s,  x1' = x0*s + x1*c
+// in fp32 with one fused multiply-add each, then rounds to the storage format.
+// Every kernel rotates through this routine, so the rotated operands of the
+// fused kernel and of the pre-rotation pass are bit-identical.
+template <int DT>
+__device__ __forceinline__ u32x4 rope_rotate8(u32x4 x, f32x4 cs_lo, f32x4 cs_hi) {
+    typedef Fmt<DT> F;
+    u32x4 y;
+    const float c[4] = {cs_lo[0], cs_lo[2], cs_hi[0], cs_hi[2]};
+    const float s[4] = {cs_lo[1], cs_lo[3], cs_hi[1], cs_hi[3]};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float x0 = F::lo(x[t]), x1 = F::hi(x[t]);
+        float a = __builtin_fmaf(x0, c[t], -(x1 * s[t]));
+        float b = __builtin_fmaf(x0, s[t], x1 * c[t]);
+        y[t] = F::pack2(a, b);
+    }
+    return y;
+}
+
+}  // namespace rac

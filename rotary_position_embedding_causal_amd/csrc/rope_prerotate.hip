@@ -1,0 +1,85 @@
+// rope_prerotate.hip -- the pre-rotation pass: q_rot = RoPE(q), k_rot = RoPE(k).
+//
+// "AttnFuse Makes RoPE a First-Class Attention Compilation Operation",
+// paragraph 3, models pre-rotation as a memory-bandwidth cost: every query and
+// key element is read once and written once. This kernel is a pure HBM stream
+// sized for that: each lane moves 16-byte chunks, and the cos/sin table entries
+// a lane needs depend only on (position, chunk), so a lane loads them once and
+// reuses them across a group of heads, keeping the table's share of the
+// traffic small next to Q and K.
+//
+// Work split: a (token position, 16-byte chunk) pair per lane, blockIdx.y
+// selecting a group of HEADS heads ("slabs") from the concatenation of the
+// B*Hq query slabs and the B*Hkv key slabs, each slab being one [N, D] matrix.
+#include "rac_device.h"
+#include "rac_internal.h"
+
+namespace rac {
+
+constexpr int PR_THREADS = 256;
+constexpr int PR_HEADS = 8;  // slabs per lane: 8 independent 16-byte loads in flight
+
+template <int DT, int D>
+__global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* q_rot,
+    uint16_t* k_rot, const float* __restrict__ table, int N, int64_t q_slabs,
+    int64_t total_slabs) {
+    constexpr int CHUNKS = D / 8;  // 16-byte chunks per row
+    const int64_t idx = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+    const int64_t row = idx / CHUNKS;
+    const int chunk = (int)(idx % CHUNKS);
+    if (row >= N) return;
+    const f32x4* tab = reinterpret_cast<const f32x4*>(table + row * D + chunk * 8);
+    const f32x4 cs_lo = tab[0];
+    const f32x4 cs_hi = tab[1];
+    const int64_t slab0 = (int64_t)blockIdx.y * PR_HEADS;
+    const int64_t within = row * D + chunk * 8;  // element offset inside a slab
+    const int64_t slab_elems = (int64_t)N * D;
+
+    u32x4 x[PR_HEADS];
+#pragma unroll
+    for (int s = 0; s < PR_HEADS; ++s) {
+        const int64_t slab = slab0 + s;
+        if (slab < total_slabs) {
+            const uint16_t* src = slab < q_slabs ? q + slab * slab_elems
+                                                 : k + (slab - q_slabs) * slab_elems;
+            x[s] = *reinterpret_cast<const u32x4*>(src + within);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < PR_HEADS; ++s) {
+        const int64_t slab = slab0 + s;
+        if (slab < total_slabs) {
+            uint16_t* dst = slab < q_slabs ? q_rot + slab * slab_elems
+                                           : k_rot + (slab - q_slabs) * slab_elems;
+            *reinterpret_cast<u32x4*>(dst + within) = rope_rotate8<DT>(x[s], cs_lo, cs_hi);
+        }
+    }
+}
+
+template <int DT, int D>
+static hipError_t launch_typed(const void* q, const void* k, void* q_rot, void* k_rot,
+                               const float* table, int B, int Hq, int Hkv, int N,
+                               hipStream_t stream) {
+    const int64_t lanes = (int64_t)N * (D / 8);
+    const int64_t q_slabs = (int64_t)B * Hq;
+    const int64_t total = q_slabs + (int64_t)B * Hkv;
+    dim3 grid((unsigned)((lanes + PR_THREADS - 1) / PR_THREADS),
+              (unsigned)((total + PR_HEADS - 1) / PR_HEADS));
+    rope_prerotate_kernel<DT, D><<<grid, PR_THREADS, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N, q_slabs, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
+                                 const float* table, int B, int Hq, int Hkv, int N, int D,
+                                 int dtype, hipStream_t stream) {
+    if (dtype == DT_BF16)
+        return D == 64 ? launch_typed<DT_BF16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                       : launch_typed<DT_BF16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return D == 64 ? launch_typed<DT_FP16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                   : launch_typed<DT_FP16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+}
+
+}  // namespace rac

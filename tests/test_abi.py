@@ -1,0 +1,135 @@
+"""The C ABI library without a GPU: it loads, exports what include/rac.h
+declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rotary_position_embedding_causal_amd as rac
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rac.h")
+
+# aligned fake device addresses: never dereferenced, every case fails validation first
+P = 1 << 20
+Q, K, V, O, L = (ctypes.c_void_p(P * (i + 1)) for i in range(5))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(rac.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L_ = rac.lib()
+    for name in declared_functions():
+        assert hasattr(L_, name), name
+
+
+def fused(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().attn_rope_causal_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                          a["Hq"], a["Hkv"], a["N"], a["D"], a["base"],
+                                          a["dtype"], None)
+
+
+def plain(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Hq=4, Hkv=2, N=64, D=64, dtype=0)
+    a.update(kw)
+    return rac.lib().attn_causal_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["N"], a["D"], a["dtype"], None)
+
+
+def prerot(**kw):
+    a = dict(q=Q, k=K, qr=O, kr=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().rope_prerotate(a["q"], a["k"], a["qr"], a["kr"], a["B"], a["Hq"], a["Hkv"],
+                                    a["N"], a["D"], a["base"], a["dtype"], None)
+
+
+BAD = [
+    (dict(dtype=2), rac.RAC_ERR_ARG),
+    (dict(D=96), rac.RAC_ERR_UNSUPPORTED),
+    (dict(D=256), rac.RAC_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), rac.RAC_ERR_ARG),
+    (dict(Hq=0), rac.RAC_ERR_ARG),
+    (dict(Hkv=0), rac.RAC_ERR_ARG),
+    (dict(B=-1), rac.RAC_ERR_ARG),
+    (dict(N=-5), rac.RAC_ERR_ARG),
+    (dict(N=rac.RAC_MAX_N + 1), rac.RAC_ERR_ARG),
+    (dict(Hq=65536, Hkv=1), rac.RAC_ERR_ARG),
+    (dict(q=None), rac.RAC_ERR_ARG),
+    (dict(v=None), rac.RAC_ERR_ARG),
+    (dict(out=None), rac.RAC_ERR_ARG),
+    (dict(q=ctypes.c_void_p(P + 8)), rac.RAC_ERR_ALIGN),
+    (dict(lse=ctypes.c_void_p(5 * P + 4)), rac.RAC_ERR_ALIGN),
+    (dict(out=Q), rac.RAC_ERR_ARG),                       # out aliases q
+    (dict(out=ctypes.c_void_p(P + 4096)), rac.RAC_ERR_ARG),  # out overlaps q
+    (dict(lse=O), rac.RAC_ERR_ARG),                       # lse overlaps out
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_attention_rejects_bad_arguments(kw, code):
+    assert plain(**kw) == code
+    assert rac.last_error() != ""
+    assert fused(**kw) == code
+
+
+@pytest.mark.parametrize("base", [0.0, -1.0, float("inf"), float("nan")])
+def test_rope_base_must_be_positive_and_finite(base):
+    assert fused(base=base) == rac.RAC_ERR_ARG
+    assert prerot(base=base) == rac.RAC_ERR_ARG
+    assert "rope_base" in rac.last_error()
+
+
+def test_prerotate_overlap_rules():
+    assert prerot(qr=None) == rac.RAC_ERR_ARG
+    assert prerot(qr=K) == rac.RAC_ERR_ARG                    # q_rot over k
+    assert prerot(kr=ctypes.c_void_p(P + 64)) == rac.RAC_ERR_ARG  # k_rot inside q
+    assert prerot(qr=ctypes.c_void_p(P + 16)) == rac.RAC_ERR_ARG  # partial in-place
+    assert prerot(kr=ctypes.c_void_p(2 * P + 16)) == rac.RAC_ERR_ARG
+    assert prerot(q=ctypes.c_void_p(P + 2)) == rac.RAC_ERR_ALIGN
+    assert prerot(D=32) == rac.RAC_ERR_UNSUPPORTED
+    assert prerot(B=65535, Hq=8, Hkv=8) == rac.RAC_ERR_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, q=None, k=None, v=None,
+                                                           out=None, lse=None)])
+def test_empty_problem_is_a_noop(kw):
+    assert plain(**kw) == rac.RAC_OK
+    assert fused(**kw) == rac.RAC_OK
+    pk = {key: val for key, val in kw.items() if key in ("B", "N")}
+    assert prerot(**pk) == rac.RAC_OK
+    assert rac.last_error() == ""
+
+
+def test_binding_maps_codes_to_exceptions():
+    with pytest.raises(NotImplementedError):
+        rac.check(rac.RAC_ERR_UNSUPPORTED, "x")
+    with pytest.raises(ValueError):
+        rac.check(rac.RAC_ERR_ARG, "x")
+    with pytest.raises(rac.RacError):
+        rac.check(rac.RAC_ERR_HIP, "x")
+    rac.check(rac.RAC_OK, "x")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(rac, "_lib", None)
+    monkeypatch.setattr(rac, "LIB_PATH", "/nonexistent/librac.so")
+    with pytest.raises(RuntimeError, match="librac.so is missing"):
+        rac.lib()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        rac.attn_causal_fwd(x, x, x)

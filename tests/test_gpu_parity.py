@@ -1,0 +1,287 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Cases: the tiny MHA workload in full; small ragged shapes that span several
+tiles and end in partial tiles (N in {1, 2, 3, 17, 63, 64, 65, 127, 129,
+300}); GQA ratios 1, 2, 4, 8; D = 64 and 128; bf16 and fp16; large-sigma
+inputs that force many running-max rescales; and the full-size workloads
+(Llama-3-8B-shaped GQA layers, the D = 64 fp16 sweep) in the launch
+configuration the bench times, checked on sampled rows the oracle computes
+one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotary_position_embedding_causal_amd as rac
+from rotary_position_embedding_causal_amd import inputs
+from parity import (assert_lse, assert_o, bits, o_errors, oracle_rows, sampled_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    rac.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B, Hq, Hkv, N, D, dtype, key, sigma=1.0):
+    q, k, v = inputs.qkv(B, Hq, Hkv, N, D, dtype, key=key, sigma=sigma)
+    return (q, k, v), (q.to(DEV), k.to(DEV), v.to(DEV))
+
+
+def _ulp_key(b):
+    """uint16 bit patterns -> integers that are monotonic in the value."""
+    b = b.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def _check_rotation(g, src_bits, positions, dt, base):
+    """GPU rotated bits vs the oracle's rotation.
+
+    At least 99.9% of the elements equal the oracle's rounded rotation bit
+    for bit. Every element is within one unit in the last place of it, or --
+    where the two products of a pair nearly cancel, so the result is far
+    smaller than its inputs -- within the error of evaluating the rotation in
+    fp32 with fp32 cos/sin: |y_gpu - y_exact| <= ulp(y_gpu) + 8 * 2^-24 *
+    (|x_2i| + |x_2i+1|) (table rounding, two products, one fused add).
+    """
+    x = oracle.decode(src_bits, dt)
+    y = oracle.rope(x, positions, base)
+    ref = oracle.encode(y, dt)
+    exact = float(np.mean(g == ref))
+    assert exact >= 0.999, "bit-exact fraction %.5f" % exact
+    gv = oracle.decode(g, dt)
+    pair = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+    pair = np.repeat(pair, 2, axis=-1)
+    ulp = np.spacing(np.abs(gv).astype(np.float16 if dt == "fp16" else np.float32))
+    if dt == "bf16":
+        ulp = ulp.astype(np.float64) * 65536.0  # bf16 spacing = fp32 spacing * 2^16
+    within_ulp = np.abs(_ulp_key(g) - _ulp_key(ref)) <= 1
+    within_model = np.abs(gv - y) <= ulp.astype(np.float64) + 8 * 2.0 ** -24 * pair
+    bad = ~(within_ulp | within_model)
+    assert not bad.any(), "%d elements outside the fp32 rotation error model" % int(bad.sum())
+    return exact
+
+
+SMALL = [  # B, Hq, Hkv, N, D, dtype, base
+    (1, 4, 4, 512, 64, "bf16", 10000.0),
+    (1, 8, 2, 300, 128, "bf16", 500000.0),
+    (2, 4, 1, 129, 64, "fp16", 10000.0),
+    (1, 8, 1, 65, 128, "fp16", 500000.0),
+    (1, 2, 2, 1, 64, "bf16", 10000.0),
+    (1, 6, 3, 17, 128, "bf16", 10000.0),
+]
+
+
+def _id(s):
+    return "B%d_Hq%d_Hkv%d_N%d_D%d_%s" % s[:6]
+
+
+# ---------------------------------------------------------------------------
+# rope_prerotate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", SMALL + [(1, 16, 16, 4096, 64, "fp16", 10000.0),
+                                          (1, 4, 2, 2048, 128, "bf16", 500000.0)], ids=_id)
+def test_prerotate_matches_rounded_oracle(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    (q, k, _), (qd, kd, _) = _inputs(B, Hq, Hkv, N, D, dt, key=(101, N, D))
+    qr, kr = rac.rope_prerotate(qd, kd, base)
+    torch.cuda.synchronize()
+    for src, got in ((q, qr), (k, kr)):
+        _check_rotation(bits(got), inputs.bits(src), np.arange(N), dt, base)
+
+
+def test_prerotate_in_place():
+    (q, k, _), (qd, kd, _) = _inputs(1, 4, 2, 257, 128, "bf16", key=(102,))
+    qr, kr = rac.rope_prerotate(qd, kd, 500000.0)
+    q2, k2 = qd.clone(), kd.clone()
+    rac.rope_prerotate(q2, k2, 500000.0, q_rot=q2, k_rot=k2)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, qr) and torch.equal(k2, kr)
+
+
+def test_prerotate_long_positions_sampled():
+    # positions up to 32767: the fp64-formed table angles keep the fp32 rotation accurate
+    B, H, N, D, dt, base = 1, 2, 32768, 64, "fp16", 10000.0
+    (q, k, _), (qd, kd, _) = _inputs(B, H, H, N, D, dt, key=(103,))
+    qr, _ = rac.rope_prerotate(qd, kd, base)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 8), np.arange(N - 300, N)])
+    _check_rotation(bits(qr)[0, 1, rows], inputs.bits(q)[0, 1, rows], rows, dt, base)
+
+
+# ---------------------------------------------------------------------------
+# attention kernels on small shapes, against the full oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_attn_causal_on_rotated_inputs(shape):
+    """attn_causal_fwd alone: its inputs are the oracle's own rounded rotation."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    (q, k, v), _ = _inputs(B, Hq, Hkv, N, D, dt, key=(104, N, D))
+    qr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(inputs.bits(q), dt), base), dt)
+    kr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(inputs.bits(k), dt), base), dt)
+    tdt = inputs.TORCH_DTYPES[dt]
+    qd = torch.from_numpy(qr_bits.view(np.int16)).view(tdt).to(DEV)
+    kd = torch.from_numpy(kr_bits.view(np.int16)).view(tdt).to(DEV)
+    o, l = rac.attn_causal_fwd(qd, kd, v.to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(oracle.decode(qr_bits, dt), oracle.decode(kr_bits, dt),
+                              oracle.decode(inputs.bits(v), dt))
+    assert_o(to_f64(o), ro, "attn_causal_fwd")
+    assert_lse(to_f64(l), rl, "attn_causal_fwd")
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+@pytest.mark.parametrize("path", ["fused", "prerotate"])
+def test_path_matches_oracle(shape, path):
+    B, Hq, Hkv, N, D, dt, base = shape
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(105, N, D))
+    if path == "fused":
+        o, l = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    else:
+        o, l = rac.prerotate_path(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    ro, rl, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="rounded")
+    eo, el, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="exact")
+    og, lg = to_f64(o), to_f64(l)
+    assert_o(og, ro, path + " vs rounded-rotation oracle")
+    assert_o(og, eo, path + " vs exact-rotation oracle")
+    assert_lse(lg, rl, path + " LSE vs rounded-rotation oracle")
+    # against the exact rotation the LSE moves by the operand rounding only
+    assert float(np.max(np.abs(lg - el))) < 2e-2
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_fused_and_prerotate_paths_agree(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    _, (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(106, N, D))
+    of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    op, lp = rac.prerotate_path(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    assert_o(to_f64(of), to_f64(op), "fused vs prerotate")
+    assert_lse(to_f64(lf), to_f64(lp), "fused vs prerotate")
+    # both paths hand identical rotated operands to the same attention arithmetic
+    assert torch.equal(of, op) and torch.equal(lf, lp)
+
+
+ODD_N = [1, 2, 3, 17, 63, 64, 65, 127, 129, 300]
+
+
+@pytest.mark.parametrize("N", ODD_N)
+@pytest.mark.parametrize("D,dt,ratio", [(64, "bf16", 1), (128, "fp16", 4), (128, "bf16", 2),
+                                        (64, "fp16", 8)])
+def test_ragged_lengths_and_gqa(N, D, dt, ratio):
+    B, Hkv = 1, 2
+    Hq = Hkv * ratio
+    base = 10000.0
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(107, N, D, ratio))
+    o, l = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    ro, rl, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt, base)
+    assert_o(to_f64(o), ro, "fused N=%d" % N)
+    assert_lse(to_f64(l), rl, "fused N=%d" % N)
+
+
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+@pytest.mark.parametrize("path", ["fused", "prerotate"])
+def test_large_sigma_inputs(sigma, path):
+    B, Hq, Hkv, N, D, dt, base = 1, 4, 2, 384, 128, "bf16", 500000.0
+    # q and k ~ N(0, sigma^2) make scores of size ~ sigma^2 and force many
+    # running-max rescales; v stays N(0, 1) so |O| keeps the scale the bounds assume
+    q = inputs.draw((B, Hq, N, D), dt, (108,), 0, sigma)
+    k = inputs.draw((B, Hkv, N, D), dt, (108,), 1, sigma)
+    v = inputs.draw((B, Hkv, N, D), dt, (108,), 2)
+    fn = rac.attn_rope_causal_fwd if path == "fused" else rac.prerotate_path
+    o, l = fn(q.to(DEV), k.to(DEV), v.to(DEV), base)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+    ro, rl, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt, base)
+    assert_o(to_f64(o), ro, "sigma=%g" % sigma)
+    lerr = float(np.max(np.abs(to_f64(l) - rl)))
+    print("sigma=%g %s: max|dLSE|=%.3e (|LSE| up to %.1f)" % (sigma, path, lerr,
+                                                              float(np.max(np.abs(rl)))))
+    # The 1e-3 LSE bound is for N(0,1) inputs. Here scores reach |s| ~ 300: the
+    # fp32 accumulation of each D-term score carries an absolute error of a few
+    # fp32 ulps of the score, which the LSE inherits, so the bound grows with
+    # the largest |LSE| (2^-16 relative: ~16x the fp32 unit roundoff's 2^-24 * sqrt(D)).
+    assert lerr <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
+
+
+def test_deterministic():
+    _, (qd, kd, vd) = _inputs(1, 8, 2, 777, 128, "bf16", key=(109,))
+    a = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)
+    b = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)
+    c = rac.prerotate_path(qd, kd, vd, 500000.0)
+    d = rac.prerotate_path(qd, kd, vd, 500000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
+
+
+def test_lse_optional_and_side_stream():
+    _, (qd, kd, vd) = _inputs(1, 4, 4, 200, 64, "fp16", key=(110,))
+    o1, l1 = rac.attn_rope_causal_fwd(qd, kd, vd, 10000.0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = rac.attn_rope_causal_fwd(qd, kd, vd, 10000.0, want_lse=False)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+def test_empty_inputs():
+    for shape in ((1, 4, 0, 64), (0, 4, 16, 64)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        o, l = rac.attn_rope_causal_fwd(x, x, x, 10000.0)
+        o2, l2 = rac.attn_causal_fwd(x, x, x)
+        qr, kr = rac.rope_prerotate(x, x, 10000.0)
+        assert o.shape == shape and l.shape == shape[:3] and qr.shape == shape
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, the launch configuration the bench times
+# ---------------------------------------------------------------------------
+
+FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
+        "mha_d64_fp16_n2048", "mha_d64_fp16_n8192", "mha_d64_fp16_n32768"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    w = inputs.WORKLOADS[name]
+    B, Hq, Hkv, N, D, dt, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"], w["base"]
+    print("full-size case %s" % name, flush=True)
+    q, k, v = inputs.workload_qkv(name)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    op, lp = rac.prerotate_path(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    assert torch.equal(of, op) and torch.equal(lf, lp)
+    rng = np.random.default_rng(len(name))
+    rows = sampled_rows(B, Hq, N, rng)
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    ref_r = oracle_rows(qb, kb, vb, dt, base, Hq, Hkv, rows, "rounded")
+    ref_e = oracle_rows(qb, kb, vb, dt, base, Hq, Hkv, rows, "exact")
+    og = to_f64(of)
+    lg = to_f64(lf)
+    got = np.concatenate([og[b, h, r] for (b, h), r in rows.items()])
+    gl = np.concatenate([lg[b, h, r] for (b, h), r in rows.items()])
+    ro = np.concatenate([ref_r[bh][0] for bh in rows])
+    rl = np.concatenate([ref_r[bh][1] for bh in rows])
+    eo = np.concatenate([ref_e[bh][0] for bh in rows])
+    assert_o(got, ro, name + " vs rounded-rotation oracle")
+    assert_o(got, eo, name + " vs exact-rotation oracle")
+    assert_lse(gl, rl, name + " LSE")
+    mx, rel = o_errors(got, ro)
+    print("%s: rows=%d max|dO|=%.3e relL2=%.3e" % (name, got.shape[0], mx, rel), flush=True)

@@ -20,7 +20,8 @@ Also printed in the same JSON line:
     workload (rotation + causal attention), in the same unit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-       [--no-cpu] [--only fused|prerotate|rope|attn] [--copy-calib]
+       [--no-cpu] [--only fused|prerotate|rope|attn [--workload NAME]]
+       [--copy-calib]
 """
 import argparse
 import json
@@ -55,6 +56,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["fused", "prerotate", "rope", "attn"], default=None,
                     help="time one kernel/path alone (for profiler runs)")
+    ap.add_argument("--workload", default=MAIN,
+                    help="workload of the --only runs (a name from inputs.WORKLOADS)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a plain 256 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -80,9 +83,10 @@ def main():
         print(json.dumps({"copy_calib_bytes": 256 << 20, "launches": 5}))
         return
 
-    w = inputs.WORKLOADS[MAIN]
+    name = args.workload if args.only else MAIN
+    w = inputs.WORKLOADS[name]
     B, Hq, Hkv, N, D, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["base"]
-    q, k, v = inputs.workload_qkv(MAIN)
+    q, k, v = inputs.workload_qkv(name)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out_f = torch.empty_like(qd)
     out_p = torch.empty_like(qd)
@@ -113,7 +117,7 @@ def main():
             fn()
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"only": args.only, "workload": MAIN, "ms_per_call": dt * 1e3}))
+        print(json.dumps({"only": args.only, "workload": name, "ms_per_call": dt * 1e3}))
         return
 
     # ---- the timed region: K steps of the whole hot path ----

@@ -56,6 +56,12 @@
  * and return without synchronising; a fault inside a kernel surfaces at the
  * caller's next synchronisation. No C++ exception crosses this boundary.
  *
+ * Launch shape: the attention kernels pick between a load-balanced launch
+ * that pairs light and heavy causal query tiles in one workgroup and one
+ * workgroup per query tile, by problem size. The environment variable
+ * RAC_ATTN_SHAPE=pair|tile forces one of them (results are identical up to
+ * floating-point summation order); any other value, or none, means automatic.
+ *
  * Library-owned memory: the cos/sin table for each (device, D, rope_base),
  * fp32 [capacity, D], grown on demand. The first call that needs a new or
  * larger table allocates it and uploads it synchronously (so warm up before

@@ -3,28 +3,49 @@
 //
 // Method: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (rainbus digest), background "FlashAttention and online softmax"
-// and the forward Algorithm 1: one workgroup per query tile walks the key
-// tiles, keeps the running row maximum m and denominator l on chip, and writes
+// and the forward Algorithm 1: a block of query rows walks the key tiles,
+// keeps the running row maximum m and denominator l on chip, and writes
 // o = u / l and the log-sum-exp L. The digest's precision design is kept:
 // fp32 statistics and accumulators, base-2 exponent. The fused variant is the
 // single kernel of "AttnFuse Makes RoPE a First-Class Attention Compilation
-// Operation", paragraph 3 ("in-kernel rotation"): the query tile is rotated
-// once when loaded, and every key tile is rotated each time a workgroup loads
-// it -- the compute-and-tiling cost that paragraph contrasts with pre-rotation.
+// Operation", paragraph 3 ("in-kernel rotation"): query rows are rotated once
+// when loaded, and every key tile is rotated each time a workgroup loads it --
+// the compute-and-tiling cost that paragraph contrasts with pre-rotation.
 //
 // gfx950 mapping (64-lane waves, v_mfma_f32_32x32x16 bf16/fp16):
-//   * workgroup = 4 waves = BM = 128 query rows of one (b, query head);
+//   * A "row block" is 4 waves = BM = 128 query rows of one (b, query head);
 //     wave w owns rows q0 + 32w .. +31, lane (n, hh) = (lane % 32, lane / 32).
 //   * Scores are computed transposed, S^T = K Q^T: A = K tile from LDS
-//     (row = key), B = the wave's Q rows kept in registers for the whole loop.
-//     The fp32 result puts one query per lane column, so row statistics need
+//     (row = key), B = the wave's Q rows, kept in registers for the whole loop.
+//     The fp32 result holds one query per lane column, so row statistics need
 //     only in-lane reductions plus one exchange between the two lane halves.
 //   * O^T = V^T P^T: the P^T accumulator registers are reused directly as the
-//     B operand (the key order inside each 16-key step is permuted, and V^T is
-//     stored in LDS in that same permuted order), A = V^T from LDS.
-//   * Key tiles of BN = 64 rows; tiles past the wave's last query are skipped
-//     and only tiles straddling the diagonal are masked.
-//   * Workgroups with the most key tiles (the last query tiles) launch first.
+//     B operand (the key order inside each 16-key step is permuted); the V^T
+//     operand comes from the row-major V tile through the LDS transpose read
+//     (ds_read_b64_tr_b16), gathering keys in that same permuted order.
+//   * Key tiles of BN = 64 rows, double-buffered in LDS with one barrier per
+//     tile; the next tile's K/V are loaded into registers while the current
+//     tile is computed (the cos/sin rows are read when a K tile is stored to
+//     LDS and rotated). Tiles past a wave's last query are skipped and only
+//     tiles straddling the diagonal are masked.
+//   * Running-max updates are lazy: a row keeps its maximum until a tile
+//     raises it by more than 2^8, so most tiles skip the accumulator rescale;
+//     probabilities stay <= 2^8 and the final o = u / l and L are unchanged.
+//
+// Two launch shapes share that per-wave core:
+//   * attn_pair_kernel (the default): causal rows see a prefix of the keys, so
+//     query tile t costs ~t+1 key-tile steps. A workgroup of 8 waves takes the
+//     light tile p and its mirror T-1-p; half A (waves 0-3) runs the heavy
+//     tile over the first X key tiles, half B (waves 4-7) runs the light tile
+//     and then the heavy tile's remaining key tiles, X chosen so both halves
+//     take the same number of steps. The two partial softmax states of the
+//     heavy rows are merged through LDS at the end. Every workgroup then does
+//     the same work, so a grid of one workgroup per CU finishes together.
+//   * attn_fwd_kernel: one 4-wave workgroup per query tile, heaviest first;
+//     used when there are too few tile pairs to fill the chip.
+//   Both use a 1-D grid whose consecutive workgroups on one XCD (the hardware
+//   deals workgroup ids round-robin over 8 XCDs) share a key/value head, so
+//   each XCD's L2 serves one K/V head to all its readers.
 #include <math.h>
 
 #include "rac_device.h"
@@ -34,144 +55,178 @@ namespace rac {
 
 constexpr int BM = 128;
 constexpr int BN = 64;
-constexpr int NWAVES = 4;
-constexpr int THREADS = NWAVES * 64;
-constexpr int VT_PAD = 8;  // elements of padding per V^T row
+constexpr int NXCD = 8;
+constexpr int NUM_CUS = 256;
+constexpr float LAZY_RESCALE_LOG2 = 8.0f;
+constexpr float LN2 = 0.69314718055994530942f;
 
-// Slot of key r (0..BN-1) inside the V^T row: bits 2 and 3 of the key index
-// are swapped. With that order the 8 keys a lane half feeds to one PV MFMA step
-// sit contiguously, matching where the score MFMA left their probabilities.
-__device__ __forceinline__ int vt_slot(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed LDS read: in each 16-lane group, lane i receives element i%4 of
+// the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+template <int D>
+struct Tile {
+    static constexpr int KS = D + 8;    // K row stride (elements): 16 B pad, conflict-free A reads
+    static constexpr int VS = D + 32;   // V row stride: 64 B pad, conflict-free transpose reads
+    static constexpr int K_ELEMS = BN * KS;
+    static constexpr int V_ELEMS = BN * VS;
+    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
+    static constexpr int LOADS = BN * CHUNKS / 256;      // per thread of a 256-thread block
+};
+
+// Number of key tiles query tile `qt` needs (keys 0 .. its last row).
+__device__ __forceinline__ int kv_tiles_of(int qt, int N) {
+    return (min(qt * BM + BM, N) - 1) / BN + 1;
+}
+
+// Staging of one K/V tile by a 256-thread block: global -> registers -> LDS.
 template <int DT, int D, bool ROPE>
-__global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ table, int Hq, int Hkv, int N, float scale_log2) {
-    typedef Fmt<DT> F;
-    typedef typename F::vec8 vec8;
-    constexpr int KS_STRIDE = D + 8;    // elements per K row in LDS (padding vs bank conflicts)
-    constexpr int VT_STRIDE = BN + VT_PAD;
-    constexpr int QCH = D / 16;         // 16-deep MFMA steps over the head dim
-    constexpr int DBLK = D / 32;        // 32-row blocks of O^T
-    constexpr int CHUNKS = D / 8;       // 16-byte chunks per row
-    constexpr int LOAD_ITERS = BN * CHUNKS / THREADS;
+struct TileStage {
+    typedef Tile<D> T;
+    u32x4 kreg[T::LOADS], vreg[T::LOADS];
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VT_STRIDE];
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int n = lane & 31;
-    const int hh = lane >> 5;
-
-    const int qtile = gridDim.x - 1 - blockIdx.x;  // heaviest tiles first
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
-    const int g = h / (Hq / Hkv);
-    const int q0 = qtile * BM;
-    const int qw0 = q0 + wave * 32;       // first query row of this wave
-    const int my_q = qw0 + n;
-
-    const int64_t q_head = ((int64_t)b * Hq + h) * N;
-    const int64_t kv_head = ((int64_t)b * Hkv + g) * N;
-
-    // ---- this wave's Q rows as MFMA B operands (rotated once if ROPE) ----
-    vec8 qf[QCH];
+    __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int t,
+                                         int N, int tid) {
+        const int k0 = t * BN;
 #pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (my_q < N) {
-            const int d0 = 16 * c + 8 * hh;
-            w = *reinterpret_cast<const u32x4*>(q + (q_head + my_q) * D + d0);
-            if (ROPE) {
-                const f32x4* t = reinterpret_cast<const f32x4*>(table + (int64_t)my_q * D + d0);
-                w = rope_rotate8<DT>(w, t[0], t[1]);
+        for (int it = 0; it < T::LOADS; ++it) {
+            const int idx = tid + it * 256;
+            const int r = idx / T::CHUNKS;
+            const int cc = idx % T::CHUNKS;
+            const int key = k0 + r;
+            if (key < N) {
+                kreg[it] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * D + cc * 8);
+                vreg[it] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * D + cc * 8);
+            } else {
+                kreg[it] = u32x4{0u, 0u, 0u, 0u};
+                vreg[it] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-        qf[c] = as_vec8<DT>(w);
     }
 
-    f32x16 acc[DBLK];
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
-    float m_run = -INFINITY;  // running max of the base-2 scaled scores
-    float l_run = 0.f;        // this lane half's share of the denominator
-
-    const int last_row = min(q0 + BM, N) - 1;
-    const int n_tiles = last_row / BN + 1;
-    const int wave_last = min(qw0 + 31, N - 1);
-    const int wave_tiles = qw0 < N ? wave_last / BN + 1 : 0;
-
-    for (int t = 0; t < n_tiles; ++t) {
+    // The cos/sin rows of a key tile are read here, when the tile is stored,
+    // rather than staged with K/V: they come from L2 (the table is small and
+    // shared by every head) and keeping them out of the staging registers
+    // keeps the D = 128 kernels within 256 VGPRs (two waves per SIMD).
+    __device__ __forceinline__ void store(uint16_t* Ks, const float* __restrict__ table, int t,
+                                          int N, int tid) {
+        uint16_t* Vs = Ks + T::K_ELEMS;
         const int k0 = t * BN;
-        __syncthreads();  // previous tile fully consumed
-        // ---- K tile -> LDS (rotated if ROPE), V tile -> LDS transposed ----
 #pragma unroll
-        for (int it = 0; it < LOAD_ITERS; ++it) {
-            const int idx = tid + it * THREADS;
-            const int r = idx / CHUNKS;
-            const int cc = idx % CHUNKS;
-            const int key = k0 + r;
-            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            if (key < N) {
-                kw = *reinterpret_cast<const u32x4*>(k + (kv_head + key) * D + cc * 8);
-                vw = *reinterpret_cast<const u32x4*>(v + (kv_head + key) * D + cc * 8);
+        for (int it = 0; it < T::LOADS; ++it) {
+            const int idx = tid + it * 256;
+            const int r = idx / T::CHUNKS;
+            const int cc = idx % T::CHUNKS;
+            u32x4 kw = kreg[it];
+            if (ROPE && k0 + r < N) {
+                const f32x4* tb =
+                    reinterpret_cast<const f32x4*>(table + (int64_t)(k0 + r) * D + cc * 8);
+                kw = rope_rotate8<DT>(kw, tb[0], tb[1]);
+            }
+            *reinterpret_cast<u32x4*>(Ks + r * T::KS + cc * 8) = kw;
+            *reinterpret_cast<u32x4*>(Vs + r * T::VS + cc * 8) = vreg[it];
+        }
+    }
+};
+
+// Per-wave flash-attention state for 32 query rows and its per-tile step.
+template <int DT, int D, bool ROPE>
+struct WaveAttn {
+    typedef Fmt<DT> F;
+    typedef typename F::vec8 vec8;
+    typedef Tile<D> T;
+    static constexpr int QCH = D / 16;   // 16-deep MFMA steps over the head dim
+    static constexpr int DBLK = D / 32;  // 32-row blocks of O^T
+
+    vec8 qf[QCH];
+    f32x16 acc[DBLK];
+    float m_run;  // running max of the base-2 scaled scores (lazy)
+    float l_run;  // this lane half's share of the denominator
+
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+        m_run = -INFINITY;
+        l_run = 0.f;
+    }
+
+    // The wave's Q rows as MFMA B operands (rotated once if ROPE).
+    __device__ __forceinline__ void load_q(const uint16_t* qrow0, const float* __restrict__ table,
+                                           int my_q, int N, int hh) {
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (my_q < N) {
+                const int d0 = 16 * c + 8 * hh;
+                w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)my_q * D + d0);
                 if (ROPE) {
-                    const f32x4* tb =
-                        reinterpret_cast<const f32x4*>(table + (int64_t)key * D + cc * 8);
-                    kw = rope_rotate8<DT>(kw, tb[0], tb[1]);
+                    const f32x4* t =
+                        reinterpret_cast<const f32x4*>(table + (int64_t)my_q * D + d0);
+                    w = rope_rotate8<DT>(w, t[0], t[1]);
                 }
             }
-            *reinterpret_cast<u32x4*>(&Ks[r * KS_STRIDE + cc * 8]) = kw;
-            const int slot = vt_slot(r);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Vt[(cc * 8 + 2 * e) * VT_STRIDE + slot] = (uint16_t)(vw[e] & 0xffffu);
-                Vt[(cc * 8 + 2 * e + 1) * VT_STRIDE + slot] = (uint16_t)(vw[e] >> 16);
-            }
+            qf[c] = as_vec8<DT>(w);
         }
-        __syncthreads();
-        if (t >= wave_tiles) continue;  // wave-uniform: every key here is above the diagonal
+    }
 
-        // ---- S^T = K Q^T for two 32-key blocks ----
+    // One key tile (k0 .. k0+63) from LDS. MASK: the tile straddles the
+    // diagonal of the wave's rows, so keys above a row's position are masked.
+    template <bool MASK>
+    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int my_q, int n, int hh,
+                                         int v_lane_off, float scale_log2) {
+        const uint16_t* Vs = Ks + T::K_ELEMS;
+        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores)
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
 #pragma unroll
-            for (int c = 0; c < QCH; ++c) {
+        for (int c = 0; c < QCH; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(
-                    &Ks[(32 * kb + n) * KS_STRIDE + 16 * c + 8 * hh]);
+                    Ks + (32 * kb + n) * T::KS + 16 * c + 8 * hh);
                 s[kb] = F::mfma(as_vec8<DT>(a), qf[c], s[kb]);
             }
-        }
 
-        // ---- online softmax (base 2); lane holds query my_q, 32 keys ----
-        const bool diag = k0 + BN - 1 > qw0;  // wave-uniform
+        // online softmax (base 2); lane holds query my_q and 32 of the keys.
+        // The row maximum is taken on raw scores (the scale is positive) and
+        // the scale is folded into the exponent's fused multiply-add.
+        if (MASK) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    if (key > my_q) s[kb][j] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float x = s[kb][j] * scale_log2;
-                if (diag) {
-                    const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    if (key > my_q) x = -INFINITY;
-                }
-                s[kb][j] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        const float m_new = mx > m_run + LAZY_RESCALE_LOG2 ? mx : m_run;
+        if (__any(m_new != m_run)) {  // wave-uniform branch
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+        }
+        const float neg_m = -m_run;
         float psum = 0.f;
         u32x4 pw[2][2];
 #pragma unroll
@@ -180,57 +235,284 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
             for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int t2 = 0; t2 < 4; ++t2) {
-                    const float p0 = exp2f(s[kb][8 * e + 2 * t2] - m_new);
-                    const float p1 = exp2f(s[kb][8 * e + 2 * t2 + 1] - m_new);
+                    const float p0 = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(s[kb][8 * e + 2 * t2], scale_log2, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(s[kb][8 * e + 2 * t2 + 1], scale_log2, neg_m));
                     psum += p0 + p1;
                     pw[kb][e][t2] = F::pack2(p0, p1);
                 }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
+        l_run += psum;
 
-        // ---- O^T += V^T P^T ----
+        // O^T += V^T P^T
 #pragma unroll
-        for (int i = 0; i < DBLK; ++i)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int e = 0; e < 2; ++e) {
+                const vec8 pb = as_vec8<DT>(pw[kb][e]);
+                const uint16_t* vp = Vs + v_lane_off + (32 * kb + 16 * e) * T::VS;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        &Vt[(32 * i + n) * VT_STRIDE + 32 * kb + 16 * e + 8 * hh]);
-                    acc[i] = F::mfma(as_vec8<DT>(a), as_vec8<DT>(pw[kb][e]), acc[i]);
+                for (int i = 0; i < DBLK; ++i) {
+                    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 32 * i));
+                    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * T::VS + 32 * i));
+                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                    acc[i] = F::mfma(as_vec8<DT>(a), pb, acc[i]);
                 }
+            }
     }
 
-    // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----
-    if (wave_tiles == 0 || my_q >= N) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = out + (q_head + my_q) * D;
+    // O = acc / l and LSE = ln2 * (m + log2 l) for the wave's row.
+    // l_tot is the full denominator (both lane halves).
+    __device__ __forceinline__ void write(uint16_t* orow, float* lse_row, float l_tot, int hh) {
+        const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i)
+        for (int i = 0; i < DBLK; ++i)
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-            const int d0 = 32 * i + 8 * grp + 4 * hh;
-            u32x2 w;
-            w[0] = F::pack2(acc[i][4 * grp] * inv, acc[i][4 * grp + 1] * inv);
-            w[1] = F::pack2(acc[i][4 * grp + 2] * inv, acc[i][4 * grp + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + d0) = w;
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = 32 * i + 8 * gq + 4 * hh;
+                u32x2 w;
+                w[0] = F::pack2(acc[i][4 * gq] * inv, acc[i][4 * gq + 1] * inv);
+                w[1] = F::pack2(acc[i][4 * gq + 2] * inv, acc[i][4 * gq + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + d0) = w;
+            }
+        if (lse_row != nullptr && hh == 0) *lse_row = (m_run + __log2f(l_tot)) * LN2;
+    }
+};
+
+// Decodes a 1-D work-unit index: XCD-aware order, (b, kv head) major, then
+// the per-head index, then the query head inside its GQA group.
+struct Unit {
+    int b, g, h, idx;  // idx = query tile slot (unpaired) or pair index
+};
+__device__ __forceinline__ Unit decode_unit(int Hq, int Hkv, int per_head) {
+    const int group = Hq / Hkv;
+    const int units = gridDim.x;
+    int u = blockIdx.x;
+    if (units % NXCD == 0) u = (u % NXCD) * (units / NXCD) + u / NXCD;
+    Unit r;
+    const int hg = u % group;
+    const int rest = u / group;
+    r.idx = rest % per_head;
+    const int bg = rest / per_head;
+    r.g = bg % Hkv;
+    r.b = bg / Hkv;
+    r.h = r.g * group + hg;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// One 4-wave workgroup per query tile (heaviest first).
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool ROPE>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, float scale_log2) {
+    typedef Tile<D> T;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+    const int grp = lane >> 4, j16 = lane & 15;
+    const int v_lane_off = ((grp >> 1) * 4 + (j16 >> 2)) * T::VS + 16 * (grp & 1) + 4 * (j16 & 3);
+
+    const Unit un = decode_unit(Hq, Hkv, n_qtiles);
+    const int qtile = n_qtiles - 1 - un.idx;
+    const int q0 = qtile * BM;
+    const int qw0 = q0 + wave * 32;
+    const int my_q = qw0 + n;
+    const int64_t q_head = ((int64_t)un.b * Hq + un.h) * N;
+    const int64_t kv_head = ((int64_t)un.b * Hkv + un.g) * N;
+    const uint16_t* kbase = k + kv_head * D;
+    const uint16_t* vbase = v + kv_head * D;
+
+    WaveAttn<DT, D, ROPE> st;
+    st.load_q(q + q_head * D, table, my_q, N, hh);
+    st.reset();
+
+    const int n_tiles = kv_tiles_of(qtile, N);
+    const int wave_tiles = qw0 < N ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
+
+    TileStage<DT, D, ROPE> stage;
+    stage.load(kbase, vbase, 0, N, tid);
+    for (int t = 0; t < n_tiles; ++t) {
+        uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
+        stage.store(Ks, table, t, N, tid);
+        if (t + 1 < n_tiles) stage.load(kbase, vbase, t + 1, N, tid);
+        __syncthreads();  // tile t visible; the other buffer is no longer read
+        if (t < wave_tiles) {
+            if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
+                st.template step<true>(Ks, t * BN, my_q, n, hh, v_lane_off, scale_log2);
+            else
+                st.template step<false>(Ks, t * BN, my_q, n, hh, v_lane_off, scale_log2);
         }
-    if (lse != nullptr && hh == 0)
-        lse[q_head + my_q] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    }
+    if (wave_tiles == 0 || my_q >= N) return;
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+}
+
+// ---------------------------------------------------------------------------
+// Paired, split, load-balanced launch: 8 waves per workgroup.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool ROPE>
+__global__ __launch_bounds__(512, 1) void attn_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, int n_pairs,
+    float scale_log2) {
+    typedef Tile<D> T;
+    typedef WaveAttn<DT, D, ROPE> W;
+    // per half: two tile buffers; after the loop the same memory holds the merge data
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * T::BUF_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int half = tid >> 8;       // 0 = A, 1 = B
+    const int htid = tid & 255;      // thread index inside the half
+    const int wave = htid >> 6;      // wave inside the half
+    const int lane = tid & 63;
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+    const int grp = lane >> 4, j16 = lane & 15;
+    const int v_lane_off = ((grp >> 1) * 4 + (j16 >> 2)) * T::VS + 16 * (grp & 1) + 4 * (j16 & 3);
+
+    const Unit un = decode_unit(Hq, Hkv, n_pairs);
+    const int p = un.idx;
+    const int t_heavy = n_qtiles - 1 - p;
+    const int t_light = p;                     // == t_heavy for the middle tile of an odd count
+    const int len_h = kv_tiles_of(t_heavy, N);
+    const int len_l = t_light < t_heavy ? kv_tiles_of(t_light, N) : 0;
+    const int split = (len_l + len_h + 1) / 2;  // heavy key tiles [0, split) go to half A
+    const int steps = split;                     // half B needs len_l + len_h - split <= split
+
+    const int64_t q_head = ((int64_t)un.b * Hq + un.h) * N;
+    const int64_t kv_head = ((int64_t)un.b * Hkv + un.g) * N;
+    const uint16_t* qhead = q + q_head * D;
+    const uint16_t* kbase = k + kv_head * D;
+    const uint16_t* vbase = v + kv_head * D;
+
+    // job of this half at step i: the key tile (or -1 for none) and its query tile
+    auto job_tile = [&](int i, int& qt) -> int {
+        if (half == 0) {
+            qt = t_heavy;
+            return i < split ? i : -1;
+        }
+        if (i < len_l) {
+            qt = t_light;
+            return i;
+        }
+        qt = t_heavy;
+        const int j = split + (i - len_l);
+        return j < len_h ? j : -1;
+    };
+
+    W st;
+    st.reset();
+    int cur_qt = -1;   // query tile whose rows this wave holds
+    int qw0 = 0, my_q = 0, wave_tiles = 0;
+
+    uint16_t* hbuf = smem + half * 2 * T::BUF_ELEMS;
+    TileStage<DT, D, ROPE> stage;
+    {
+        int qt;
+        const int kt = job_tile(0, qt);
+        if (kt >= 0) stage.load(kbase, vbase, kt, N, htid);
+    }
+    for (int i = 0; i < steps; ++i) {
+        int qt;
+        const int kt = job_tile(i, qt);
+        uint16_t* Ks = hbuf + (i & 1) * T::BUF_ELEMS;
+        if (kt >= 0) stage.store(Ks, table, kt, N, htid);
+        int qt1;
+        const int kt1 = job_tile(i + 1, qt1);
+        if (i + 1 < steps && kt1 >= 0) stage.load(kbase, vbase, kt1, N, htid);
+        if (kt >= 0 && qt != cur_qt) {
+            // half B moving from the light rows to the heavy rows: finish the light rows
+            if (cur_qt >= 0 && wave_tiles > 0 && my_q < N) {
+                const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+                st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+            }
+            cur_qt = qt;
+            qw0 = qt * BM + wave * 32;
+            my_q = qw0 + n;
+            wave_tiles = qw0 < N ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
+            st.load_q(qhead, table, my_q, N, hh);
+            st.reset();
+        }
+        __syncthreads();  // tile i visible to this half; the other buffer is no longer read
+        if (kt >= 0 && kt < wave_tiles) {
+            if (kt * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
+                st.template step<true>(Ks, kt * BN, my_q, n, hh, v_lane_off, scale_log2);
+            else
+                st.template step<false>(Ks, kt * BN, my_q, n, hh, v_lane_off, scale_log2);
+        }
+    }
+
+    // half B: if its last rows were the light ones, they are complete now
+    if (half == 1 && cur_qt == t_light && t_light != t_heavy) {
+        if (wave_tiles > 0 && my_q < N) {
+            const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+            st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+        }
+        st.reset();  // no share of the heavy rows
+    }
+
+    // ---- merge the two halves' partial states of the heavy rows ----
+    __syncthreads();  // every wave is done with the tile buffers
+    constexpr int SLOTS = 16 * W::DBLK + 2;
+    float* my = reinterpret_cast<float*>(smem) + (wave * SLOTS) * 64 + lane;  // [wave][slot][lane]
+    const float l_half = st.l_run + __shfl_xor(st.l_run, 32);
+    if (half == 1) {
+#pragma unroll
+        for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) my[(16 * i + j) * 64] = st.acc[i][j];
+        my[(16 * W::DBLK) * 64] = st.m_run;
+        my[(16 * W::DBLK + 1) * 64] = l_half;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const int hq = t_heavy * BM + wave * 32 + n;  // this lane's heavy row
+    if (hq >= N) return;
+    const float m_b = my[(16 * W::DBLK) * 64];
+    const float l_b = my[(16 * W::DBLK + 1) * 64];
+    const float m = fmaxf(st.m_run, m_b);
+    const float a_a = __builtin_amdgcn_exp2f(st.m_run - m);
+    const float a_b = l_b > 0.f ? __builtin_amdgcn_exp2f(m_b - m) : 0.f;
+#pragma unroll
+    for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.acc[i][j] = st.acc[i][j] * a_a + my[(16 * i + j) * 64] * a_b;
+    st.m_run = m;
+    const float l_tot = l_half * a_a + l_b * a_b;
+    st.write(out + (q_head + hq) * D, lse ? lse + q_head + hq : nullptr, l_tot, hh);
 }
 
 template <int DT, int D, bool ROPE>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    dim3 grid((unsigned)((a.N + BM - 1) / BM), (unsigned)a.Hq, (unsigned)a.B);
-    attn_fwd_kernel<DT, D, ROPE><<<grid, THREADS, 0, stream>>>(
-        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-        a.Hq, a.Hkv, a.N, scale_log2);
+    const int n_qtiles = (a.N + BM - 1) / BM;
+    const int n_pairs = (n_qtiles + 1) / 2;
+    const int64_t pair_units = (int64_t)n_pairs * a.Hq * a.B;
+    const int64_t tile_units = (int64_t)n_qtiles * a.Hq * a.B;
+    if (tile_units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    bool pair = pair_units >= NUM_CUS && n_qtiles >= 2;
+    if (a.shape == ATTN_SHAPE_PAIR) pair = true;
+    if (a.shape == ATTN_SHAPE_TILE) pair = false;
+    if (pair) {
+        attn_pair_kernel<DT, D, ROPE><<<dim3((unsigned)pair_units), 512, 0, stream>>>(
+            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
+            a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
+    } else {
+        attn_fwd_kernel<DT, D, ROPE><<<dim3((unsigned)tile_units), 256, 0, stream>>>(
+            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
+            a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
+    }
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -144,6 +145,15 @@ int check_attn_ptrs(const void* q, const void* k, const void* v, const void* out
     return RAC_OK;
 }
 
+// RAC_ATTN_SHAPE=pair|tile forces the attention launch shape (default: by size).
+int attn_shape_from_env() {
+    const char* e = getenv("RAC_ATTN_SHAPE");
+    if (!e) return rac::ATTN_SHAPE_AUTO;
+    if (!strcmp(e, "pair")) return rac::ATTN_SHAPE_PAIR;
+    if (!strcmp(e, "tile")) return rac::ATTN_SHAPE_TILE;
+    return rac::ATTN_SHAPE_AUTO;
+}
+
 int hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(RAC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -164,7 +174,7 @@ int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out,
     if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
-    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype};
+    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
     return hip_status(rac::launch_attn_fwd(a, true, static_cast<hipStream_t>(stream)),
                       "attn_rope_causal_fwd launch");
 }
@@ -176,7 +186,7 @@ int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, floa
     if (rc != RAC_OK) return rc;
     if (empty) return ok();
     if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
-    rac::AttnArgs a{q, k, v, out, lse, nullptr, B, Hq, Hkv, N, D, dtype};
+    rac::AttnArgs a{q, k, v, out, lse, nullptr, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
     return hip_status(rac::launch_attn_fwd(a, false, static_cast<hipStream_t>(stream)),
                       "attn_causal_fwd launch");
 }

@@ -15,6 +15,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_BF16 = 0, DT_FP16 = 1 };
 
@@ -26,11 +29,9 @@ template <> struct Fmt<DT_BF16> {
     typedef bf16x8 vec8;
     static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-    // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    // two values, round to nearest even, one v_cvt_pk_bf16_f32 (a in the low half)
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-        __bf16 x = (__bf16)a, y = (__bf16)b;
-        return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
     }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -45,11 +46,9 @@ template <> struct Fmt<DT_FP16> {
     static __device__ __forceinline__ float hi(uint32_t w) {
         return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
     }
-    // round to nearest even (v_cvt_f16_f32 in the default rounding mode)
+    // two values, round to nearest even (the default mode), one v_cvt_pk_f16_f32
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-        _Float16 x = (_Float16)a, y = (_Float16)b;
-        return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
     }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);

@@ -7,6 +7,10 @@
 
 namespace rac {
 
+// Launch shape of the attention kernels: chosen from the problem size, or
+// forced (tests cover both shapes on small problems; tuning).
+enum { ATTN_SHAPE_AUTO = 0, ATTN_SHAPE_PAIR = 1, ATTN_SHAPE_TILE = 2 };
+
 struct AttnArgs {
     const void* q;
     const void* k;
@@ -16,6 +20,7 @@ struct AttnArgs {
     const float* table;  // cos/sin table [>= N][D] (fp32, cos/sin interleaved); null when no RoPE
     int B, Hq, Hkv, N, D;
     int dtype;
+    int shape;           // ATTN_SHAPE_*
 };
 
 // Causal attention forward; rotates Q/K tiles in the kernel when `rope`.

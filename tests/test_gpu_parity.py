@@ -31,6 +31,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+@pytest.fixture(params=["auto", "pair", "tile"])
+def launch_shape(request, monkeypatch):
+    """Runs a test under each attention launch shape (RAC_ATTN_SHAPE)."""
+    monkeypatch.setenv("RAC_ATTN_SHAPE", request.param)
+    return request.param
+
+
 def _inputs(B, Hq, Hkv, N, D, dtype, key, sigma=1.0):
     q, k, v = inputs.qkv(B, Hq, Hkv, N, D, dtype, key=key, sigma=sigma)
     return (q, k, v), (q.to(DEV), k.to(DEV), v.to(DEV))
@@ -124,7 +131,7 @@ def test_prerotate_long_positions_sampled():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("shape", SMALL, ids=_id)
-def test_attn_causal_on_rotated_inputs(shape):
+def test_attn_causal_on_rotated_inputs(shape, launch_shape):
     """attn_causal_fwd alone: its inputs are the oracle's own rounded rotation."""
     B, Hq, Hkv, N, D, dt, base = shape
     (q, k, v), _ = _inputs(B, Hq, Hkv, N, D, dt, key=(104, N, D))
@@ -143,7 +150,7 @@ def test_attn_causal_on_rotated_inputs(shape):
 
 @pytest.mark.parametrize("shape", SMALL, ids=_id)
 @pytest.mark.parametrize("path", ["fused", "prerotate"])
-def test_path_matches_oracle(shape, path):
+def test_path_matches_oracle(shape, path, launch_shape):
     B, Hq, Hkv, N, D, dt, base = shape
     (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(105, N, D))
     if path == "fused":
@@ -163,7 +170,7 @@ def test_path_matches_oracle(shape, path):
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=_id)
-def test_fused_and_prerotate_paths_agree(shape):
+def test_fused_and_prerotate_paths_agree(shape, launch_shape):
     B, Hq, Hkv, N, D, dt, base = shape
     _, (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(106, N, D))
     of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
@@ -181,7 +188,7 @@ ODD_N = [1, 2, 3, 17, 63, 64, 65, 127, 129, 300]
 @pytest.mark.parametrize("N", ODD_N)
 @pytest.mark.parametrize("D,dt,ratio", [(64, "bf16", 1), (128, "fp16", 4), (128, "bf16", 2),
                                         (64, "fp16", 8)])
-def test_ragged_lengths_and_gqa(N, D, dt, ratio):
+def test_ragged_lengths_and_gqa(N, D, dt, ratio, launch_shape):
     B, Hkv = 1, 2
     Hq = Hkv * ratio
     base = 10000.0
@@ -195,7 +202,7 @@ def test_ragged_lengths_and_gqa(N, D, dt, ratio):
 
 @pytest.mark.parametrize("sigma", [4.0, 8.0])
 @pytest.mark.parametrize("path", ["fused", "prerotate"])
-def test_large_sigma_inputs(sigma, path):
+def test_large_sigma_inputs(sigma, path, launch_shape):
     B, Hq, Hkv, N, D, dt, base = 1, 4, 2, 384, 128, "bf16", 500000.0
     # q and k ~ N(0, sigma^2) make scores of size ~ sigma^2 and force many
     # running-max rescales; v stays N(0, 1) so |O| keeps the scale the bounds assume
@@ -218,7 +225,7 @@ def test_large_sigma_inputs(sigma, path):
     assert lerr <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
 
 
-def test_deterministic():
+def test_deterministic(launch_shape):
     _, (qd, kd, vd) = _inputs(1, 8, 2, 777, 128, "bf16", key=(109,))
     a = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)
     b = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)

@@ -24,10 +24,11 @@
 //     operand comes from the row-major V tile through the LDS transpose read
 //     (ds_read_b64_tr_b16), gathering keys in that same permuted order.
 //   * Key tiles of BN = 64 rows, double-buffered in LDS with one barrier per
-//     tile; the next tile's K/V are loaded into registers while the current
-//     tile is computed (the cos/sin rows are read when a K tile is stored to
-//     LDS and rotated). Tiles past a wave's last query are skipped and only
-//     tiles straddling the diagonal are masked.
+//     tile. The next tile's K and V go straight from global memory into LDS
+//     (global_load_lds_dwordx4) while the current tile is computed; with RoPE
+//     each thread also prefetches the cos/sin rows of the K chunks it loads
+//     and rotates them in place before the barrier. Tiles past a wave's last
+//     query are skipped and only tiles straddling the diagonal are masked.
 //   * Running-max updates are lazy: a row keeps its maximum until a tile
 //     raises it by more than 2^8, so most tiles skip the accumulator rescale;
 //     probabilities stay <= 2^8 and the final o = u / l and L are unchanged.
@@ -71,69 +72,113 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 
 template <int D>
 struct Tile {
-    static constexpr int KS = D + 8;    // K row stride (elements): 16 B pad, conflict-free A reads
-    static constexpr int VS = D + 32;   // V row stride: 64 B pad, conflict-free transpose reads
-    static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = BN * VS;
+    // K and V tiles are stored unpadded, row = key, as 16-byte chunks whose
+    // position inside the row is XOR-swizzled so that the MFMA operand reads
+    // hit distinct LDS banks (see kswz / vswz).
+    static constexpr int CH = D / 8;                     // 16-byte chunks per row
+    static constexpr int K_ELEMS = BN * D;
+    static constexpr int V_ELEMS = BN * D;
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
-    static constexpr int LOADS = BN * CHUNKS / 256;      // per thread of a 256-thread block
+    static constexpr int INSTR = BN * CH / 256;          // 1 KiB DMA blocks per wave and tensor
 };
+
+// Chunk swizzles. K: the score MFMA reads one chunk column from 16 consecutive
+// rows at once, so rows spread over all chunk positions. V: the transpose read
+// takes 4 adjacent chunks from each of 4 consecutive rows, so rows take
+// disjoint aligned groups of 4 chunks.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 // Number of key tiles query tile `qt` needs (keys 0 .. its last row).
 __device__ __forceinline__ int kv_tiles_of(int qt, int N) {
     return (min(qt * BM + BM, N) - 1) / BN + 1;
 }
 
-// Staging of one K/V tile by a 256-thread block: global -> registers -> LDS.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Loads of one K/V tile by a 4-wave block, straight from global memory into
+// LDS (global_load_lds_dwordx4: lane i of an instruction fills bytes
+// 16i..16i+15 of a 1 KiB block). Block b of a tile holds chunks 64b..64b+63;
+// a lane fetches the global chunk that the swizzle places there. Rows past
+// the sequence end repeat its last row: their scores are masked by causality
+// and their probabilities are zero.
+// With ROPE the K chunks land unrotated; each thread prefetches the cos/sin
+// entries of the chunks it loaded and, once its loads have landed, rotates
+// those chunks in place before the block's barrier.
 template <int DT, int D, bool ROPE>
 struct TileStage {
     typedef Tile<D> T;
-    u32x4 kreg[T::LOADS], vreg[T::LOADS];
+    f32x4 cs[ROPE ? T::INSTR : 1][2];
 
-    __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int t,
-                                         int N, int tid) {
-        const int k0 = t * BN;
-#pragma unroll
-        for (int it = 0; it < T::LOADS; ++it) {
-            const int idx = tid + it * 256;
-            const int r = idx / T::CHUNKS;
-            const int cc = idx % T::CHUNKS;
-            const int key = k0 + r;
-            if (key < N) {
-                kreg[it] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * D + cc * 8);
-                vreg[it] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * D + cc * 8);
-            } else {
-                kreg[it] = u32x4{0u, 0u, 0u, 0u};
-                vreg[it] = u32x4{0u, 0u, 0u, 0u};
-            }
+    // Loads block j (0 <= j < INSTR) of this wave's share: one 1 KiB block of
+    // K, one of V, and (ROPE) the cos/sin entries of the K block.
+    __device__ __forceinline__ void issue_part(int j, uint16_t* buf, const uint16_t* kbase,
+                                               const uint16_t* vbase,
+                                               const float* __restrict__ table, int t, int N,
+                                               int wave, int lane) {
+        const int blk = wave * T::INSTR + j;
+        const int g = blk * 64 + lane;          // chunk index inside the tile
+        const int row = g / T::CH;
+        const int pc = g % T::CH;               // physical chunk position
+        const int key = min(t * BN + row, N - 1);
+        const int64_t krow = (int64_t)key * D;
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(kbase + krow + 8 * (pc ^ kswz<D>(row))),
+            (lds_void*)(buf + blk * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(vbase + krow + 8 * (pc ^ vswz<D>(row))),
+            (lds_void*)(buf + T::K_ELEMS + blk * 512), 16, 0, 0);
+        if (ROPE) {
+            const f32x4* tb = reinterpret_cast<const f32x4*>(
+                table + krow + 8 * (pc ^ kswz<D>(row)));
+            cs[j][0] = tb[0];
+            cs[j][1] = tb[1];
         }
     }
 
-    // The cos/sin rows of a key tile are read here, when the tile is stored,
-    // rather than staged with K/V: they come from L2 (the table is small and
-    // shared by every head) and keeping them out of the staging registers
-    // keeps the D = 128 kernels within 256 VGPRs (two waves per SIMD).
-    __device__ __forceinline__ void store(uint16_t* Ks, const float* __restrict__ table, int t,
-                                          int N, int tid) {
-        uint16_t* Vs = Ks + T::K_ELEMS;
-        const int k0 = t * BN;
+    __device__ __forceinline__ void issue(uint16_t* buf, const uint16_t* kbase,
+                                          const uint16_t* vbase, const float* __restrict__ table,
+                                          int t, int N, int wave, int lane) {
 #pragma unroll
-        for (int it = 0; it < T::LOADS; ++it) {
-            const int idx = tid + it * 256;
-            const int r = idx / T::CHUNKS;
-            const int cc = idx % T::CHUNKS;
-            u32x4 kw = kreg[it];
-            if (ROPE && k0 + r < N) {
-                const f32x4* tb =
-                    reinterpret_cast<const f32x4*>(table + (int64_t)(k0 + r) * D + cc * 8);
-                kw = rope_rotate8<DT>(kw, tb[0], tb[1]);
-            }
-            *reinterpret_cast<u32x4*>(Ks + r * T::KS + cc * 8) = kw;
-            *reinterpret_cast<u32x4*>(Vs + r * T::VS + cc * 8) = vreg[it];
+        for (int j = 0; j < T::INSTR; ++j) issue_part(j, buf, kbase, vbase, table, t, N, wave, lane);
+    }
+
+    // ROPE only: rotate the K chunks this thread loaded. Call after its loads
+    // have completed (s_waitcnt) and before the block's barrier.
+    __device__ __forceinline__ void rotate(uint16_t* buf, int wave, int lane) {
+        if (!ROPE) return;
+#pragma unroll
+        for (int j = 0; j < T::INSTR; ++j) {
+            u32x4* p = reinterpret_cast<u32x4*>(buf + (wave * T::INSTR + j) * 512 + lane * 8);
+            *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
         }
     }
 };
+
+// The next tile's loads, handed to the score MFMA loop so that their issue
+// (which stalls while the memory pipeline drains earlier requests) overlaps
+// matrix work instead of stalling the wave between tiles. Plain values only:
+// the staging registers are passed separately by reference, so they stay in
+// registers after inlining.
+struct NextLoads {
+    bool active;  // false: nothing to load
+    uint16_t* buf;
+    const uint16_t* kbase;
+    const uint16_t* vbase;
+    const float* table;
+    int t, N, wave, lane;
+};
+
+// Waits for this wave's outstanding memory operations, including its loads
+// into LDS.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Per-wave flash-attention state for 32 query rows and its per-tile step.
 template <int DT, int D, bool ROPE>
@@ -148,6 +193,7 @@ struct WaveAttn {
     f32x16 acc[DBLK];
     float m_run;  // running max of the base-2 scaled scores (lazy)
     float l_run;  // this lane half's share of the denominator
+    u32x4 pw[2][2];  // the last tile's probabilities, packed as PV B operands
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -179,24 +225,37 @@ struct WaveAttn {
 
     // One key tile (k0 .. k0+63) from LDS. MASK: the tile straddles the
     // diagonal of the wave's rows, so keys above a row's position are masked.
+    // Scores of one key tile (keys k0 .. k0+63, K tile at Ks) and the online
+    // softmax update: rescales acc when the running maximum moves, adds the
+    // tile's probabilities to l, and leaves them packed in pw for pv().
     template <bool MASK>
-    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int my_q, int n, int hh,
-                                         int v_lane_off, float scale_log2) {
-        const uint16_t* Vs = Ks + T::K_ELEMS;
-        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores)
+    __device__ __forceinline__ void qk_softmax(const uint16_t* Ks, int k0, int my_q, int n,
+                                               int hh, float scale_log2,
+                                               TileStage<DT, D, ROPE>& stage,
+                                               const NextLoads& next) {
+        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores). Each
+        // block's MFMAs run back to back on one accumulator: a dependent chain
+        // issues at full rate through accumulator forwarding, while two
+        // alternating chains measured ~20% slower on gfx950.
         f32x16 s[2];
+        __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves share a SIMD
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
 #pragma unroll
-        for (int c = 0; c < QCH; ++c)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int c = 0; c < QCH; ++c) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(
-                    Ks + (32 * kb + n) * T::KS + 16 * c + 8 * hh);
+                    Ks + (32 * kb + n) * D + 8 * ((2 * c + hh) ^ kswz<D>(n)));
                 s[kb] = F::mfma(as_vec8<DT>(a), qf[c], s[kb]);
+                // one block of the next tile's loads after every second MFMA
+                // of the second key block (INSTR == QCH / 2)
+                if (kb == 1 && (c & 1) && next.active)
+                    stage.issue_part(c >> 1, next.buf, next.kbase, next.vbase, next.table, next.t,
+                                     next.N, next.wave, next.lane);
             }
+        }
+        __builtin_amdgcn_s_setprio(0);
 
         // online softmax (base 2); lane holds query my_q and 32 of the keys.
         // The row maximum is taken on raw scores (the scale is positive) and
@@ -210,12 +269,22 @@ struct WaveAttn {
                     if (key > my_q) s[kb][j] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        // row maximum: a shallow tree over the lane's 32 scores, then the other
+        // lane half's value (v_permlane32_swap leaves {x[l], x[l^32]} in its
+        // two results)
+        float m8[8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        for (int g = 0; g < 8; ++g) {
+            const int kb = g >> 2, j = 4 * (g & 3);
+            m8[g] = fmaxf(fmaxf(s[kb][j], s[kb][j + 1]), fmaxf(s[kb][j + 2], s[kb][j + 3]));
+        }
+        float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                             false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        }
         const float m_new = mx > m_run + LAZY_RESCALE_LOG2 ? mx : m_run;
         if (__any(m_new != m_run)) {  // wave-uniform branch
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -227,8 +296,7 @@ struct WaveAttn {
                 for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
         }
         const float neg_m = -m_run;
-        float psum = 0.f;
-        u32x4 pw[2][2];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short add chains)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,26 +307,48 @@ struct WaveAttn {
                         __builtin_fmaf(s[kb][8 * e + 2 * t2], scale_log2, neg_m));
                     const float p1 = __builtin_amdgcn_exp2f(
                         __builtin_fmaf(s[kb][8 * e + 2 * t2 + 1], scale_log2, neg_m));
-                    psum += p0 + p1;
+                    ps[t2] += p0 + p1;
                     pw[kb][e][t2] = F::pack2(p0, p1);
                 }
-        l_run += psum;
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
 
-        // O^T += V^T P^T
+    // O^T += V^T P^T for the tile whose probabilities qk_softmax left in pw
+    // (V tile at Vs).
+    __device__ __forceinline__ void pv(const uint16_t* Vs, int lane) {
+        // transpose-read lane geometry (see lds_read_tr16): each 16-lane group
+        // reads 4 rows x 4 elements; rows repeat every 8, so the swizzle is fixed
+        const int grp = lane >> 4, j16 = lane & 15;
+        const int v_lane_row = 4 * (grp >> 1) + (j16 >> 2);
+        const int v_lane_c = 2 * (grp & 1) + ((j16 & 3) >> 1);
+        const int v_lane_e = 4 * (j16 & 1);
+        const int v_lane_sw = vswz<D>(v_lane_row);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const vec8 pb = as_vec8<DT>(pw[kb][e]);
-                const uint16_t* vp = Vs + v_lane_off + (32 * kb + 16 * e) * T::VS;
+                const uint16_t* vp = Vs + (32 * kb + 16 * e) * D;
 #pragma unroll
                 for (int i = 0; i < DBLK; ++i) {
-                    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 32 * i));
-                    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * T::VS + 32 * i));
+                    const int off = v_lane_row * D + 8 * ((4 * i + v_lane_c) ^ v_lane_sw) + v_lane_e;
+                    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + off));
+                    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * D + off));
                     const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
                     acc[i] = F::mfma(as_vec8<DT>(a), pb, acc[i]);
                 }
             }
+        __builtin_amdgcn_s_setprio(0);
+    }
+
+    // Both halves of a key-tile step: tile at Ks (K) and Ks + K_ELEMS (V).
+    template <bool MASK>
+    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int my_q, int n, int hh,
+                                         int lane, float scale_log2,
+                                         TileStage<DT, D, ROPE>& stage, const NextLoads& next) {
+        qk_softmax<MASK>(Ks, k0, my_q, n, hh, scale_log2, stage, next);
+        pv(Ks + T::K_ELEMS, lane);
     }
 
     // O = acc / l and LSE = ln2 * (m + log2 l) for the wave's row.
@@ -316,9 +406,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int lane = tid & 63;
     const int n = lane & 31;
     const int hh = lane >> 5;
-    const int grp = lane >> 4, j16 = lane & 15;
-    const int v_lane_off = ((grp >> 1) * 4 + (j16 >> 2)) * T::VS + 16 * (grp & 1) + 4 * (j16 & 3);
-
     const Unit un = decode_unit(Hq, Hkv, n_qtiles);
     const int qtile = n_qtiles - 1 - un.idx;
     const int q0 = qtile * BM;
@@ -337,17 +424,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int wave_tiles = qw0 < N ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
 
     TileStage<DT, D, ROPE> stage;
-    stage.load(kbase, vbase, 0, N, tid);
+    stage.issue(smem, kbase, vbase, table, 0, N, wave, lane);
     for (int t = 0; t < n_tiles; ++t) {
         uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
-        stage.store(Ks, table, t, N, tid);
-        if (t + 1 < n_tiles) stage.load(kbase, vbase, t + 1, N, tid);
-        __syncthreads();  // tile t visible; the other buffer is no longer read
+        wait_all_loads();              // this wave's part of tile t has landed
+        stage.rotate(Ks, wave, lane);  // RoPE on the K chunks this thread loaded
+        __syncthreads();               // tile t complete; the other buffer is no longer read
+        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS, kbase, vbase,
+                             table, t + 1, N, wave, lane};
         if (t < wave_tiles) {
             if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, t * BN, my_q, n, hh, v_lane_off, scale_log2);
+                st.template step<true>(Ks, t * BN, my_q, n, hh, lane, scale_log2, stage, next);
             else
-                st.template step<false>(Ks, t * BN, my_q, n, hh, v_lane_off, scale_log2);
+                st.template step<false>(Ks, t * BN, my_q, n, hh, lane, scale_log2, stage, next);
+        } else if (next.active) {
+            stage.issue(next.buf, kbase, vbase, table, next.t, N, wave, lane);
         }
     }
     if (wave_tiles == 0 || my_q >= N) return;
@@ -376,9 +467,6 @@ __global__ __launch_bounds__(512, 1) void attn_pair_kernel(
     const int lane = tid & 63;
     const int n = lane & 31;
     const int hh = lane >> 5;
-    const int grp = lane >> 4, j16 = lane & 15;
-    const int v_lane_off = ((grp >> 1) * 4 + (j16 >> 2)) * T::VS + 16 * (grp & 1) + 4 * (j16 & 3);
-
     const Unit un = decode_unit(Hq, Hkv, n_pairs);
     const int p = un.idx;
     const int t_heavy = n_qtiles - 1 - p;
@@ -419,16 +507,14 @@ __global__ __launch_bounds__(512, 1) void attn_pair_kernel(
     {
         int qt;
         const int kt = job_tile(0, qt);
-        if (kt >= 0) stage.load(kbase, vbase, kt, N, htid);
+        if (kt >= 0) stage.issue(hbuf, kbase, vbase, table, kt, N, wave, lane);
     }
     for (int i = 0; i < steps; ++i) {
         int qt;
         const int kt = job_tile(i, qt);
         uint16_t* Ks = hbuf + (i & 1) * T::BUF_ELEMS;
-        if (kt >= 0) stage.store(Ks, table, kt, N, htid);
-        int qt1;
-        const int kt1 = job_tile(i + 1, qt1);
-        if (i + 1 < steps && kt1 >= 0) stage.load(kbase, vbase, kt1, N, htid);
+        wait_all_loads();  // this wave's part of the half's tile i has landed
+        if (kt >= 0) stage.rotate(Ks, wave, lane);
         if (kt >= 0 && qt != cur_qt) {
             // half B moving from the light rows to the heavy rows: finish the light rows
             if (cur_qt >= 0 && wave_tiles > 0 && my_q < N) {
@@ -442,12 +528,18 @@ __global__ __launch_bounds__(512, 1) void attn_pair_kernel(
             st.load_q(qhead, table, my_q, N, hh);
             st.reset();
         }
-        __syncthreads();  // tile i visible to this half; the other buffer is no longer read
+        __syncthreads();  // tile i complete in both halves; their other buffers are free
+        int qt1;
+        const int kt1 = job_tile(i + 1, qt1);
+        const NextLoads next{i + 1 < steps && kt1 >= 0, hbuf + ((i + 1) & 1) * T::BUF_ELEMS,
+                             kbase, vbase, table, kt1, N, wave, lane};
         if (kt >= 0 && kt < wave_tiles) {
             if (kt * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, kt * BN, my_q, n, hh, v_lane_off, scale_log2);
+                st.template step<true>(Ks, kt * BN, my_q, n, hh, lane, scale_log2, stage, next);
             else
-                st.template step<false>(Ks, kt * BN, my_q, n, hh, v_lane_off, scale_log2);
+                st.template step<false>(Ks, kt * BN, my_q, n, hh, lane, scale_log2, stage, next);
+        } else if (next.active) {
+            stage.issue(next.buf, kbase, vbase, table, next.t, N, wave, lane);
         }
     }
 
@@ -499,7 +591,10 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     const int64_t pair_units = (int64_t)n_pairs * a.Hq * a.B;
     const int64_t tile_units = (int64_t)n_qtiles * a.Hq * a.B;
     if (tile_units > 0x7fffffff) return hipErrorInvalidConfiguration;
-    bool pair = pair_units >= NUM_CUS && n_qtiles >= 2;
+    // The pair launch fixes the causal imbalance when the grid has only a few
+    // workgroups per CU; with more, the heaviest-first tile launch balances as
+    // well and keeps more workgroups resident per CU.
+    bool pair = tile_units < 4 * NUM_CUS && pair_units >= NUM_CUS / 2 && n_qtiles >= 2;
     if (a.shape == ATTN_SHAPE_PAIR) pair = true;
     if (a.shape == ATTN_SHAPE_TILE) pair = false;
     if (pair) {

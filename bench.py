@@ -34,9 +34,68 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}  # MI355X dense, published
+CSRC = os.path.join(ROOT, "rotary_position_embedding_causal_amd", "csrc")
+ATTN_SOURCES = ("attn_fwd.hip", "rac_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fused_traffic_llama3_8b_gqa_n2048.json")
+FUSED_KERNEL_MATCH = "attn_"  # attention kernels; the fused ones end in "true>"
 HBM_PEAK_GBS = 8000.0
 MAIN = "llama3_8b_gqa_n2048"
 METRIC = "causal RoPE-attn fwd TFLOP/s (fused & pre-rotate) + % of MFMA peak; N*"
+
+
+def attn_source_hash():
+    """sha256 over the attention kernel sources (counters are tied to it)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per fused-kernel launch from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != attn_source_hash():
+        return None
+    return t["read_bytes"] + t["write_bytes"]
+
+
+def ingest_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir):
+    """Turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs of a `--only fused`
+    run and of a `--copy-calib` run into the traffic summary under profiles/."""
+    import csv
+    import glob
+
+    def per_dispatch(d, pick):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(f[0])) if pick(r["Kernel_Name"])]
+        return sum(vals) / len(vals), len(vals)
+
+    fused = lambda k: "attn_" in k and k.split("(")[0].rstrip().endswith("true>")  # noqa: E731
+    copy = lambda k: "copyBuffer" in k or "elementwise" in k  # noqa: E731
+    fetch, nf = per_dispatch(fetch_dir, fused)
+    write, nw = per_dispatch(write_dir, fused)
+    cfetch, _ = per_dispatch(calib_fetch_dir, lambda k: "copyBuffer" in k)
+    cwrite, _ = per_dispatch(calib_write_dir, lambda k: "copyBuffer" in k)
+    copy_bytes = 256 << 20
+    rscale = copy_bytes / (cfetch * 1024.0)
+    wscale = copy_bytes / (cwrite * 1024.0)
+    out = {"kernel": "attn fused (RoPE) forward", "workload": MAIN,
+           "source_sha256": attn_source_hash(),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [nf, nw],
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib": cfetch, "write_kib": cwrite,
+                           "read_scale": rscale, "write_scale": wscale},
+           "read_bytes": fetch * 1024.0 * rscale, "write_bytes": write * 1024.0 * wscale}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def attn_flops(w):
@@ -58,9 +117,15 @@ def main():
                     help="time one kernel/path alone (for profiler runs)")
     ap.add_argument("--workload", default=MAIN,
                     help="workload of the --only runs (a name from inputs.WORKLOADS)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar="DIR",
+                    help="FETCH_SIZE and WRITE_SIZE counter dirs of a --only fused run, then of "
+                         "a --copy-calib run: write the traffic summary under profiles/ and exit")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a plain 256 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -188,7 +253,7 @@ def main():
                    "flops_per_path": fl},
         "roofline": {"kernel": "attn_fwd_kernel<bf16,128,rope>", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None},
+                     "frac": achieved / peak, "traffic": measured_traffic()},
         "paths": paths,
     }
 

@@ -25,7 +25,7 @@
 //     (ds_read_b64_tr_b16), gathering keys in that same permuted order.
 //   * Key tiles of BN = 64 rows, double-buffered in LDS with one barrier per
 //     tile. The next tile's K and V go straight from global memory into LDS
-//     (global_load_lds_dwordx4) while the current tile is computed; with RoPE
+//     (buffer_load_dwordx4 ... lds) while the current tile is computed; with RoPE
 //     each thread also prefetches the cos/sin rows of the K chunks it loads
 //     and rotates them in place before the barrier. Tiles past a wave's last
 //     query are skipped and only tiles straddling the diagonal are masked.
@@ -79,7 +79,6 @@ struct Tile {
     static constexpr int K_ELEMS = BN * D;
     static constexpr int V_ELEMS = BN * D;
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int INSTR = BN * CH / 256;          // 1 KiB DMA blocks per wave and tensor
 };
 
 // Chunk swizzles. K: the score MFMA reads one chunk column from 16 consecutive
@@ -101,53 +100,71 @@ __device__ __forceinline__ int kv_tiles_of(int qt, int N) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
-// Loads of one K/V tile by a 4-wave block, straight from global memory into
-// LDS (global_load_lds_dwordx4: lane i of an instruction fills bytes
+// Buffer descriptors of one key tile: K, V and (RoPE) cos/sin rows starting
+// at the tile's first key. The descriptor's record count ends at the sequence
+// end, so rows past it read as zeros (their scores are masked by causality and
+// their probabilities are zero) without any per-lane clamping.
+constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw (unformatted) 32-bit data
+struct TileRsrc {
+    __amdgpu_buffer_rsrc_t k, v, t;
+};
+template <int D>
+__device__ __forceinline__ TileRsrc tile_rsrc(const uint16_t* kbase, const uint16_t* vbase,
+                                              const float* table, int t, int N) {
+    const int k0 = t * BN;
+    const int64_t rows = N - k0;
+    const int kv_bytes = (int)min(rows * D * 2, (int64_t)0x7fffffff);
+    const int tab_bytes = (int)min(rows * D * 4, (int64_t)0x7fffffff);
+    TileRsrc r;
+    r.k = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * D), 0, kv_bytes,
+                                            BUF_RSRC_FLAGS);
+    r.v = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * D), 0, kv_bytes,
+                                            BUF_RSRC_FLAGS);
+    r.t = __builtin_amdgcn_make_buffer_rsrc((void*)(table ? table + (int64_t)k0 * D : nullptr), 0,
+                                            table ? tab_bytes : 0, BUF_RSRC_FLAGS);
+    return r;
+}
+
+// Loads of one K/V tile by a block of NW waves, straight from global memory
+// into LDS (buffer_load ... lds: lane i of an instruction fills bytes
 // 16i..16i+15 of a 1 KiB block). Block b of a tile holds chunks 64b..64b+63;
-// a lane fetches the global chunk that the swizzle places there. Rows past
-// the sequence end repeat its last row: their scores are masked by causality
-// and their probabilities are zero.
+// a lane fetches the global chunk that the swizzle places there.
 // With ROPE the K chunks land unrotated; each thread prefetches the cos/sin
 // entries of the chunks it loaded and, once its loads have landed, rotates
 // those chunks in place before the block's barrier.
-template <int DT, int D, bool ROPE>
+template <int DT, int D, bool ROPE, int NW>
 struct TileStage {
     typedef Tile<D> T;
-    f32x4 cs[ROPE ? T::INSTR : 1][2];
+    static constexpr int INSTR = BN * T::CH / (64 * NW);  // 1 KiB blocks per wave and tensor
+    f32x4 cs[ROPE ? INSTR : 1][2];
 
     // Loads block j (0 <= j < INSTR) of this wave's share: one 1 KiB block of
-    // K, one of V, and (ROPE) the cos/sin entries of the K block.
-    __device__ __forceinline__ void issue_part(int j, uint16_t* buf, const uint16_t* kbase,
-                                               const uint16_t* vbase,
-                                               const float* __restrict__ table, int t, int N,
+    // K, one of V, and (ROPE) the cos/sin entries of the K block. `wave` must
+    // be wave-uniform.
+    __device__ __forceinline__ void issue_part(int j, uint16_t* buf, const TileRsrc& rs,
                                                int wave, int lane) {
-        const int blk = wave * T::INSTR + j;
+        const int blk = wave * INSTR + j;
         const int g = blk * 64 + lane;          // chunk index inside the tile
         const int row = g / T::CH;
         const int pc = g % T::CH;               // physical chunk position
-        const int key = min(t * BN + row, N - 1);
-        const int64_t krow = (int64_t)key * D;
-        __builtin_amdgcn_global_load_lds(
-            (glb_void*)(kbase + krow + 8 * (pc ^ kswz<D>(row))),
-            (lds_void*)(buf + blk * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (glb_void*)(vbase + krow + 8 * (pc ^ vswz<D>(row))),
-            (lds_void*)(buf + T::K_ELEMS + blk * 512), 16, 0, 0);
+        const int kel = row * D + 8 * (pc ^ kswz<D>(row));  // element offsets in the tile
+        const int vel = row * D + 8 * (pc ^ vswz<D>(row));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void*)(buf + blk * 512), 16, kel * 2,
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(buf + T::K_ELEMS + blk * 512),
+                                                 16, vel * 2, 0, 0, 0);
         if (ROPE) {
-            const f32x4* tb = reinterpret_cast<const f32x4*>(
-                table + krow + 8 * (pc ^ kswz<D>(row)));
-            cs[j][0] = tb[0];
-            cs[j][1] = tb[1];
+            cs[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs.t, kel * 4, 0, 0));
+            cs[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs.t, kel * 4 + 16, 0, 0));
         }
     }
 
-    __device__ __forceinline__ void issue(uint16_t* buf, const uint16_t* kbase,
-                                          const uint16_t* vbase, const float* __restrict__ table,
-                                          int t, int N, int wave, int lane) {
+    __device__ __forceinline__ void issue(uint16_t* buf, const TileRsrc& rs, int wave, int lane) {
 #pragma unroll
-        for (int j = 0; j < T::INSTR; ++j) issue_part(j, buf, kbase, vbase, table, t, N, wave, lane);
+        for (int j = 0; j < INSTR; ++j) issue_part(j, buf, rs, wave, lane);
     }
 
     // ROPE only: rotate the K chunks this thread loaded. Call after its loads
@@ -155,8 +172,8 @@ struct TileStage {
     __device__ __forceinline__ void rotate(uint16_t* buf, int wave, int lane) {
         if (!ROPE) return;
 #pragma unroll
-        for (int j = 0; j < T::INSTR; ++j) {
-            u32x4* p = reinterpret_cast<u32x4*>(buf + (wave * T::INSTR + j) * 512 + lane * 8);
+        for (int j = 0; j < INSTR; ++j) {
+            u32x4* p = reinterpret_cast<u32x4*>(buf + (wave * INSTR + j) * 512 + lane * 8);
             *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
         }
     }
@@ -164,109 +181,122 @@ struct TileStage {
 
 // The next tile's loads, handed to the score MFMA loop so that their issue
 // (which stalls while the memory pipeline drains earlier requests) overlaps
-// matrix work instead of stalling the wave between tiles. Plain values only:
-// the staging registers are passed separately by reference, so they stay in
-// registers after inlining.
+// matrix work instead of stalling the wave between tiles.
 struct NextLoads {
     bool active;  // false: nothing to load
     uint16_t* buf;
-    const uint16_t* kbase;
-    const uint16_t* vbase;
-    const float* table;
-    int t, N, wave, lane;
+    TileRsrc rs;
+    int wave, lane;
 };
 
 // Waits for this wave's outstanding memory operations, including its loads
 // into LDS.
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Per-wave flash-attention state for 32 query rows and its per-tile step.
-template <int DT, int D, bool ROPE>
+// Per-wave flash-attention state for QB blocks of 32 query rows (rows
+// q_first + 32b + n, b < QB) and its per-tile work. Every block's scores use
+// the same K operands and its PV the same V operands; with QB = 2 the second
+// block's score MFMAs overlap the first block's softmax, and the first block's
+// PV MFMAs overlap the second block's softmax, inside one wave.
+template <int DT, int D, bool ROPE, int QB>
 struct WaveAttn {
     typedef Fmt<DT> F;
     typedef typename F::vec8 vec8;
     typedef Tile<D> T;
+    typedef TileStage<DT, D, ROPE, 4 / QB> Stage;  // a row block is 4 / QB waves
     static constexpr int QCH = D / 16;   // 16-deep MFMA steps over the head dim
     static constexpr int DBLK = D / 32;  // 32-row blocks of O^T
 
-    vec8 qf[QCH];
-    f32x16 acc[DBLK];
-    float m_run;  // running max of the base-2 scaled scores (lazy)
-    float l_run;  // this lane half's share of the denominator
-    u32x4 pw[2][2];  // the last tile's probabilities, packed as PV B operands
+    vec8 qf[QB][QCH];
+    f32x16 acc[QB][DBLK];
+    f32x16 s[QB][2];    // the current tile's raw scores
+    float m_run[QB];    // running max of the base-2 scaled scores (lazy)
+    float l_run[QB];    // this lane half's share of the denominator
+    float alpha[QB];    // rescale factor of acc still to apply (1 = none)
+    u32x4 pw[QB][2][2];  // the tile's probabilities, packed as PV B operands
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
-        for (int i = 0; i < DBLK; ++i)
+        for (int b = 0; b < QB; ++b) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
-        m_run = -INFINITY;
-        l_run = 0.f;
-    }
-
-    // The wave's Q rows as MFMA B operands (rotated once if ROPE).
-    __device__ __forceinline__ void load_q(const uint16_t* qrow0, const float* __restrict__ table,
-                                           int my_q, int N, int hh) {
+            for (int i = 0; i < DBLK; ++i)
 #pragma unroll
-        for (int c = 0; c < QCH; ++c) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (my_q < N) {
-                const int d0 = 16 * c + 8 * hh;
-                w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)my_q * D + d0);
-                if (ROPE) {
-                    const f32x4* t =
-                        reinterpret_cast<const f32x4*>(table + (int64_t)my_q * D + d0);
-                    w = rope_rotate8<DT>(w, t[0], t[1]);
-                }
-            }
-            qf[c] = as_vec8<DT>(w);
+                for (int j = 0; j < 16; ++j) acc[b][i][j] = 0.f;
+            m_run[b] = -INFINITY;
+            l_run[b] = 0.f;
+            alpha[b] = 1.f;
         }
     }
 
-    // One key tile (k0 .. k0+63) from LDS. MASK: the tile straddles the
-    // diagonal of the wave's rows, so keys above a row's position are masked.
-    // Scores of one key tile (keys k0 .. k0+63, K tile at Ks) and the online
-    // softmax update: rescales acc when the running maximum moves, adds the
-    // tile's probabilities to l, and leaves them packed in pw for pv().
-    template <bool MASK>
-    __device__ __forceinline__ void qk_softmax(const uint16_t* Ks, int k0, int my_q, int n,
-                                               int hh, float scale_log2,
-                                               TileStage<DT, D, ROPE>& stage,
-                                               const NextLoads& next) {
-        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores). Each
-        // block's MFMAs run back to back on one accumulator: a dependent chain
-        // issues at full rate through accumulator forwarding, while two
-        // alternating chains measured ~20% slower on gfx950.
-        f32x16 s[2];
-        __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves share a SIMD
+    // Q rows q_first + 32b + n as MFMA B operands (rotated once if ROPE).
+    __device__ __forceinline__ void load_q(const uint16_t* qrow0, const float* __restrict__ table,
+                                           int q_first, int N, int n, int hh) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const int row = q_first + 32 * b + n;
+#pragma unroll
+            for (int c = 0; c < QCH; ++c) {
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (row < N) {
+                    const int d0 = 16 * c + 8 * hh;
+                    w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)row * D + d0);
+                    if (ROPE) {
+                        const f32x4* t =
+                            reinterpret_cast<const f32x4*>(table + (int64_t)row * D + d0);
+                        w = rope_rotate8<DT>(w, t[0], t[1]);
+                    }
+                }
+                qf[b][c] = as_vec8<DT>(w);
+            }
+        }
+    }
+
+    // S^T = K Q^T for block b and both 32-key halves of the tile (raw scores).
+    // Each half's MFMAs run back to back on one accumulator (a dependent
+    // chain issues at full rate through accumulator forwarding). With LOADS,
+    // one block of the next tile's loads follows every second MFMA of the
+    // second half, so their issue overlaps matrix work.
+    template <bool LOADS>
+    __device__ __forceinline__ void score(int b, const uint16_t* Ks, int n, int hh,
+                                          Stage& stage, const NextLoads& next) {
+        __builtin_amdgcn_s_setprio(1);  // matrix phase first when waves share a SIMD
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+            for (int j = 0; j < 16; ++j) s[b][kb][j] = 0.f;
 #pragma unroll
             for (int c = 0; c < QCH; ++c) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(
                     Ks + (32 * kb + n) * D + 8 * ((2 * c + hh) ^ kswz<D>(n)));
-                s[kb] = F::mfma(as_vec8<DT>(a), qf[c], s[kb]);
-                // one block of the next tile's loads after every second MFMA
-                // of the second key block (INSTR == QCH / 2)
-                if (kb == 1 && (c & 1) && next.active)
-                    stage.issue_part(c >> 1, next.buf, next.kbase, next.vbase, next.table, next.t,
-                                     next.N, next.wave, next.lane);
+                s[b][kb] = F::mfma(as_vec8<DT>(a), qf[b][c], s[b][kb]);
+                if (LOADS && kb == 1 && next.active) {
+                    // Stage::INSTR / QCH blocks per MFMA step
+                    constexpr int PER = (Stage::INSTR + QCH - 1) / QCH;
+#pragma unroll
+                    for (int j = 0; j < PER; ++j)
+                        if (c * PER + j < Stage::INSTR)
+                            stage.issue_part(c * PER + j, next.buf, next.rs, next.wave, next.lane);
+                }
             }
         }
         __builtin_amdgcn_s_setprio(0);
+    }
 
-        // online softmax (base 2); lane holds query my_q and 32 of the keys.
-        // The row maximum is taken on raw scores (the scale is positive) and
-        // the scale is folded into the exponent's fused multiply-add.
+    // Online softmax (base 2) of block b's scores, branch free: masks keys
+    // above the row (MASK), raises the running maximum lazily (only when a
+    // tile exceeds it by more than 2^8), records the acc rescale factor for
+    // rescale(), adds the probabilities to l and packs them for pv(). The row
+    // maximum is taken on raw scores (the scale is positive); the scale is
+    // folded into the exponent's fused multiply-add.
+    template <bool MASK>
+    __device__ __forceinline__ void softmax(int b, int k0, int row, int hh, float scale_log2) {
         if (MASK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    if (key > my_q) s[kb][j] = -INFINITY;
+                    if (key > row) s[b][kb][j] = -INFINITY;
                 }
         }
         // row maximum: a shallow tree over the lane's 32 scores, then the other
@@ -276,7 +306,7 @@ struct WaveAttn {
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             const int kb = g >> 2, j = 4 * (g & 3);
-            m8[g] = fmaxf(fmaxf(s[kb][j], s[kb][j + 1]), fmaxf(s[kb][j + 2], s[kb][j + 3]));
+            m8[g] = fmaxf(fmaxf(s[b][kb][j], s[b][kb][j + 1]), fmaxf(s[b][kb][j + 2], s[b][kb][j + 3]));
         }
         float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
                          fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
@@ -285,17 +315,12 @@ struct WaveAttn {
                                                              false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
         }
-        const float m_new = mx > m_run + LAZY_RESCALE_LOG2 ? mx : m_run;
-        if (__any(m_new != m_run)) {  // wave-uniform branch
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) acc[i][j] *= alpha;
-        }
-        const float neg_m = -m_run;
+        const float m_old = m_run[b];
+        const float m_new = mx > m_old + LAZY_RESCALE_LOG2 ? mx : m_old;
+        const float al = __builtin_amdgcn_exp2f(m_old - m_new);  // 1 when unchanged
+        alpha[b] = al;
+        m_run[b] = m_new;
+        const float neg_m = -m_new;
         float ps[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short add chains)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -304,18 +329,28 @@ struct WaveAttn {
 #pragma unroll
                 for (int t2 = 0; t2 < 4; ++t2) {
                     const float p0 = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[kb][8 * e + 2 * t2], scale_log2, neg_m));
+                        __builtin_fmaf(s[b][kb][8 * e + 2 * t2], scale_log2, neg_m));
                     const float p1 = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[kb][8 * e + 2 * t2 + 1], scale_log2, neg_m));
+                        __builtin_fmaf(s[b][kb][8 * e + 2 * t2 + 1], scale_log2, neg_m));
                     ps[t2] += p0 + p1;
-                    pw[kb][e][t2] = F::pack2(p0, p1);
+                    pw[b][kb][e][t2] = F::pack2(p0, p1);
                 }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        l_run[b] = l_run[b] * al + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     }
 
-    // O^T += V^T P^T for the tile whose probabilities qk_softmax left in pw
-    // (V tile at Vs).
-    __device__ __forceinline__ void pv(const uint16_t* Vs, int lane) {
+    // Applies block b's pending acc rescale; skipped (wave-uniform branch)
+    // when no row of the wave moved its maximum, which is most tiles.
+    __device__ __forceinline__ void rescale(int b) {
+        if (__any(alpha[b] != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[b][i][j] *= alpha[b];
+        }
+    }
+
+    // O^T += V^T P^T for block b (V tile at Vs).
+    __device__ __forceinline__ void pv(int b, const uint16_t* Vs, int lane) {
         // transpose-read lane geometry (see lds_read_tr16): each 16-lane group
         // reads 4 rows x 4 elements; rows repeat every 8, so the swizzle is fixed
         const int grp = lane >> 4, j16 = lane & 15;
@@ -328,7 +363,7 @@ struct WaveAttn {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const vec8 pb = as_vec8<DT>(pw[kb][e]);
+                const vec8 pb = as_vec8<DT>(pw[b][kb][e]);
                 const uint16_t* vp = Vs + (32 * kb + 16 * e) * D;
 #pragma unroll
                 for (int i = 0; i < DBLK; ++i) {
@@ -336,24 +371,40 @@ struct WaveAttn {
                     const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + off));
                     const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * D + off));
                     const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                    acc[i] = F::mfma(as_vec8<DT>(a), pb, acc[i]);
+                    acc[b][i] = F::mfma(as_vec8<DT>(a), pb, acc[b][i]);
                 }
             }
         __builtin_amdgcn_s_setprio(0);
     }
 
-    // Both halves of a key-tile step: tile at Ks (K) and Ks + K_ELEMS (V).
+    // One key tile for all blocks: keys k0 .. k0+63, K at Ks, V at Ks + K_ELEMS;
+    // q_first = the wave's first row. MASK: the tile reaches past q_first.
     template <bool MASK>
-    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int my_q, int n, int hh,
-                                         int lane, float scale_log2,
-                                         TileStage<DT, D, ROPE>& stage, const NextLoads& next) {
-        qk_softmax<MASK>(Ks, k0, my_q, n, hh, scale_log2, stage, next);
-        pv(Ks + T::K_ELEMS, lane);
+    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int q_first, int n, int hh,
+                                         int lane, float scale_log2, Stage& stage,
+                                         const NextLoads& next) {
+        const uint16_t* Vs = Ks + T::K_ELEMS;
+        if (QB == 1) {
+            score<true>(0, Ks, n, hh, stage, next);
+            softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
+            rescale(0);
+            pv(0, Vs, lane);
+        } else {
+            score<false>(0, Ks, n, hh, stage, next);
+            score<true>(1, Ks, n, hh, stage, next);
+            softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
+            rescale(0);
+            pv(0, Vs, lane);
+            softmax<MASK>(1, k0, q_first + 32 + n, hh, scale_log2);
+            rescale(1);
+            pv(1, Vs, lane);
+        }
     }
 
-    // O = acc / l and LSE = ln2 * (m + log2 l) for the wave's row.
-    // l_tot is the full denominator (both lane halves).
-    __device__ __forceinline__ void write(uint16_t* orow, float* lse_row, float l_tot, int hh) {
+    // O = acc / l and LSE = ln2 * (m + log2 l) for block b's row of this
+    // lane; l_tot is the full denominator (both lane halves).
+    __device__ __forceinline__ void write(int b, uint16_t* orow, float* lse_row, float l_tot,
+                                          int hh) {
         const float inv = 1.f / l_tot;
 #pragma unroll
         for (int i = 0; i < DBLK; ++i)
@@ -361,11 +412,11 @@ struct WaveAttn {
             for (int gq = 0; gq < 4; ++gq) {
                 const int d0 = 32 * i + 8 * gq + 4 * hh;
                 u32x2 w;
-                w[0] = F::pack2(acc[i][4 * gq] * inv, acc[i][4 * gq + 1] * inv);
-                w[1] = F::pack2(acc[i][4 * gq + 2] * inv, acc[i][4 * gq + 3] * inv);
+                w[0] = F::pack2(acc[b][i][4 * gq] * inv, acc[b][i][4 * gq + 1] * inv);
+                w[1] = F::pack2(acc[b][i][4 * gq + 2] * inv, acc[b][i][4 * gq + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + d0) = w;
             }
-        if (lse_row != nullptr && hh == 0) *lse_row = (m_run + __log2f(l_tot)) * LN2;
+        if (lse_row != nullptr && hh == 0) *lse_row = (m_run[b] + __log2f(l_tot)) * LN2;
     }
 };
 
@@ -391,14 +442,15 @@ __device__ __forceinline__ Unit decode_unit(int Hq, int Hkv, int per_head) {
 }
 
 // ---------------------------------------------------------------------------
-// One 4-wave workgroup per query tile (heaviest first).
+// One workgroup (4 / QB waves, BM = 128 rows) per query tile, heaviest first.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool ROPE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+template <int DT, int D, bool ROPE, int QB>
+__global__ __launch_bounds__(256 / QB, QB == 1 ? 2 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, float scale_log2) {
     typedef Tile<D> T;
+    typedef WaveAttn<DT, D, ROPE, QB> W;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
 
     const int tid = threadIdx.x;
@@ -406,63 +458,71 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int lane = tid & 63;
     const int n = lane & 31;
     const int hh = lane >> 5;
+
     const Unit un = decode_unit(Hq, Hkv, n_qtiles);
     const int qtile = n_qtiles - 1 - un.idx;
-    const int q0 = qtile * BM;
-    const int qw0 = q0 + wave * 32;
-    const int my_q = qw0 + n;
+    const int qw0 = qtile * BM + wave * 32 * QB;  // the wave's first row
     const int64_t q_head = ((int64_t)un.b * Hq + un.h) * N;
     const int64_t kv_head = ((int64_t)un.b * Hkv + un.g) * N;
     const uint16_t* kbase = k + kv_head * D;
     const uint16_t* vbase = v + kv_head * D;
 
-    WaveAttn<DT, D, ROPE> st;
-    st.load_q(q + q_head * D, table, my_q, N, hh);
+    W st;
+    st.load_q(q + q_head * D, table, qw0, N, n, hh);
     st.reset();
 
     const int n_tiles = kv_tiles_of(qtile, N);
-    const int wave_tiles = qw0 < N ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
+    const int wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
 
-    TileStage<DT, D, ROPE> stage;
-    stage.issue(smem, kbase, vbase, table, 0, N, wave, lane);
+    typename W::Stage stage;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
+    stage.issue(smem, tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
     for (int t = 0; t < n_tiles; ++t) {
         uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
         wait_all_loads();              // this wave's part of tile t has landed
-        stage.rotate(Ks, wave, lane);  // RoPE on the K chunks this thread loaded
+        stage.rotate(Ks, uwave, lane);  // RoPE on the K chunks this thread loaded
         __syncthreads();               // tile t complete; the other buffer is no longer read
-        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS, kbase, vbase,
-                             table, t + 1, N, wave, lane};
+        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS,
+                             tile_rsrc<D>(kbase, vbase, table, t + 1, N), uwave, lane};
         if (t < wave_tiles) {
             if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, t * BN, my_q, n, hh, lane, scale_log2, stage, next);
+                st.template step<true>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
             else
-                st.template step<false>(Ks, t * BN, my_q, n, hh, lane, scale_log2, stage, next);
+                st.template step<false>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
         } else if (next.active) {
-            stage.issue(next.buf, kbase, vbase, table, next.t, N, wave, lane);
+            stage.issue(next.buf, next.rs, uwave, lane);
         }
     }
-    if (wave_tiles == 0 || my_q >= N) return;
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+    if (wave_tiles == 0) return;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = qw0 + 32 * b + n;
+        const float l_tot = st.l_run[b] + __shfl_xor(st.l_run[b], 32);
+        if (row < N)
+            st.write(b, out + (q_head + row) * D, lse ? lse + q_head + row : nullptr, l_tot, hh);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Paired, split, load-balanced launch: 8 waves per workgroup.
+// Paired, split, load-balanced launch: two halves of 4 / QB waves each.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool ROPE>
-__global__ __launch_bounds__(512, 1) void attn_pair_kernel(
+template <int DT, int D, bool ROPE, int QB>
+__global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, int n_pairs,
     float scale_log2) {
     typedef Tile<D> T;
-    typedef WaveAttn<DT, D, ROPE> W;
+    typedef WaveAttn<DT, D, ROPE, QB> W;
+    constexpr int HT = 256 / QB;  // threads per half
     // per half: two tile buffers; after the loop the same memory holds the merge data
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * T::BUF_ELEMS];
 
     const int tid = threadIdx.x;
-    const int half = tid >> 8;       // 0 = A, 1 = B
-    const int htid = tid & 255;      // thread index inside the half
+    // wave-uniform by construction; readfirstlane lets the compiler see it,
+    // so the tile descriptors stay scalar
+    const int half = __builtin_amdgcn_readfirstlane(tid / HT);  // 0 = A, 1 = B
+    const int htid = tid % HT;       // thread index inside the half
     const int wave = htid >> 6;      // wave inside the half
     const int lane = tid & 63;
     const int n = lane & 31;
@@ -500,54 +560,66 @@ __global__ __launch_bounds__(512, 1) void attn_pair_kernel(
     W st;
     st.reset();
     int cur_qt = -1;   // query tile whose rows this wave holds
-    int qw0 = 0, my_q = 0, wave_tiles = 0;
+    int qw0 = 0, wave_tiles = 0;
 
     uint16_t* hbuf = smem + half * 2 * T::BUF_ELEMS;
-    TileStage<DT, D, ROPE> stage;
+    typename W::Stage stage;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
     {
         int qt;
         const int kt = job_tile(0, qt);
-        if (kt >= 0) stage.issue(hbuf, kbase, vbase, table, kt, N, wave, lane);
+        if (kt >= 0) stage.issue(hbuf, tile_rsrc<D>(kbase, vbase, table, kt, N), uwave, lane);
     }
     for (int i = 0; i < steps; ++i) {
         int qt;
         const int kt = job_tile(i, qt);
         uint16_t* Ks = hbuf + (i & 1) * T::BUF_ELEMS;
         wait_all_loads();  // this wave's part of the half's tile i has landed
-        if (kt >= 0) stage.rotate(Ks, wave, lane);
+        if (kt >= 0) stage.rotate(Ks, uwave, lane);
         if (kt >= 0 && qt != cur_qt) {
             // half B moving from the light rows to the heavy rows: finish the light rows
-            if (cur_qt >= 0 && wave_tiles > 0 && my_q < N) {
-                const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-                st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+            if (cur_qt >= 0 && wave_tiles > 0) {
+#pragma unroll
+                for (int b = 0; b < QB; ++b) {
+                    const int row = qw0 + 32 * b + n;
+                    const float l_tot = st.l_run[b] + __shfl_xor(st.l_run[b], 32);
+                    if (row < N)
+                        st.write(b, out + (q_head + row) * D, lse ? lse + q_head + row : nullptr,
+                                 l_tot, hh);
+                }
             }
             cur_qt = qt;
-            qw0 = qt * BM + wave * 32;
-            my_q = qw0 + n;
-            wave_tiles = qw0 < N ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
-            st.load_q(qhead, table, my_q, N, hh);
+            qw0 = qt * BM + wave * 32 * QB;
+            wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
+            st.load_q(qhead, table, qw0, N, n, hh);
             st.reset();
         }
         __syncthreads();  // tile i complete in both halves; their other buffers are free
         int qt1;
         const int kt1 = job_tile(i + 1, qt1);
         const NextLoads next{i + 1 < steps && kt1 >= 0, hbuf + ((i + 1) & 1) * T::BUF_ELEMS,
-                             kbase, vbase, table, kt1, N, wave, lane};
+                             tile_rsrc<D>(kbase, vbase, table, kt1 < 0 ? 0 : kt1, N), uwave, lane};
         if (kt >= 0 && kt < wave_tiles) {
             if (kt * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, kt * BN, my_q, n, hh, lane, scale_log2, stage, next);
+                st.template step<true>(Ks, kt * BN, qw0, n, hh, lane, scale_log2, stage, next);
             else
-                st.template step<false>(Ks, kt * BN, my_q, n, hh, lane, scale_log2, stage, next);
+                st.template step<false>(Ks, kt * BN, qw0, n, hh, lane, scale_log2, stage, next);
         } else if (next.active) {
-            stage.issue(next.buf, kbase, vbase, table, next.t, N, wave, lane);
+            stage.issue(next.buf, next.rs, uwave, lane);
         }
     }
 
     // half B: if its last rows were the light ones, they are complete now
     if (half == 1 && cur_qt == t_light && t_light != t_heavy) {
-        if (wave_tiles > 0 && my_q < N) {
-            const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-            st.write(out + (q_head + my_q) * D, lse ? lse + q_head + my_q : nullptr, l_tot, hh);
+        if (wave_tiles > 0) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int row = qw0 + 32 * b + n;
+                const float l_tot = st.l_run[b] + __shfl_xor(st.l_run[b], 32);
+                if (row < N)
+                    st.write(b, out + (q_head + row) * D, lse ? lse + q_head + row : nullptr, l_tot,
+                             hh);
+            }
         }
         st.reset();  // no share of the heavy rows
     }
@@ -555,36 +627,53 @@ __global__ __launch_bounds__(512, 1) void attn_pair_kernel(
     // ---- merge the two halves' partial states of the heavy rows ----
     __syncthreads();  // every wave is done with the tile buffers
     constexpr int SLOTS = 16 * W::DBLK + 2;
-    float* my = reinterpret_cast<float*>(smem) + (wave * SLOTS) * 64 + lane;  // [wave][slot][lane]
-    const float l_half = st.l_run + __shfl_xor(st.l_run, 32);
+    float* my = reinterpret_cast<float*>(smem) + (wave * QB * SLOTS) * 64 + lane;  // [wave][b][slot][lane]
+    float l_half[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) l_half[b] = st.l_run[b] + __shfl_xor(st.l_run[b], 32);
     if (half == 1) {
 #pragma unroll
-        for (int i = 0; i < W::DBLK; ++i)
+        for (int b = 0; b < QB; ++b) {
+            float* mb = my + b * SLOTS * 64;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) my[(16 * i + j) * 64] = st.acc[i][j];
-        my[(16 * W::DBLK) * 64] = st.m_run;
-        my[(16 * W::DBLK + 1) * 64] = l_half;
+            for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mb[(16 * i + j) * 64] = st.acc[b][i][j];
+            mb[(16 * W::DBLK) * 64] = st.m_run[b];
+            mb[(16 * W::DBLK + 1) * 64] = l_half[b];
+        }
     }
     __syncthreads();
     if (half == 1) return;
-    const int hq = t_heavy * BM + wave * 32 + n;  // this lane's heavy row
-    if (hq >= N) return;
-    const float m_b = my[(16 * W::DBLK) * 64];
-    const float l_b = my[(16 * W::DBLK + 1) * 64];
-    const float m = fmaxf(st.m_run, m_b);
-    const float a_a = __builtin_amdgcn_exp2f(st.m_run - m);
-    const float a_b = l_b > 0.f ? __builtin_amdgcn_exp2f(m_b - m) : 0.f;
 #pragma unroll
-    for (int i = 0; i < W::DBLK; ++i)
+    for (int b = 0; b < QB; ++b) {
+        const int hq = t_heavy * BM + wave * 32 * QB + 32 * b + n;  // this lane's heavy row
+        if (hq >= N) continue;
+        const float* mb = my + b * SLOTS * 64;
+        const float m_b = mb[(16 * W::DBLK) * 64];
+        const float l_b = mb[(16 * W::DBLK + 1) * 64];
+        const float m = fmaxf(st.m_run[b], m_b);
+        const float a_a = __builtin_amdgcn_exp2f(st.m_run[b] - m);
+        const float a_b = l_b > 0.f ? __builtin_amdgcn_exp2f(m_b - m) : 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) st.acc[i][j] = st.acc[i][j] * a_a + my[(16 * i + j) * 64] * a_b;
-    st.m_run = m;
-    const float l_tot = l_half * a_a + l_b * a_b;
-    st.write(out + (q_head + hq) * D, lse ? lse + q_head + hq : nullptr, l_tot, hh);
+        for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                st.acc[b][i][j] = st.acc[b][i][j] * a_a + mb[(16 * i + j) * 64] * a_b;
+        st.m_run[b] = m;
+        const float l_tot = l_half[b] * a_a + l_b * a_b;
+        st.write(b, out + (q_head + hq) * D, lse ? lse + q_head + hq : nullptr, l_tot, hh);
+    }
 }
+
+// Rows per wave: 32 x QB. One 64-row wave per SIMD (QB = 2) uses the full
+// register file and overlaps one block's softmax with the other's MFMAs.
+template <int D>
+constexpr int qb_for() { return 1; }
 
 template <int DT, int D, bool ROPE>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
+    constexpr int QB = qb_for<D>();
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int n_qtiles = (a.N + BM - 1) / BM;
     const int n_pairs = (n_qtiles + 1) / 2;
@@ -598,12 +687,12 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     if (a.shape == ATTN_SHAPE_PAIR) pair = true;
     if (a.shape == ATTN_SHAPE_TILE) pair = false;
     if (pair) {
-        attn_pair_kernel<DT, D, ROPE><<<dim3((unsigned)pair_units), 512, 0, stream>>>(
+        attn_pair_kernel<DT, D, ROPE, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
     } else {
-        attn_fwd_kernel<DT, D, ROPE><<<dim3((unsigned)tile_units), 256, 0, stream>>>(
+        attn_fwd_kernel<DT, D, ROPE, QB><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);

@@ -198,12 +198,12 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 // the same K operands and its PV the same V operands; with QB = 2 the second
 // block's score MFMAs overlap the first block's softmax, and the first block's
 // PV MFMAs overlap the second block's softmax, inside one wave.
-template <int DT, int D, bool ROPE, int QB>
+template <int DT, int D, bool ROPE, int QB, int NW = 4 / QB>
 struct WaveAttn {
     typedef Fmt<DT> F;
     typedef typename F::vec8 vec8;
     typedef Tile<D> T;
-    typedef TileStage<DT, D, ROPE, 4 / QB> Stage;  // a row block is 4 / QB waves
+    typedef TileStage<DT, D, ROPE, NW> Stage;  // NW waves share each key tile
     static constexpr int QCH = D / 16;   // 16-deep MFMA steps over the head dim
     static constexpr int DBLK = D / 32;  // 32-row blocks of O^T
 
@@ -425,44 +425,52 @@ struct WaveAttn {
 struct Unit {
     int b, g, h, idx;  // idx = query tile slot (unpaired) or pair index
 };
-__device__ __forceinline__ Unit decode_unit(int Hq, int Hkv, int per_head) {
+// hpu = query heads per unit (consecutive heads of one GQA group); h is the
+// first of them.
+__device__ __forceinline__ Unit decode_unit(int Hq, int Hkv, int per_head, int hpu = 1) {
     const int group = Hq / Hkv;
+    const int packs = group / hpu;
     const int units = gridDim.x;
     int u = blockIdx.x;
     if (units % NXCD == 0) u = (u % NXCD) * (units / NXCD) + u / NXCD;
     Unit r;
-    const int hg = u % group;
-    const int rest = u / group;
+    const int hp = u % packs;
+    const int rest = u / packs;
     r.idx = rest % per_head;
     const int bg = rest / per_head;
     r.g = bg % Hkv;
     r.b = bg / Hkv;
-    r.h = r.g * group + hg;
+    r.h = r.g * group + hp * hpu;
     return r;
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup (4 / QB waves, BM = 128 rows) per query tile, heaviest first.
+// One workgroup per query tile (BM = 128 rows), heaviest first. The
+// workgroup serves HG query heads of one GQA group (4 / QB waves per head),
+// which all read the same key/value tiles: each tile is loaded (and, with
+// RoPE, rotated) once for HG x 128 query rows.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool ROPE, int QB>
-__global__ __launch_bounds__(256 / QB, QB == 1 ? 2 : 2) void attn_fwd_kernel(
+template <int DT, int D, bool ROPE, int QB, int HG>
+__global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, float scale_log2) {
     typedef Tile<D> T;
-    typedef WaveAttn<DT, D, ROPE, QB> W;
+    constexpr int WPH = 4 / QB;  // waves per head
+    typedef WaveAttn<DT, D, ROPE, QB, WPH * HG> W;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = tid >> 6;         // 0 .. WPH * HG - 1: every wave loads a share of each tile
+    const int rwave = wave % WPH;      // row block of the wave inside its head
     const int lane = tid & 63;
     const int n = lane & 31;
     const int hh = lane >> 5;
 
-    const Unit un = decode_unit(Hq, Hkv, n_qtiles);
+    const Unit un = decode_unit(Hq, Hkv, n_qtiles, HG);
     const int qtile = n_qtiles - 1 - un.idx;
-    const int qw0 = qtile * BM + wave * 32 * QB;  // the wave's first row
-    const int64_t q_head = ((int64_t)un.b * Hq + un.h) * N;
+    const int qw0 = qtile * BM + rwave * 32 * QB;  // the wave's first row
+    const int64_t q_head = ((int64_t)un.b * Hq + un.h + wave / WPH) * N;
     const int64_t kv_head = ((int64_t)un.b * Hkv + un.g) * N;
     const uint16_t* kbase = k + kv_head * D;
     const uint16_t* vbase = v + kv_head * D;
@@ -691,8 +699,15 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
+    } else if ((a.Hq / a.Hkv) % 2 == 0) {
+        // GQA: two query heads of a group per workgroup share every key tile
+        attn_fwd_kernel<DT, D, ROPE, QB, 2><<<dim3((unsigned)(tile_units / 2)), 512 / QB, 0,
+                                             stream>>>(
+            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
+            a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
     } else {
-        attn_fwd_kernel<DT, D, ROPE, QB><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
+        attn_fwd_kernel<DT, D, ROPE, QB, 1><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);

@@ -77,7 +77,8 @@ def ingest_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir):
         vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(f[0])) if pick(r["Kernel_Name"])]
         return sum(vals) / len(vals), len(vals)
 
-    fused = lambda k: "attn_" in k and k.split("(")[0].rstrip().endswith("true>")  # noqa: E731
+    # the attention kernels' template arguments are <dtype, head dim, rope, ...>
+    fused = lambda k: "attn_" in k and ", true" in k.split("(")[0]  # noqa: E731
     copy = lambda k: "copyBuffer" in k or "elementwise" in k  # noqa: E731
     fetch, nf = per_dispatch(fetch_dir, fused)
     write, nw = per_dispatch(write_dir, fused)
@@ -251,7 +252,7 @@ def main():
                    "rope_base": base, "causal": True,
                    "step": "attn_rope_causal_fwd + (rope_prerotate -> attn_causal_fwd)",
                    "flops_per_path": fl},
-        "roofline": {"kernel": "attn_fwd_kernel<bf16,128,rope>", "bound": "mfma",
+        "roofline": {"kernel": "attn_rope_causal_fwd kernel (bf16, D=128)", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic()},
         "paths": paths,

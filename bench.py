@@ -14,13 +14,17 @@ Also printed in the same JSON line:
     against the dense bf16 MFMA peak;
   * paths: per-path and per-kernel times (warm, and cold after a 512 MiB
     cache flush), TFLOP/s, % of MFMA peak, rope_prerotate GB/s vs 8 TB/s;
-  * crossover: fused vs pre-rotation times over the D=64 fp16 MHA sweep
-    (N = 2048 .. 32768) and the GQA shapes, with the measured crossover N*;
+    also the GQA split path (rope_prerotate_k then attn_rope_q_causal_fwd),
+    timed after the step loop and not part of `value`;
+  * crossover: fused vs pre-rotation (and split) times over the D=64 fp16
+    MHA sweep (N = 2048 .. 32768) and the GQA shapes, with the measured
+    crossover N* of fused vs pre-rotation;
   * cpu_baseline: the fp64 CPU oracle timed on this host over the full
     workload (rotation + causal attention), in the same unit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-       [--no-cpu] [--only fused|prerotate|rope|attn [--workload NAME]]
+       [--no-cpu] [--only fused|prerotate|rope|attn|split|rope_k|attn_q
+       [--workload NAME]]
        [--copy-calib]
 """
 import argparse
@@ -37,7 +41,14 @@ MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}  # MI355X dense, published
 CSRC = os.path.join(ROOT, "rotary_position_embedding_causal_amd", "csrc")
 ATTN_SOURCES = ("attn_fwd.hip", "rac_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fused_traffic_llama3_8b_gqa_n2048.json")
-FUSED_KERNEL_MATCH = "attn_"  # attention kernels; the fused ones end in "true>"
+
+
+def rotation_mode(kernel_name):
+    """Rotation-mode template argument of an attention kernel name
+    (attn_*_kernel<dtype, head dim, mode, ...>): 0 none, 1 Q and K, 2 Q only."""
+    args = kernel_name.split("(")[0].split("<", 1)[1].rsplit(">", 1)[0].split(",")
+    return int(args[2])
+
 HBM_PEAK_GBS = 8000.0
 MAIN = "llama3_8b_gqa_n2048"
 METRIC = "causal RoPE-attn fwd TFLOP/s (fused & pre-rotate) + % of MFMA peak; N*"
@@ -77,8 +88,7 @@ def ingest_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir):
         vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(f[0])) if pick(r["Kernel_Name"])]
         return sum(vals) / len(vals), len(vals)
 
-    # the attention kernels' template arguments are <dtype, head dim, rope, ...>
-    fused = lambda k: "attn_" in k and ", true" in k.split("(")[0]  # noqa: E731
+    fused = lambda k: "attn_" in k and "<" in k and rotation_mode(k) == 1  # noqa: E731
     copy = lambda k: "copyBuffer" in k or "elementwise" in k  # noqa: E731
     fetch, nf = per_dispatch(fetch_dir, fused)
     write, nw = per_dispatch(write_dir, fused)
@@ -107,6 +117,10 @@ def prerot_bytes(w):
     return 2.0 * w["B"] * (w["Hq"] + w["Hkv"]) * w["N"] * w["D"] * 2
 
 
+def prerot_k_bytes(w):
+    return 2.0 * w["B"] * w["Hkv"] * w["N"] * w["D"] * 2
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fused", "prerotate", "rope", "attn"], default=None,
+    ap.add_argument("--only", choices=["fused", "prerotate", "rope", "attn", "split", "rope_k",
+                                       "attn_q"], default=None,
                     help="time one kernel/path alone (for profiler runs)")
     ap.add_argument("--workload", default=MAIN,
                     help="workload of the --only runs (a name from inputs.WORKLOADS)")
@@ -160,6 +175,9 @@ def main():
     lse_p = torch.empty_like(lse_f)
     qr = torch.empty_like(qd)
     kr = torch.empty_like(kd)
+    kr_s = torch.empty_like(kd)
+    out_s = torch.empty_like(qd)
+    lse_s = torch.empty_like(lse_f)
 
     def fused():
         rac.attn_rope_causal_fwd(qd, kd, vd, base, out=out_f, lse=lse_f)
@@ -170,11 +188,19 @@ def main():
     def attn():
         rac.attn_causal_fwd(qr, kr, vd, out=out_p, lse=lse_p)
 
+    # the GQA split path: K alone through the streaming pass, Q rotated in the kernel
+    def rope_k():
+        rac.rope_prerotate_k(kd, base, k_rot=kr_s)
+
+    def attn_q():
+        rac.attn_rope_q_causal_fwd(qd, kr_s, vd, base, out=out_s, lse=lse_s)
+
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     if args.only:
         fn = {"fused": fused, "rope": rope, "attn": attn,
-              "prerotate": lambda: (rope(), attn())}[args.only]
+              "prerotate": lambda: (rope(), attn()), "rope_k": rope_k, "attn_q": attn_q,
+              "split": lambda: (rope_k(), attn_q())}[args.only]
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -229,6 +255,20 @@ def main():
 
     c_fused, c_rope, c_attn = cold(fused), cold(rope), cold(attn)
     pb = prerot_bytes(w)
+
+    # ---- the GQA split path, timed the same way after the timed region ----
+    for _ in range(args.warmup):
+        rope_k(); attn_q()
+    torch.cuda.synchronize()
+    rk_ev = [(ev(), ev()) for _ in range(args.steps)]
+    aq_ev = [(ev(), ev()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        rk_ev[i][0].record(); rope_k(); rk_ev[i][1].record()
+        aq_ev[i][0].record(); attn_q(); aq_ev[i][1].record()
+    torch.cuda.synchronize()
+    t_rk, t_aq = avg_ms(rk_ev), avg_ms(aq_ev)
+    c_rk, c_aq = cold(rope_k), cold(attn_q)
+    kb = prerot_k_bytes(w)
     paths = {
         "fused": {"ms": t_fused, "tflops": fl / t_fused / 1e9, "mfma_frac": fl / t_fused / 1e9 / peak,
                   "cold_ms": c_fused, "cold_tflops": fl / c_fused / 1e9},
@@ -241,6 +281,13 @@ def main():
                            "hbm_frac": pb / t_rope / 1e6 / HBM_PEAK_GBS, "cold_ms": c_rope,
                            "cold_gbs": pb / c_rope / 1e6,
                            "cold_hbm_frac": pb / c_rope / 1e6 / HBM_PEAK_GBS, "bytes": pb},
+        "split": {"ms": t_rk + t_aq, "tflops": fl / (t_rk + t_aq) / 1e9,
+                  "mfma_frac": fl / (t_rk + t_aq) / 1e9 / peak, "cold_ms": c_rk + c_aq},
+        "attn_rope_q_causal_fwd": {"ms": t_aq, "tflops": fl / t_aq / 1e9,
+                                   "mfma_frac": fl / t_aq / 1e9 / peak, "cold_ms": c_aq},
+        "rope_prerotate_k": {"ms": t_rk, "gbs": kb / t_rk / 1e6,
+                             "hbm_frac": kb / t_rk / 1e6 / HBM_PEAK_GBS, "cold_ms": c_rk,
+                             "cold_gbs": kb / c_rk / 1e6, "bytes": kb},
     }
 
     result = {
@@ -279,11 +326,14 @@ def crossover(torch, rac, inputs, dev, ev, reps=10):
         o = torch.empty_like(qd)
         lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
         qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+        krs = torch.empty_like(kd)
         fns = {
             "fused": lambda: rac.attn_rope_causal_fwd(qd, kd, vd, base, out=o, lse=lse),
             "prerotate": lambda: (rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
                                   rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse)),
             "attn": lambda: rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse),
+            "split": lambda: (rac.rope_prerotate_k(kd, base, k_rot=krs),
+                              rac.attn_rope_q_causal_fwd(qd, krs, vd, base, out=o, lse=lse)),
         }
         t = {}
         for key, fn in fns.items():
@@ -299,10 +349,11 @@ def crossover(torch, rac, inputs, dev, ev, reps=10):
         fl = attn_flops(w)
         rows.append({"workload": name, "N": w["N"], "fused_ms": t["fused"],
                      "prerotate_ms": t["prerotate"], "attn_only_ms": t["attn"],
+                     "split_ms": t["split"],
                      "fused_tflops": fl / t["fused"] / 1e9,
                      "prerotate_tflops": fl / t["prerotate"] / 1e9,
                      "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0})
-        del qd, kd, vd, o, lse, qr, kr
+        del qd, kd, vd, o, lse, qr, kr, krs
         torch.cuda.empty_cache()
     sweep = [r for r in rows if r["workload"].startswith("mha_d64")]
     n_star = None

@@ -1,7 +1,7 @@
 /*
  * rac.h -- RoPE + causal attention forward on AMD MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels. Three operations:
+ * A C ABI over hand-written HIP kernels. Five operations and a dispatcher:
  *
  *   attn_rope_causal_fwd  one kernel: rotary position embedding applied to the
  *                         query and key tiles inside a causal attention
@@ -10,6 +10,16 @@
  *                         Q and K ("pre-rotation").
  *   attn_causal_fwd       causal attention forward on already-rotated inputs;
  *                         with rope_prerotate it forms the pre-rotation path.
+ *   rope_prerotate_k      the pre-rotation pass on K alone, and
+ *   attn_rope_q_causal_fwd  causal attention that rotates Q in the kernel (once
+ *                         per query row) and takes K already rotated: together
+ *                         the "GQA split" path, which moves only the Hkv key
+ *                         heads through the streaming pass instead of all
+ *                         Hq + Hkv heads and rotates no key tile in the kernel.
+ *   attn_rope_causal_auto the same result as attn_rope_causal_fwd through
+ *                         whichever of the three paths is fastest for the
+ *                         shape on MI355X (the report's paragraph 5: the
+ *                         choice is measured per architecture and shape).
  *
  * The two paths and the choice between them are the subject of "AttnFuse Makes
  * RoPE a First-Class Attention Compilation Operation" (tdteach paper-news,
@@ -70,6 +80,8 @@
 #ifndef RAC_H
 #define RAC_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -114,6 +126,59 @@ int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
 int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                     int B, int Hq, int Hkv, int N, int D,
                     int dtype, void* stream);
+
+/*
+ * GQA split path, first half: k_rot = RoPE(k), each element rounded once to
+ * `dtype` -- exactly the k_rot that rope_prerotate writes. k, k_rot:
+ * [B,Hkv,N,D]; k_rot may equal k (in place), any other overlap is an error.
+ * B*Hkv <= 524280. Not a method step of its own on the pages: it splits the
+ * cost model of the AttnFuse report (paragraph 3) between its two terms, the
+ * bandwidth cost paid for K only and the in-kernel cost for Q only.
+ */
+int rope_prerotate_k(const void* k, void* k_rot, int B, int Hkv, int N, int D,
+                     double rope_base, int dtype, void* stream);
+
+/*
+ * GQA split path, second half: causal attention with RoPE applied to each
+ * query row inside the kernel (as attn_rope_causal_fwd does) and keys taken
+ * already rotated (k_rot, e.g. from rope_prerotate_k). With k_rot =
+ * rope_prerotate_k(k) the result is bit-identical to attn_rope_causal_fwd.
+ * Same layouts and rules as attn_rope_causal_fwd.
+ */
+int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void* out,
+                           float* lse, int B, int Hq, int Hkv, int N, int D,
+                           double rope_base, int dtype, void* stream);
+
+enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
+
+/*
+ * Dispatcher: out/lse of attn_rope_causal_fwd (bit-identical: every path hands
+ * the same rotated operands to the same attention arithmetic), computed by the
+ * path measured fastest on MI355X for this shape -- pre-rotation of Q and K
+ * for short sequences, the split path for long ones, never the fused kernel
+ * when a workspace is given (rotating every key tile in the kernel cost
+ * 28-43 % over plain attention, more than the streaming pass). The choice of
+ * pre-rotation versus in-kernel rotation is the one the AttnFuse report,
+ * paragraphs 3 and 5, says depends on the GPU and the shape.
+ *
+ * workspace: caller-owned device memory for the rotated copies (Q' and K',
+ * or K' alone), 16-byte aligned, not overlapping any tensor argument; the
+ * library allocates nothing. If it is NULL or smaller than the preferred
+ * path needs, the next path it holds is taken (split, then fused, which
+ * needs none). rac_auto_plan tells the path and the bytes the preferred path
+ * needs. Calls that share a workspace must not run concurrently.
+ */
+int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int N, int D, double rope_base,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The path (RAC_PATH_*) attn_rope_causal_auto takes for this shape and
+ * workspace size, and the workspace bytes its preferred path needs. Either
+ * output pointer may be NULL. Host only: no GPU work, no allocation.
+ */
+int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t workspace_bytes,
+                  int* path, size_t* preferred_bytes);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 const char* rac_last_error(void);

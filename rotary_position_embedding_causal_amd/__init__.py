@@ -10,6 +10,10 @@ Operations (names as in the C ABI):
   attn_rope_causal_fwd(q, k, v, rope_base)  -> (out, lse)   fused RoPE + attention
   rope_prerotate(q, k, rope_base)           -> (q_rot, k_rot)
   attn_causal_fwd(q, k, v)                  -> (out, lse)   on pre-rotated inputs
+  rope_prerotate_k(k, rope_base)            -> k_rot          K only (GQA split path)
+  attn_rope_q_causal_fwd(q, k_rot, v, rope_base) -> (out, lse) RoPE on Q in the kernel
+  attn_rope_causal_auto(q, k, v, rope_base, workspace) -> (out, lse) fastest path
+  auto_plan(B, Hq, Hkv, N, D, dtype, workspace_bytes) -> (path, preferred_bytes)
 Tensors are contiguous [B, H, N, D] bf16/fp16 on one HIP device; lse is fp32
 [B, Hq, N] (natural log).
 """
@@ -26,8 +30,11 @@ LIB_PATH = os.path.join(_HERE, "librac.so")
 RAC_BF16, RAC_FP16 = 0, 1
 RAC_OK, RAC_ERR_ARG, RAC_ERR_ALIGN, RAC_ERR_UNSUPPORTED, RAC_ERR_HIP = 0, -1, -2, -3, -4
 RAC_MAX_N = 1 << 22
-EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rac_last_error",
-            "rac_release_tables")
+EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_prerotate_k",
+            "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
+            "rac_last_error", "rac_release_tables")
+RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
+PATH_NAMES = {RAC_PATH_FUSED: "fused", RAC_PATH_PREROTATE: "prerotate", RAC_PATH_SPLIT: "split"}
 
 _DTYPES = {torch.bfloat16: RAC_BF16, torch.float16: RAC_FP16}
 
@@ -54,6 +61,15 @@ def lib() -> ctypes.CDLL:
     L.rope_prerotate.restype = i
     L.attn_causal_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, i, vp]
     L.attn_causal_fwd.restype = i
+    L.rope_prerotate_k.argtypes = [vp, vp, i, i, i, i, d, i, vp]
+    L.rope_prerotate_k.restype = i
+    L.attn_rope_q_causal_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, vp]
+    L.attn_rope_q_causal_fwd.restype = i
+    sz = ctypes.c_size_t
+    L.attn_rope_causal_auto.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, vp, sz, vp]
+    L.attn_rope_causal_auto.restype = i
+    L.rac_auto_plan.argtypes = [i, i, i, i, i, i, sz, ctypes.POINTER(i), ctypes.POINTER(sz)]
+    L.rac_auto_plan.restype = i
     L.rac_last_error.argtypes = []
     L.rac_last_error.restype = ctypes.c_char_p
     L.rac_release_tables.argtypes = []
@@ -168,3 +184,68 @@ def prerotate_path(q, k, v, rope_base: float, want_lse: bool = True):
     """The pre-rotation path: rope_prerotate then attn_causal_fwd. Returns (out, lse)."""
     q_rot, k_rot = rope_prerotate(q, k, rope_base)
     return attn_causal_fwd(q_rot, k_rot, v, want_lse=want_lse)
+
+
+def rope_prerotate_k(k, rope_base: float, k_rot=None):
+    """Pre-rotation of K alone (the GQA split path). Returns k_rot; k_rot=k is in place."""
+    B, Hkv, Hkv2, N, D, dt = _check_qkv(k, k, None)
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    if k_rot.shape != k.shape or k_rot.dtype != k.dtype or not k_rot.is_contiguous() \
+            or k_rot.device != k.device:
+        raise ValueError("k_rot must be a contiguous tensor like k")
+    with torch.cuda.device(k.device):
+        rc = lib().rope_prerotate_k(_ptr(k), _ptr(k_rot), B, Hkv, N, D, float(rope_base), dt,
+                                    _stream(k.device))
+    check(rc, "rope_prerotate_k")
+    return k_rot
+
+
+def attn_rope_q_causal_fwd(q, k_rot, v, rope_base: float, out=None, lse=None,
+                           want_lse: bool = True):
+    """Causal attention rotating Q in the kernel; K already rotated. Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k_rot, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_q_causal_fwd(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(lse),
+                                          B, Hq, Hkv, N, D, float(rope_base), dt,
+                                          _stream(q.device))
+    check(rc, "attn_rope_q_causal_fwd")
+    return out, lse
+
+
+def split_path(q, k, v, rope_base: float, want_lse: bool = True):
+    """The GQA split path: rope_prerotate_k then attn_rope_q_causal_fwd. Returns (out, lse)."""
+    return attn_rope_q_causal_fwd(q, rope_prerotate_k(k, rope_base), v, rope_base,
+                                  want_lse=want_lse)
+
+
+def auto_plan(B: int, Hq: int, Hkv: int, N: int, D: int, dtype, workspace_bytes: int = 0):
+    """(path, preferred_bytes): the RAC_PATH_* attn_rope_causal_auto takes for this shape
+    with `workspace_bytes` of workspace, and the bytes its preferred path needs."""
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    path, need = ctypes.c_int(0), ctypes.c_size_t(0)
+    check(lib().rac_auto_plan(B, Hq, Hkv, N, D, dt, int(workspace_bytes), ctypes.byref(path),
+                              ctypes.byref(need)), "rac_auto_plan")
+    return path.value, need.value
+
+
+def attn_rope_causal_auto(q, k, v, rope_base: float, workspace=None, out=None, lse=None,
+                          want_lse: bool = True):
+    """RoPE + causal attention through the path measured fastest for the shape.
+
+    `workspace` is a caller-owned device tensor (any dtype, contiguous) for the rotated
+    copies; None or too small falls back to a path that fits (the fused kernel needs
+    none). auto_plan() gives the bytes the preferred path needs. Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    wbytes = 0
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        wbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_auto(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         B, Hq, Hkv, N, D, float(rope_base), dt,
+                                         _ptr(workspace), wbytes, _stream(q.device))
+    check(rc, "attn_rope_causal_auto")
+    return out, lse

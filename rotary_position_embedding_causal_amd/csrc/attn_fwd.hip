@@ -1,5 +1,6 @@
 // attn_fwd.hip -- causal MHA/GQA attention forward for gfx950, with RoPE fused
-// into the tile loads (ROPE = true) or not (ROPE = false).
+// into the loads of both Q and K (RM = ROT_QK), of Q only (RM = ROT_Q: the
+// GQA split path, K rotated beforehand) or of neither (RM = ROT_NONE).
 //
 // Method: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (rainbus digest), background "FlashAttention and online softmax"
@@ -198,12 +199,14 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 // the same K operands and its PV the same V operands; with QB = 2 the second
 // block's score MFMAs overlap the first block's softmax, and the first block's
 // PV MFMAs overlap the second block's softmax, inside one wave.
-template <int DT, int D, bool ROPE, int QB, int NW = 4 / QB>
+template <int DT, int D, int RM, int QB, int NW = 4 / QB>
 struct WaveAttn {
+    static constexpr bool ROPE_Q = RM != ROT_NONE;  // rotate Q rows when loading them
+    static constexpr bool ROPE_K = RM == ROT_QK;    // rotate every K tile in LDS
     typedef Fmt<DT> F;
     typedef typename F::vec8 vec8;
     typedef Tile<D> T;
-    typedef TileStage<DT, D, ROPE, NW> Stage;  // NW waves share each key tile
+    typedef TileStage<DT, D, ROPE_K, NW> Stage;  // NW waves share each key tile
     static constexpr int QCH = D / 16;   // 16-deep MFMA steps over the head dim
     static constexpr int DBLK = D / 32;  // 32-row blocks of O^T
 
@@ -228,7 +231,7 @@ struct WaveAttn {
         }
     }
 
-    // Q rows q_first + 32b + n as MFMA B operands (rotated once if ROPE).
+    // Q rows q_first + 32b + n as MFMA B operands (rotated once if ROPE_Q).
     __device__ __forceinline__ void load_q(const uint16_t* qrow0, const float* __restrict__ table,
                                            int q_first, int N, int n, int hh) {
 #pragma unroll
@@ -240,7 +243,7 @@ struct WaveAttn {
                 if (row < N) {
                     const int d0 = 16 * c + 8 * hh;
                     w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)row * D + d0);
-                    if (ROPE) {
+                    if (ROPE_Q) {
                         const f32x4* t =
                             reinterpret_cast<const f32x4*>(table + (int64_t)row * D + d0);
                         w = rope_rotate8<DT>(w, t[0], t[1]);
@@ -450,14 +453,14 @@ __device__ __forceinline__ Unit decode_unit(int Hq, int Hkv, int per_head, int h
 // which all read the same key/value tiles: each tile is loaded (and, with
 // RoPE, rotated) once for HG x 128 query rows.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool ROPE, int QB, int HG>
+template <int DT, int D, int RM, int QB, int HG>
 __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, float scale_log2) {
     typedef Tile<D> T;
     constexpr int WPH = 4 / QB;  // waves per head
-    typedef WaveAttn<DT, D, ROPE, QB, WPH * HG> W;
+    typedef WaveAttn<DT, D, RM, QB, WPH * HG> W;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
 
     const int tid = threadIdx.x;
@@ -514,14 +517,14 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
 // ---------------------------------------------------------------------------
 // Paired, split, load-balanced launch: two halves of 4 / QB waves each.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool ROPE, int QB>
+template <int DT, int D, int RM, int QB>
 __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, int n_pairs,
     float scale_log2) {
     typedef Tile<D> T;
-    typedef WaveAttn<DT, D, ROPE, QB> W;
+    typedef WaveAttn<DT, D, RM, QB> W;
     constexpr int HT = 256 / QB;  // threads per half
     // per half: two tile buffers; after the loop the same memory holds the merge data
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * T::BUF_ELEMS];
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
 template <int D>
 constexpr int qb_for() { return 1; }
 
-template <int DT, int D, bool ROPE>
+template <int DT, int D, int RM>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     constexpr int QB = qb_for<D>();
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -695,19 +698,19 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     if (a.shape == ATTN_SHAPE_PAIR) pair = true;
     if (a.shape == ATTN_SHAPE_TILE) pair = false;
     if (pair) {
-        attn_pair_kernel<DT, D, ROPE, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
+        attn_pair_kernel<DT, D, RM, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
     } else if ((a.Hq / a.Hkv) % 2 == 0) {
         // GQA: two query heads of a group per workgroup share every key tile
-        attn_fwd_kernel<DT, D, ROPE, QB, 2><<<dim3((unsigned)(tile_units / 2)), 512 / QB, 0,
+        attn_fwd_kernel<DT, D, RM, QB, 2><<<dim3((unsigned)(tile_units / 2)), 512 / QB, 0,
                                              stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
     } else {
-        attn_fwd_kernel<DT, D, ROPE, QB, 1><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
+        attn_fwd_kernel<DT, D, RM, QB, 1><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
             a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
@@ -715,15 +718,21 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DT, bool ROPE>
+template <int DT, int RM>
 static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
-    return a.D == 64 ? launch_typed<DT, 64, ROPE>(a, stream) : launch_typed<DT, 128, ROPE>(a, stream);
+    return a.D == 64 ? launch_typed<DT, 64, RM>(a, stream) : launch_typed<DT, 128, RM>(a, stream);
 }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, bool rope, hipStream_t stream) {
-    if (a.dtype == DT_BF16)
-        return rope ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_BF16, false>(a, stream);
-    return rope ? launch_dt<DT_FP16, true>(a, stream) : launch_dt<DT_FP16, false>(a, stream);
+template <int DT>
+static hipError_t launch_rot(const AttnArgs& a, int rot, hipStream_t stream) {
+    if (rot == ROT_QK) return launch_dt<DT, ROT_QK>(a, stream);
+    if (rot == ROT_Q) return launch_dt<DT, ROT_Q>(a, stream);
+    return launch_dt<DT, ROT_NONE>(a, stream);
+}
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream) {
+    return a.dtype == DT_BF16 ? launch_rot<DT_BF16>(a, rot, stream)
+                              : launch_rot<DT_FP16>(a, rot, stream);
 }
 
 }  // namespace rac

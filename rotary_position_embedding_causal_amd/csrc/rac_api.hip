@@ -154,6 +154,41 @@ int attn_shape_from_env() {
     return rac::ATTN_SHAPE_AUTO;
 }
 
+// ---- the path dispatcher ------------------------------------------------------
+//
+// All three paths give bit-identical results (they hand the same rotated
+// operands to the same attention arithmetic), so the choice is about time
+// only. Measured on MI355X (bench crossover rows, bf16 D=128 GQA 4:1 at
+// N = 2048 / 4096 (B=4) / 8192 and fp16 D=64 MHA at N = 2048 .. 32768): the
+// fused kernel was never the fastest -- rotating every K tile in the kernel
+// costs 28-43 % over plain attention, more than the streaming pass costs at
+// 8 TB/s; pre-rotation of Q and K was fastest up to N = 2048 (GQA) and
+// N = 6144 (MHA); the split path (K pre-rotated, Q rotated in the kernel) was
+// fastest beyond, where the in-kernel Q rotation is amortised over more key
+// tiles and moving Q through the pass costs more.
+size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
+    const size_t q = (size_t)B * Hq * N * D * 2, k = (size_t)B * Hkv * N * D * 2;
+    const size_t q16 = (q + 255) & ~(size_t)255;  // K' starts 256-byte aligned
+    if (path == RAC_PATH_PREROTATE) return q16 + k;
+    if (path == RAC_PATH_SPLIT) return k;
+    return 0;
+}
+
+int preferred_path(int Hq, int Hkv, int N) {
+    const int n_split = Hq / Hkv >= 2 ? 3072 : 7168;  // between the measured crossings
+    return N >= n_split ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
+}
+
+// The preferred path if the workspace holds it, else the next one it holds.
+int plan_path(int B, int Hq, int Hkv, int N, int D, size_t workspace_bytes) {
+    const int pref = preferred_path(Hq, Hkv, N);
+    if (workspace_bytes >= path_workspace(pref, B, Hq, Hkv, N, D)) return pref;
+    if (pref == RAC_PATH_PREROTATE &&
+        workspace_bytes >= path_workspace(RAC_PATH_SPLIT, B, Hq, Hkv, N, D))
+        return RAC_PATH_SPLIT;
+    return RAC_PATH_FUSED;
+}
+
 int hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(RAC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -175,8 +210,24 @@ int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out,
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
     rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
-    return hip_status(rac::launch_attn_fwd(a, true, static_cast<hipStream_t>(stream)),
+    return hip_status(rac::launch_attn_fwd(a, rac::ROT_QK, static_cast<hipStream_t>(stream)),
                       "attn_rope_causal_fwd launch");
+}
+
+int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void* out,
+                           float* lse, int B, int Hq, int Hkv, int N, int D, double rope_base,
+                           int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k_rot, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    const float* table = nullptr;
+    if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    rac::AttnArgs a{q, k_rot, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
+    return hip_status(rac::launch_attn_fwd(a, rac::ROT_Q, static_cast<hipStream_t>(stream)),
+                      "attn_rope_q_causal_fwd launch");
 }
 
 int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -187,7 +238,7 @@ int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, floa
     if (empty) return ok();
     if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     rac::AttnArgs a{q, k, v, out, lse, nullptr, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
-    return hip_status(rac::launch_attn_fwd(a, false, static_cast<hipStream_t>(stream)),
+    return hip_status(rac::launch_attn_fwd(a, rac::ROT_NONE, static_cast<hipStream_t>(stream)),
                       "attn_causal_fwd launch");
 }
 
@@ -216,6 +267,73 @@ int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B
     return hip_status(rac::launch_rope_prerotate(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D,
                                                  dtype, static_cast<hipStream_t>(stream)),
                       "rope_prerotate launch");
+}
+
+int rope_prerotate_k(const void* k, void* k_rot, int B, int Hkv, int N, int D, double rope_base,
+                     int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hkv, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((int64_t)B * Hkv > 8LL * 65535) return fail(RAC_ERR_ARG, "B*Hkv must be <= 524280");
+    if (empty) return ok();
+    if (!k || !k_rot) return fail(RAC_ERR_ARG, "k and k_rot must be non-null");
+    if (!aligned16(k) || !aligned16(k_rot))
+        return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int64_t kbytes = (int64_t)B * Hkv * N * D * 2;
+    if (k_rot != k && overlap(k_rot, kbytes, k, kbytes))
+        return fail(RAC_ERR_ARG, "k_rot may alias k exactly, and must not overlap it otherwise");
+    const float* table = nullptr;
+    if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    // the pre-rotation pass with no query slabs
+    return hip_status(rac::launch_rope_prerotate(nullptr, k, nullptr, k_rot, table, B, 0, Hkv, N,
+                                                 D, dtype, static_cast<hipStream_t>(stream)),
+                      "rope_prerotate_k launch");
+}
+
+int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t workspace_bytes,
+                  int* path, size_t* preferred_bytes) {
+    bool empty = false;
+    const int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    const int pref = preferred_path(Hq, Hkv, N);
+    if (path) *path = empty ? RAC_PATH_FUSED : plan_path(B, Hq, Hkv, N, D, workspace_bytes);
+    if (preferred_bytes) *preferred_bytes = empty ? 0 : path_workspace(pref, B, Hq, Hkv, N, D);
+    return ok();
+}
+
+int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    if (!workspace) workspace_bytes = 0;
+    const int path = plan_path(B, Hq, Hkv, N, D, workspace_bytes);
+    if (path == RAC_PATH_FUSED)
+        return attn_rope_causal_fwd(q, k, v, out, lse, B, Hq, Hkv, N, D, rope_base, dtype, stream);
+    if (!aligned16(workspace)) return fail(RAC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
+    const int64_t kvbytes = (int64_t)B * Hkv * N * D * 2;
+    const int64_t wbytes = (int64_t)path_workspace(path, B, Hq, Hkv, N, D);
+    if (overlap(workspace, wbytes, q, qbytes) || overlap(workspace, wbytes, k, kvbytes) ||
+        overlap(workspace, wbytes, v, kvbytes) || overlap(workspace, wbytes, out, qbytes) ||
+        (lse && overlap(workspace, wbytes, lse, (int64_t)B * Hq * N * 4)))
+        return fail(RAC_ERR_ARG, "workspace must not overlap q, k, v, out or lse");
+    char* ws = static_cast<char*>(workspace);
+    if (path == RAC_PATH_SPLIT) {
+        if ((rc = rope_prerotate_k(k, ws, B, Hkv, N, D, rope_base, dtype, stream)) != RAC_OK)
+            return rc;
+        return attn_rope_q_causal_fwd(q, ws, v, out, lse, B, Hq, Hkv, N, D, rope_base, dtype,
+                                      stream);
+    }
+    char* kr = ws + (((size_t)qbytes + 255) & ~(size_t)255);
+    if ((rc = rope_prerotate(q, k, ws, kr, B, Hq, Hkv, N, D, rope_base, dtype, stream)) != RAC_OK)
+        return rc;
+    return attn_causal_fwd(ws, kr, v, out, lse, B, Hq, Hkv, N, D, dtype, stream);
 }
 
 const char* rac_last_error(void) { return g_last_error.c_str(); }

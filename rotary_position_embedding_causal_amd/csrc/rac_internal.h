@@ -17,14 +17,18 @@ struct AttnArgs {
     const void* v;
     void* out;
     float* lse;          // may be null
-    const float* table;  // cos/sin table [>= N][D] (fp32, cos/sin interleaved); null when no RoPE
+    const float* table;  // cos/sin table [>= N][D] (fp32, cos/sin interleaved); null for ROT_NONE
     int B, Hq, Hkv, N, D;
     int dtype;
     int shape;           // ATTN_SHAPE_*
 };
 
-// Causal attention forward; rotates Q/K tiles in the kernel when `rope`.
-hipError_t launch_attn_fwd(const AttnArgs& a, bool rope, hipStream_t stream);
+// Rotation applied inside the attention kernel: none (inputs already
+// rotated), Q and K (the fused path), or Q only (K rotated beforehand).
+enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2 };
+
+// Causal attention forward; `rot` is a ROT_* mode.
+hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream);
 
 // q_rot = RoPE(q), k_rot = RoPE(k).
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,

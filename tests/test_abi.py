@@ -54,6 +54,21 @@ def prerot(**kw):
                                     a["N"], a["D"], a["base"], a["dtype"], None)
 
 
+def qonly(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().attn_rope_q_causal_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                            a["Hq"], a["Hkv"], a["N"], a["D"], a["base"],
+                                            a["dtype"], None)
+
+
+def prerot_k(**kw):
+    a = dict(k=K, kr=L, B=1, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().rope_prerotate_k(a["k"], a["kr"], a["B"], a["Hkv"], a["N"], a["D"],
+                                      a["base"], a["dtype"], None)
+
+
 BAD = [
     (dict(dtype=2), rac.RAC_ERR_ARG),
     (dict(D=96), rac.RAC_ERR_UNSUPPORTED),
@@ -81,6 +96,7 @@ def test_attention_rejects_bad_arguments(kw, code):
     assert plain(**kw) == code
     assert rac.last_error() != ""
     assert fused(**kw) == code
+    assert qonly(**kw) == code
 
 
 @pytest.mark.parametrize("base", [0.0, -1.0, float("inf"), float("nan")])
@@ -88,6 +104,8 @@ def test_rope_base_must_be_positive_and_finite(base):
     assert fused(base=base) == rac.RAC_ERR_ARG
     assert prerot(base=base) == rac.RAC_ERR_ARG
     assert "rope_base" in rac.last_error()
+    assert qonly(base=base) == rac.RAC_ERR_ARG
+    assert prerot_k(base=base) == rac.RAC_ERR_ARG
 
 
 def test_prerotate_overlap_rules():
@@ -101,11 +119,26 @@ def test_prerotate_overlap_rules():
     assert prerot(B=65535, Hq=8, Hkv=8) == rac.RAC_ERR_ARG
 
 
+def test_prerotate_k_argument_rules():
+    assert prerot_k(kr=None) == rac.RAC_ERR_ARG
+    assert prerot_k(k=None) == rac.RAC_ERR_ARG
+    assert prerot_k(kr=ctypes.c_void_p(2 * P + 16)) == rac.RAC_ERR_ARG  # partial in-place
+    assert prerot_k(k=ctypes.c_void_p(2 * P + 8)) == rac.RAC_ERR_ALIGN
+    assert prerot_k(D=96) == rac.RAC_ERR_UNSUPPORTED
+    assert prerot_k(dtype=3) == rac.RAC_ERR_ARG
+    assert prerot_k(Hkv=0) == rac.RAC_ERR_ARG
+    assert prerot_k(N=-1) == rac.RAC_ERR_ARG
+    assert prerot_k(B=65535, Hkv=9) == rac.RAC_ERR_ARG  # more key slabs than the grid holds
+    assert prerot_k(B=0) == rac.RAC_OK
+    assert prerot_k(N=0, k=None, kr=None) == rac.RAC_OK
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, q=None, k=None, v=None,
                                                            out=None, lse=None)])
 def test_empty_problem_is_a_noop(kw):
     assert plain(**kw) == rac.RAC_OK
     assert fused(**kw) == rac.RAC_OK
+    assert qonly(**kw) == rac.RAC_OK
     pk = {key: val for key, val in kw.items() if key in ("B", "N")}
     assert prerot(**pk) == rac.RAC_OK
     assert rac.last_error() == ""
@@ -133,3 +166,51 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="HIP device"):
         rac.attn_causal_fwd(x, x, x)
+
+
+def auto(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0,
+             ws=ctypes.c_void_p(P * 16), wbytes=1 << 20)
+    a.update(kw)
+    return rac.lib().attn_rope_causal_auto(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                           a["Hq"], a["Hkv"], a["N"], a["D"], a["base"],
+                                           a["dtype"], a["ws"], a["wbytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_dispatcher_rejects_bad_arguments(kw, code):
+    assert auto(**kw) == code
+
+
+def test_dispatcher_workspace_rules():
+    # workspace overlapping an input or output is rejected before any launch
+    assert auto(ws=ctypes.c_void_p(P * 1 + 4096)) == rac.RAC_ERR_ARG
+    assert "workspace" in rac.last_error()
+    assert auto(ws=ctypes.c_void_p(P * 16 + 8)) == rac.RAC_ERR_ALIGN
+    assert auto(base=-1.0) == rac.RAC_ERR_ARG
+    assert auto(B=0) == rac.RAC_OK
+
+
+def test_auto_plan_paths():
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    for N in (1, 512, 2048):
+        path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 40)
+        assert path == rac.RAC_PATH_PREROTATE
+        q = B * Hq * N * D * 2
+        assert need == ((q + 255) // 256) * 256 + B * Hkv * N * D * 2
+        # too small for Q' and K': K' alone (split), then nothing (fused)
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_SPLIT
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, B * Hkv * N * D * 2 - 1)[0] == rac.RAC_PATH_FUSED
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
+    for N in (4096, 8192):
+        path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 40)
+        assert path == rac.RAC_PATH_SPLIT and need == B * Hkv * N * D * 2
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_FUSED
+    # MHA: pre-rotation up to 6144, the split path from 8192
+    assert rac.auto_plan(1, 16, 16, 6144, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_PREROTATE
+    assert rac.auto_plan(1, 16, 16, 8192, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_SPLIT
+    assert rac.auto_plan(0, 16, 16, 8192, 64, 1, 0) == (rac.RAC_PATH_FUSED, 0)
+    with pytest.raises(NotImplementedError):
+        rac.auto_plan(1, 4, 4, 64, 96, 0, 0)
+    with pytest.raises(ValueError):
+        rac.auto_plan(1, 4, 3, 64, 64, 0, 0)

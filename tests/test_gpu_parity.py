@@ -116,6 +116,19 @@ def test_prerotate_in_place():
     assert torch.equal(q2, qr) and torch.equal(k2, kr)
 
 
+@pytest.mark.parametrize("shape", SMALL, ids=_id)
+def test_prerotate_k_matches_prerotate(shape):
+    """The K-only pass writes exactly the k_rot of the full pass (in place too)."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    _, (qd, kd, _) = _inputs(B, Hq, Hkv, N, D, dt, key=(111, N, D))
+    _, kr = rac.rope_prerotate(qd, kd, base)
+    kr2 = rac.rope_prerotate_k(kd, base)
+    k3 = kd.clone()
+    rac.rope_prerotate_k(k3, base, k_rot=k3)
+    torch.cuda.synchronize()
+    assert torch.equal(kr2, kr) and torch.equal(k3, kr)
+
+
 def test_prerotate_long_positions_sampled():
     # positions up to 32767: the fp64-formed table angles keep the fp32 rotation accurate
     B, H, N, D, dt, base = 1, 2, 32768, 64, "fp16", 10000.0
@@ -149,14 +162,16 @@ def test_attn_causal_on_rotated_inputs(shape, launch_shape):
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=_id)
-@pytest.mark.parametrize("path", ["fused", "prerotate"])
+@pytest.mark.parametrize("path", ["fused", "prerotate", "split"])
 def test_path_matches_oracle(shape, path, launch_shape):
     B, Hq, Hkv, N, D, dt, base = shape
     (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(105, N, D))
     if path == "fused":
         o, l = rac.attn_rope_causal_fwd(qd, kd, vd, base)
-    else:
+    elif path == "prerotate":
         o, l = rac.prerotate_path(qd, kd, vd, base)
+    else:
+        o, l = rac.split_path(qd, kd, vd, base)
     torch.cuda.synchronize()
     qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
     ro, rl, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="rounded")
@@ -175,11 +190,43 @@ def test_fused_and_prerotate_paths_agree(shape, launch_shape):
     _, (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(106, N, D))
     of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
     op, lp = rac.prerotate_path(qd, kd, vd, base)
+    osp, lsp = rac.split_path(qd, kd, vd, base)
     torch.cuda.synchronize()
     assert_o(to_f64(of), to_f64(op), "fused vs prerotate")
     assert_lse(to_f64(lf), to_f64(lp), "fused vs prerotate")
-    # both paths hand identical rotated operands to the same attention arithmetic
+    # all paths hand identical rotated operands to the same attention arithmetic
     assert torch.equal(of, op) and torch.equal(lf, lp)
+    assert torch.equal(of, osp) and torch.equal(lf, lsp)
+
+
+@pytest.mark.parametrize("shape", SMALL + [(1, 8, 2, 4096, 128, "bf16", 500000.0),
+                                          (1, 4, 4, 8192, 64, "fp16", 10000.0)], ids=_id)
+def test_dispatcher_matches_fused(shape):
+    """attn_rope_causal_auto gives the fused kernel's result bit for bit, whichever path the
+    workspace allows: the preferred one, the split path (K' only), or none (fused)."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(112, N, D))
+    of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    pref, need = rac.auto_plan(B, Hq, Hkv, N, D, qd.dtype, 1 << 40)
+    kbytes = B * Hkv * N * D * 2
+    seen = set()
+    for wbytes in (None, kbytes, need):
+        ws = None if wbytes is None else torch.empty(wbytes, dtype=torch.uint8, device=DEV)
+        path = rac.auto_plan(B, Hq, Hkv, N, D, qd.dtype, 0 if ws is None else wbytes)[0]
+        seen.add(path)
+        ws_before = None if ws is None else ws.clone()
+        oa, la = rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, of) and torch.equal(la, lf), rac.PATH_NAMES[path]
+        if path == rac.RAC_PATH_FUSED and ws is not None:
+            assert torch.equal(ws, ws_before)  # the fused path leaves the workspace alone
+    assert pref in seen and rac.RAC_PATH_FUSED in seen
+    if N > 1024:
+        return  # the fused kernel at these sizes is checked against the oracle elsewhere
+    ro, rl, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt,
+                                         base, variant="rounded")
+    assert_o(to_f64(of), ro, "auto")
+    assert_lse(to_f64(lf), rl, "auto")
 
 
 ODD_N = [1, 2, 3, 17, 63, 64, 65, 127, 129, 300]
@@ -194,14 +241,16 @@ def test_ragged_lengths_and_gqa(N, D, dt, ratio, launch_shape):
     base = 10000.0
     (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(107, N, D, ratio))
     o, l = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    os_, ls_ = rac.split_path(qd, kd, vd, base)
     torch.cuda.synchronize()
     ro, rl, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt, base)
     assert_o(to_f64(o), ro, "fused N=%d" % N)
     assert_lse(to_f64(l), rl, "fused N=%d" % N)
+    assert torch.equal(o, os_) and torch.equal(l, ls_)
 
 
 @pytest.mark.parametrize("sigma", [4.0, 8.0])
-@pytest.mark.parametrize("path", ["fused", "prerotate"])
+@pytest.mark.parametrize("path", ["fused", "prerotate", "split"])
 def test_large_sigma_inputs(sigma, path, launch_shape):
     B, Hq, Hkv, N, D, dt, base = 1, 4, 2, 384, 128, "bf16", 500000.0
     # q and k ~ N(0, sigma^2) make scores of size ~ sigma^2 and force many
@@ -209,7 +258,8 @@ def test_large_sigma_inputs(sigma, path, launch_shape):
     q = inputs.draw((B, Hq, N, D), dt, (108,), 0, sigma)
     k = inputs.draw((B, Hkv, N, D), dt, (108,), 1, sigma)
     v = inputs.draw((B, Hkv, N, D), dt, (108,), 2)
-    fn = rac.attn_rope_causal_fwd if path == "fused" else rac.prerotate_path
+    fn = {"fused": rac.attn_rope_causal_fwd, "prerotate": rac.prerotate_path,
+          "split": rac.split_path}[path]
     o, l = fn(q.to(DEV), k.to(DEV), v.to(DEV), base)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
@@ -253,7 +303,10 @@ def test_empty_inputs():
         o, l = rac.attn_rope_causal_fwd(x, x, x, 10000.0)
         o2, l2 = rac.attn_causal_fwd(x, x, x)
         qr, kr = rac.rope_prerotate(x, x, 10000.0)
+        kr2 = rac.rope_prerotate_k(x, 10000.0)
+        o3, l3 = rac.attn_rope_q_causal_fwd(x, x, x, 10000.0)
         assert o.shape == shape and l.shape == shape[:3] and qr.shape == shape
+        assert kr2.shape == shape and o3.shape == shape
 
 
 # ---------------------------------------------------------------------------
@@ -273,8 +326,10 @@ def test_full_size_sampled_rows(name):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
     op, lp = rac.prerotate_path(qd, kd, vd, base)
+    osp, lsp = rac.split_path(qd, kd, vd, base)
     torch.cuda.synchronize()
     assert torch.equal(of, op) and torch.equal(lf, lp)
+    assert torch.equal(of, osp) and torch.equal(lf, lsp)
     rng = np.random.default_rng(len(name))
     rows = sampled_rows(B, Hq, N, rng)
     qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)

@@ -50,6 +50,7 @@ def rotation_mode(kernel_name):
     return int(args[2])
 
 HBM_PEAK_GBS = 8000.0
+WARM_SECONDS = 0.2  # minimum warm-up before any timed region
 MAIN = "llama3_8b_gqa_n2048"
 METRIC = "causal RoPE-attn fwd TFLOP/s (fused & pre-rotate) + % of MFMA peak; N*"
 
@@ -107,6 +108,18 @@ def ingest_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def warm(fn, calls, min_seconds, sync):
+    """Runs fn at least `calls` times and for at least `min_seconds` (GPU clocks
+    settle only after tens of milliseconds of work), then synchronizes."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < calls or time.perf_counter() - t0 < min_seconds:
+        for _ in range(max(1, min(calls, 10))):
+            fn()
+        done += max(1, min(calls, 10))
+        sync()
 
 
 def attn_flops(w):
@@ -201,9 +214,7 @@ def main():
         fn = {"fused": fused, "rope": rope, "attn": attn,
               "prerotate": lambda: (rope(), attn()), "rope_k": rope_k, "attn_q": attn_q,
               "split": lambda: (rope_k(), attn_q())}[args.only]
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm(fn, args.warmup, WARM_SECONDS, torch.cuda.synchronize)
         t0 = time.perf_counter()
         for _ in range(args.steps):
             fn()
@@ -213,9 +224,8 @@ def main():
         return
 
     # ---- the timed region: K steps of the whole hot path ----
-    for _ in range(args.warmup):
-        fused(); rope(); attn()
-    torch.cuda.synchronize()
+    # warm-up: W steps, and at least WARM_SECONDS of them
+    warm(lambda: (fused(), rope(), attn()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
     fused_ev = [(ev(), ev()) for _ in range(args.steps)]
     rope_ev = [(ev(), ev()) for _ in range(args.steps)]
     attn_ev = [(ev(), ev()) for _ in range(args.steps)]
@@ -257,9 +267,7 @@ def main():
     pb = prerot_bytes(w)
 
     # ---- the GQA split path, timed the same way after the timed region ----
-    for _ in range(args.warmup):
-        rope_k(); attn_q()
-    torch.cuda.synchronize()
+    warm(lambda: (rope_k(), attn_q()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
     rk_ev = [(ev(), ev()) for _ in range(args.steps)]
     aq_ev = [(ev(), ev()) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -312,11 +320,18 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def crossover(torch, rac, inputs, dev, ev, reps=10):
-    """Fused vs pre-rotation path time per shape; N* where their order flips."""
+def crossover(torch, rac, inputs, dev, ev, reps=15):
+    """Fused vs pre-rotation path time per shape; N* where their order flips.
+
+    Each path is warmed up for 50 ms, then timed as the median of `reps`
+    back-to-back calls, each bracketed by HIP events on the launch stream.
+    Also per shape: the GQA split path, the dispatcher (with a workspace for
+    its preferred path), and rope_prerotate bandwidth warm and cold (after a
+    512 MiB cache flush, larger than the 256 MB MALL)."""
     rows = []
     names = ["mha_d64_fp16_n%d" % n for n in inputs.SWEEP_NS] + [
         "llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192"]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for name in names:
         w = inputs.WORKLOADS[name]
         q, k, v = inputs.workload_qkv(name)
@@ -327,33 +342,53 @@ def crossover(torch, rac, inputs, dev, ev, reps=10):
         lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
         qr, kr = torch.empty_like(qd), torch.empty_like(kd)
         krs = torch.empty_like(kd)
+        path, need = rac.auto_plan(w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], qd.dtype, 1 << 62)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
         fns = {
             "fused": lambda: rac.attn_rope_causal_fwd(qd, kd, vd, base, out=o, lse=lse),
             "prerotate": lambda: (rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
                                   rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse)),
             "attn": lambda: rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse),
+            "rope": lambda: rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
             "split": lambda: (rac.rope_prerotate_k(kd, base, k_rot=krs),
                               rac.attn_rope_q_causal_fwd(qd, krs, vd, base, out=o, lse=lse)),
+            "auto": lambda: rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws, out=o,
+                                                      lse=lse),
         }
         t = {}
         for key, fn in fns.items():
-            for _ in range(3):
-                fn()
-            a, b = ev(), ev()
-            a.record()
-            for _ in range(reps):
-                fn()
-            b.record()
+            warm(fn, 3, 0.05, torch.cuda.synchronize)
+            pairs = [(ev(), ev()) for _ in range(reps)]
+            for a, b in pairs:
+                a.record(); fn(); b.record()
             torch.cuda.synchronize()
-            t[key] = a.elapsed_time(b) / reps
+            ts = sorted(a.elapsed_time(b) for a, b in pairs)
+            t[key] = ts[len(ts) // 2]
+        cold = []
+        for _ in range(reps):
+            flush.zero_()
+            a, b = ev(), ev()
+            a.record(); fns["rope"](); b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        cold.sort()
+        t_rope_cold = cold[len(cold) // 2]
         fl = attn_flops(w)
+        pb = prerot_bytes(w)
+        fastest = min(("fused", "prerotate", "split"), key=lambda p: t[p])
         rows.append({"workload": name, "N": w["N"], "fused_ms": t["fused"],
                      "prerotate_ms": t["prerotate"], "attn_only_ms": t["attn"],
-                     "split_ms": t["split"],
+                     "split_ms": t["split"], "auto_ms": t["auto"],
+                     "auto_path": rac.PATH_NAMES[path], "fastest_path": fastest,
                      "fused_tflops": fl / t["fused"] / 1e9,
                      "prerotate_tflops": fl / t["prerotate"] / 1e9,
-                     "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0})
-        del qd, kd, vd, o, lse, qr, kr, krs
+                     "attn_only_tflops": fl / t["attn"] / 1e9,
+                     "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0,
+                     "rope_prerotate_ms": t["rope"], "rope_prerotate_gbs": pb / t["rope"] / 1e6,
+                     "rope_prerotate_cold_ms": t_rope_cold,
+                     "rope_prerotate_cold_gbs": pb / t_rope_cold / 1e6,
+                     "rope_prerotate_cold_hbm_frac": pb / t_rope_cold / 1e6 / HBM_PEAK_GBS})
+        del qd, kd, vd, o, lse, qr, kr, krs, ws
         torch.cuda.empty_cache()
     sweep = [r for r in rows if r["workload"].startswith("mha_d64")]
     n_star = None

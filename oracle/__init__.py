@@ -18,6 +18,9 @@ What it follows (the pages define the method, this file restates it):
   softmax" and the forward method (Algorithm 1: o_i = u_i / l_i and L_i),
   with scale 1/sqrt(D); MHA/GQA per "AttnFuse Makes RoPE a First-Class
   Attention Compilation Operation", paragraph 4.
+* Backward -- the gradients of that attention with respect to q, k, v by the
+  chain rule through the same definition (softmax Jacobian with
+  Delta_i = sum_j P_ij dP_ij), and RoPE's gradient, the inverse rotation.
 * Two variants of the rotated operands: ``exact`` (fp64 rotation) and
   ``rounded`` (fp64 rotation then one round-to-nearest-even to the storage
   dtype, i.e. what a separate pre-rotation pass writes to memory).
@@ -56,6 +59,8 @@ class Oracle:
         lib.oracle_attn_rows.argtypes = [f64p, f64p, f64p] + [ctypes.c_int] * 5 + [
             i64p, ctypes.c_int64, f64p, f64p]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [f64p] * 4 + [ctypes.c_int] * 5 + [f64p] * 5
+        lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -155,6 +160,56 @@ class Oracle:
         return o, lse, qr, kr
 
 
+    def attention_bwd(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray):
+        """Gradients of the causal attention above, fp64, from the definition.
+
+        q, dout [B, Hq, N, D]; k, v [B, Hkv, N, D]. Returns (dq, dk, dv, lse,
+        delta): the gradients with respect to q, k and v (dk, dv summed over
+        the query heads of each GQA group), and per query row L_i and
+        Delta_i = sum_j P_ij dP_ij.
+        """
+        q, k, v, dout = (np.ascontiguousarray(t, dtype=np.float64) for t in (q, k, v, dout))
+        B, Hq, N, D = q.shape
+        Hkv = k.shape[1]
+        if k.shape != (B, Hkv, N, D) or v.shape != k.shape or dout.shape != q.shape:
+            raise ValueError("k, v must be [B, Hkv, N, D] and dout like q")
+        dq = np.empty_like(q)
+        dk = np.empty_like(k)
+        dv = np.empty_like(v)
+        lse = np.empty(q.shape[:-1], dtype=np.float64)
+        delta = np.empty(q.shape[:-1], dtype=np.float64)
+        p = lambda a: _ptr(a, ctypes.c_double)  # noqa: E731
+        rc = self.lib.oracle_attn_bwd(p(q), p(k), p(v), p(dout), B, Hq, Hkv, N, D, p(dq), p(dk),
+                                      p(dv), p(lse), p(delta))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd: bad arguments")
+        return dq, dk, dv, lse, delta
+
+    def rope_attention_bwd(self, q_bits, k_bits, v_bits, do_bits, dtype: str, base: float,
+                           variant: str = "rounded"):
+        """Gradients of RoPE then causal attention with respect to the
+        unrotated q, k and to v, from bf16/fp16 bit patterns.
+
+        The attention gradients are taken at the rotated operands (``variant``
+        as in rope_attention); RoPE's gradient is its inverse rotation, the
+        turn by -p theta_i. Returns (dq, dk, dv, delta, lse).
+        """
+        q = self.decode(q_bits, dtype)
+        k = self.decode(k_bits, dtype)
+        v = self.decode(v_bits, dtype)
+        do = self.decode(do_bits, dtype)
+        qr = self.rope_bhnd(q, base)
+        kr = self.rope_bhnd(k, base)
+        if variant == "rounded":
+            qr = self.decode(self.encode(qr, dtype), dtype)
+            kr = self.decode(self.encode(kr, dtype), dtype)
+        elif variant != "exact":
+            raise ValueError("variant must be 'exact' or 'rounded'")
+        dqr, dkr, dv, lse, delta = self.attention_bwd(qr, kr, v, do)
+        neg = -np.arange(q.shape[-2], dtype=np.int64)
+        return self.rope(dqr, neg, base), self.rope(dkr, neg, base), dv, delta, lse
+
+
 def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
@@ -199,3 +254,11 @@ def attention(q, k, v, rows=None):
 
 def rope_attention(q_bits, k_bits, v_bits, dtype, base, rows=None, variant="rounded"):
     return default().rope_attention(q_bits, k_bits, v_bits, dtype, base, rows, variant)
+
+
+def attention_bwd(q, k, v, dout):
+    return default().attention_bwd(q, k, v, dout)
+
+
+def rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant="rounded"):
+    return default().rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant)

@@ -36,6 +36,18 @@
  *   fp64 values are rounded to bf16/fp16 once, round-to-nearest-even, by this
  *   file's own code (the "rounded rotation" variant of the oracle).
  *
+ *   Backward. The gradients of that attention with respect to q, k and v,
+ *   given the gradient dO of the output, by the chain rule through the same
+ *   definition: P_ij = exp(s_ij - L_i), dv_j = sum_i P_ij dO_i,
+ *   dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - Delta_i) with
+ *   Delta_i = sum_j P_ij dP_ij (the softmax Jacobian), dq_i = tau sum_j dS_ij
+ *   k_j and dk_j = tau sum_i dS_ij q_i; dk and dv of a key/value head sum
+ *   over the query heads that read it. RoPE's gradient is the inverse
+ *   rotation (turn by -p theta_i), i.e. oracle_rope at negated positions. The
+ *   digest's method section describes its own backward as a two-pass
+ *   recomputation from the stored L_i; this oracle recomputes everything from
+ *   the definition and stores nothing between rows.
+ *
  * Every routine is plain fp64 C; OpenMP only splits independent rows.
  */
 #include <math.h>
@@ -198,6 +210,131 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
         free(s);
     }
     return bad ? -1 : 0;
+}
+
+/* ---- causal attention, backward ------------------------------------------ */
+
+/* The scores of query row `row` (flattened (b*Hq + h)*N + i) against the
+ * visible keys j = 0..i of its key head, s[j] = tau q_i . k_j; returns i. */
+static int64_t row_scores(const double* q, const double* k, int Hq, int Hkv, int N, int D,
+                          int64_t row, double tau, double* s) {
+    const int group = Hq / Hkv;
+    int64_t i = row % N;
+    int64_t bh = row / N;
+    int64_t h = bh % Hq, b = bh / Hq;
+    const int64_t kv_head = b * Hkv + h / group;
+    const double* qi = q + row * D;
+    const double* kb = k + kv_head * (int64_t)N * D;
+    for (int64_t j = 0; j <= i; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qi[d] * kb[j * D + d];
+        s[j] = tau * dot;
+    }
+    return i;
+}
+
+/* q [B,Hq,N,D], k, v [B,Hkv,N,D], dout [B,Hq,N,D], all fp64 and contiguous.
+ * Writes dq [B,Hq,N,D], dk and dv [B,Hkv,N,D], and per query row its
+ * log-sum-exp lse and Delta [B,Hq,N]. Three passes, each recomputing the
+ * scores: (1) per query row, L_i and Delta_i; (2) per query row, dq_i;
+ * (3) per key row j of each key head, dk_j and dv_j over the query rows
+ * i >= j of every query head of its group. Returns 0, or -1 on bad
+ * arguments. */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    int B, int Hq, int Hkv, int N, int D,
+                    double* dq, double* dk, double* dv, double* lse, double* delta) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv != 0) return -1;
+    const int64_t qrows = (int64_t)B * Hq * N;
+    const int64_t krows = (int64_t)B * Hkv * N;
+    const int group = Hq / Hkv;
+    const double tau = pow((double)D, -0.5);
+    int bad = 0;
+    /* pass 1: L_i and Delta_i */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t row = 0; row < qrows; ++row) {
+            if (!s) { bad = 1; continue; }
+            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, s);
+            int64_t bh = row / N;
+            int64_t g = (bh % Hq) / group, b = bh / Hq;
+            const double* vb = v + (b * Hkv + g) * (int64_t)N * D;
+            const double* doi = dout + row * D;
+            double M = -INFINITY;
+            for (int64_t j = 0; j <= i; ++j)
+                if (s[j] > M) M = s[j];
+            double l = 0.0;
+            for (int64_t j = 0; j <= i; ++j) l += exp(s[j] - M);
+            double L = M + log(l);
+            double dl = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dp = 0.0;
+                for (int d = 0; d < D; ++d) dp += doi[d] * vb[j * D + d];
+                dl += exp(s[j] - L) * dp;
+            }
+            lse[row] = L;
+            delta[row] = dl;
+        }
+        free(s);
+    }
+    if (bad) return -1;
+    /* pass 2: dq_i = tau sum_j P_ij (dP_ij - Delta_i) k_j */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t row = 0; row < qrows; ++row) {
+            if (!s) { bad = 1; continue; }
+            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, s);
+            int64_t bh = row / N;
+            int64_t g = (bh % Hq) / group, b = bh / Hq;
+            const double* kb = k + (b * Hkv + g) * (int64_t)N * D;
+            const double* vb = v + (b * Hkv + g) * (int64_t)N * D;
+            const double* doi = dout + row * D;
+            double* dqi = dq + row * D;
+            for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dp = 0.0;
+                for (int d = 0; d < D; ++d) dp += doi[d] * vb[j * D + d];
+                double ds = exp(s[j] - lse[row]) * (dp - delta[row]);
+                for (int d = 0; d < D; ++d) dqi[d] += tau * ds * kb[j * D + d];
+            }
+        }
+        free(s);
+    }
+    if (bad) return -1;
+    /* pass 3: dk_j = tau sum_{h, i >= j} dS_ij q_i, dv_j = sum_{h, i >= j} P_ij dO_i */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t krow = 0; krow < krows; ++krow) {
+        int64_t j = krow % N;
+        int64_t bg = krow / N;
+        int64_t g = bg % Hkv, b = bg / Hkv;
+        const double* kj = k + krow * D;
+        const double* vj = v + krow * D;
+        double* dkj = dk + krow * D;
+        double* dvj = dv + krow * D;
+        for (int d = 0; d < D; ++d) dkj[d] = dvj[d] = 0.0;
+        for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+            for (int64_t i = j; i < N; ++i) {
+                int64_t row = (b * Hq + h) * (int64_t)N + i;
+                const double* qi = q + row * D;
+                const double* doi = dout + row * D;
+                double dot = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    dot += qi[d] * kj[d];
+                    dp += doi[d] * vj[d];
+                }
+                double p = exp(tau * dot - lse[row]);
+                double ds = p * (dp - delta[row]);
+                for (int d = 0; d < D; ++d) {
+                    dkj[d] += tau * ds * qi[d];
+                    dvj[d] += p * doi[d];
+                }
+            }
+        }
+    }
+    return 0;
 }
 
 int oracle_num_threads(void) {

@@ -375,4 +375,110 @@ def pin_rope_attention_variants(orc):
     assert np.array_equal(qe[:, :, 0], qr[:, :, 0])
 
 
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def pin_attention_bwd_torch_autograd(orc):
+    # library special case: torch's fp64 autograd through scaled_dot_product_attention
+    rng = _rng(19)
+    for (B, Hq, Hkv, N, D) in ((1, 2, 2, 7, 8), (2, 4, 2, 33, 16), (1, 8, 1, 20, 64)):
+        q, k, v = _qkv(rng, B, Hq, Hkv, N, D)
+        do = rng.standard_normal(q.shape)
+        dq, dk, dv, lse, delta = orc.attention_bwd(q, k, v, do)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        rep = Hq // Hkv
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(rep, 1), vt.repeat_interleave(rep, 1), is_causal=True)
+        o.backward(torch.from_numpy(do))
+        for got, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+            ref = ref.numpy()
+            assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+        # Delta_i = sum_j P_ij dP_ij equals dO_i . o_i
+        assert np.max(np.abs(delta - np.sum(do * o.detach().numpy(), axis=-1))) < 1e-12
+        _, lse_f = orc.attention(q, k, v)
+        assert np.max(np.abs(lse - lse_f)) < 1e-13
+
+
+def pin_attention_bwd_finite_differences(orc):
+    # central differences of L = sum(dO * o) through the oracle's forward
+    rng = _rng(20)
+    B, Hq, Hkv, N, D = 1, 4, 2, 9, 6
+    q, k, v = _qkv(rng, B, Hq, Hkv, N, D)
+    do = rng.standard_normal(q.shape)
+    dq, dk, dv, _, _ = orc.attention_bwd(q, k, v, do)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * orc.attention(q_, k_, v_)[0]))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [tuple(rng.integers(0, s) for s in x.shape) for _ in range(12)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def pin_attention_bwd_special_cases(orc):
+    rng = _rng(21)
+    B, Hq, Hkv, N, D = 1, 4, 2, 24, 16
+    q, k, v = _qkv(rng, B, Hq, Hkv, N, D)
+    do = rng.standard_normal(q.shape)
+    # every key equal: the scores of a row are all equal, softmax is flat in
+    # them, so the query gradient vanishes
+    kc = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    dq, _, _, _, _ = orc.attention_bwd(q, kc, v, do)
+    assert np.max(np.abs(dq)) < 1e-12
+    # probabilities of a row sum to one: the value gradients of a key head sum
+    # to the output gradients of its query heads
+    _, dk, dv, _, _ = orc.attention_bwd(q, k, v, do)
+    ref = do.reshape(B, Hkv, Hq // Hkv, N, D).sum(axis=(2, 3))
+    assert np.max(np.abs(dv.sum(axis=2) - ref)) < 1e-11
+    # dS rows sum to zero, so sum_j dk_j = tau sum_i (sum_j dS_ij) q_i = 0
+    assert np.max(np.abs(dk.sum(axis=2))) < 1e-11
+    # row 0 sees only key 0: its P is 1 and dS is 0, so dO_0 reaches only v_0
+    do0 = np.zeros_like(do)
+    do0[:, :, 0] = do[:, :, 0]
+    dq0, dk0, dv0, _, _ = orc.attention_bwd(q, k, v, do0)
+    assert np.max(np.abs(dq0)) == 0.0 and np.max(np.abs(dk0)) == 0.0
+    assert np.max(np.abs(dv0[:, :, 1:])) == 0.0
+
+
+def pin_rope_attention_bwd_finite_differences(orc):
+    # gradients with respect to the unrotated q and k (the inverse rotation),
+    # against central differences of the RoPE-then-attention forward
+    rng = _rng(22)
+    B, Hq, Hkv, N, D, base = 1, 2, 1, 12, 8, 10000.0
+
+    def bf16_bits(shape):
+        x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+        return x.view(torch.int16).numpy().view(np.uint16)
+
+    qb, kb, vb, dob = (bf16_bits(s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                              (B, Hq, N, D)))
+    q, k, v, do = (orc.decode(b, "bf16") for b in (qb, kb, vb, dob))
+    dq, dk, dv, delta, lse = orc.rope_attention_bwd(qb, kb, vb, dob, "bf16", base,
+                                                    variant="exact")
+    pos = np.arange(N)
+
+    def loss(q_, k_, v_):
+        o, _ = orc.attention(orc.rope(q_, pos, base), orc.rope(k_, pos, base), v_)
+        return float(np.sum(do * o))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [tuple(rng.integers(0, s) for s in x.shape) for _ in range(12)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

@@ -36,6 +36,16 @@ MUTANTS = {
     "round_half_up": ("double n = nearbyint(r);", "double n = floor(r + 0.5);"),
     "fp16_exponent_bias": ("(uint16_t)(((e - 1 + 15) << 10) | m)", "(uint16_t)(((e + 15) << 10) | m)"),
     "bf16_decode_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "bwd_delta_sign": ("double ds = exp(s[j] - lse[row]) * (dp - delta[row]);",
+                       "double ds = exp(s[j] - lse[row]) * (dp + delta[row]);"),
+    "bwd_dq_no_scale": ("dqi[d] += tau * ds * kb[j * D + d];", "dqi[d] += ds * kb[j * D + d];"),
+    "bwd_dk_uses_dout": ("dkj[d] += tau * ds * qi[d];", "dkj[d] += tau * ds * doi[d];"),
+    "bwd_dv_uses_ds": ("dvj[d] += p * doi[d];", "dvj[d] += ds * doi[d];"),
+    "bwd_key_pass_strict": ("for (int64_t i = j; i < N; ++i) {", "for (int64_t i = j + 1; i < N; ++i) {"),
+    "bwd_delta_drops_p": ("dl += exp(s[j] - L) * dp;", "dl += dp;"),
+    "bwd_scale_one_over_d": ("pow((double)D, -0.5)", "pow((double)D, -1.0)"),
+    "bwd_gqa_modulo": ("const int64_t kv_head = b * Hkv + h / group;",
+                       "const int64_t kv_head = b * Hkv + h % Hkv;"),
 }
 
 

@@ -1,7 +1,8 @@
 /*
  * rac.h -- RoPE + causal attention forward on AMD MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels. Five operations and a dispatcher:
+ * A C ABI over hand-written HIP kernels. Five forward operations, a
+ * dispatcher, and the backward of both paths:
  *
  *   attn_rope_causal_fwd  one kernel: rotary position embedding applied to the
  *                         query and key tiles inside a causal attention
@@ -16,6 +17,8 @@
  *                         the "GQA split" path, which moves only the Hkv key
  *                         heads through the streaming pass instead of all
  *                         Hq + Hkv heads and rotates no key tile in the kernel.
+ *   attn_rope_causal_bwd, attn_causal_bwd, rope_prerotate_bwd
+ *                         the gradients of the fused and pre-rotation paths.
  *   attn_rope_causal_auto the same result as attn_rope_causal_fwd through
  *                         whichever of the three paths is fastest for the
  *                         shape on MI355X (the report's paragraph 5: the
@@ -179,6 +182,53 @@ int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out
  */
 int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t workspace_bytes,
                   int* path, size_t* preferred_bytes);
+
+/*
+ * Backward of attn_rope_causal_fwd: the gradients of the loss with respect to
+ * the UNROTATED q and k and to v, given dout = dLoss/dout. The chain rule
+ * through the forward's definition; the schedule is the two-pass backward of
+ * "Fast and Exact Relative-Position Attention via Structure-Aware Kernels"
+ * (rainbus digest), method section, Algorithm 2: a query-parallel pass
+ * computes dq, a key-parallel pass dk and dv, each element with one writer
+ * (no atomics; deterministic). RoPE's gradient, the inverse turn R(-p), is
+ * applied to dq and dk in fp32 inside the kernels. The training step of
+ * "AttnFuse Makes RoPE a First-Class Attention Compilation Operation",
+ * paragraph 3, needs this backward.
+ *
+ *   q, dout, out, dq: [B,Hq,N,D]; k, v, dk, dv: [B,Hkv,N,D]; all `dtype`.
+ *   out, lse: the forward's outputs for these inputs (lse fp32 [B,Hq,N],
+ *             natural log) -- the backward rebuilds the probabilities from
+ *             them rather than recomputing the row statistics.
+ *   delta:    fp32 [B,Hq,N], written: rowsum(dout * out), which the
+ *             key-parallel pass reads (caller-allocated, like the outputs).
+ *   dk, dv:   summed over the Hq/Hkv query heads of each group.
+ * Every pointer is a caller-owned device pointer, 16-byte aligned; lse is
+ * required. Outputs must not overlap inputs or each other. Two kernels are
+ * enqueued on `stream` (the dq pass first: it writes delta).
+ */
+int attn_rope_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* delta, int B, int Hq, int Hkv, int N, int D, double rope_base,
+                         int dtype, void* stream);
+
+/*
+ * Backward of attn_causal_fwd (q and k already rotated): the gradients with
+ * respect to the rotated q and k (and v). Same arguments and rules as
+ * attn_rope_causal_bwd without rope_base. With rope_prerotate_bwd it is the
+ * backward of the pre-rotation path.
+ */
+int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    float* delta, int B, int Hq, int Hkv, int N, int D, int dtype, void* stream);
+
+/*
+ * Backward of rope_prerotate: dq = R(-p) dq_rot, dk = R(-p) dk_rot, each pair
+ * turned back by its position (x0 = y0 cos + y1 sin, x1 = y1 cos - y0 sin in
+ * fp32, one rounding to `dtype`). Same shapes and aliasing rules as
+ * rope_prerotate (exact in-place use allowed).
+ */
+int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
+                       int Hkv, int N, int D, double rope_base, int dtype, void* stream);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 const char* rac_last_error(void);

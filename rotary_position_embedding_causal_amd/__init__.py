@@ -13,6 +13,9 @@ Operations (names as in the C ABI):
   rope_prerotate_k(k, rope_base)            -> k_rot          K only (GQA split path)
   attn_rope_q_causal_fwd(q, k_rot, v, rope_base) -> (out, lse) RoPE on Q in the kernel
   attn_rope_causal_auto(q, k, v, rope_base, workspace) -> (out, lse) fastest path
+  attn_rope_causal_bwd(q, k, v, out, lse, dout, rope_base) -> (dq, dk, dv, delta)
+  attn_causal_bwd(q, k, v, out, lse, dout) -> (dq, dk, dv, delta)  on rotated inputs
+  rope_prerotate_bwd(dq_rot, dk_rot, rope_base) -> (dq, dk)
   auto_plan(B, Hq, Hkv, N, D, dtype, workspace_bytes) -> (path, preferred_bytes)
 Tensors are contiguous [B, H, N, D] bf16/fp16 on one HIP device; lse is fp32
 [B, Hq, N] (natural log).
@@ -32,6 +35,7 @@ RAC_OK, RAC_ERR_ARG, RAC_ERR_ALIGN, RAC_ERR_UNSUPPORTED, RAC_ERR_HIP = 0, -1, -2
 RAC_MAX_N = 1 << 22
 EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_prerotate_k",
             "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
+            "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
             "rac_last_error", "rac_release_tables")
 RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
 PATH_NAMES = {RAC_PATH_FUSED: "fused", RAC_PATH_PREROTATE: "prerotate", RAC_PATH_SPLIT: "split"}
@@ -70,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.attn_rope_causal_auto.restype = i
     L.rac_auto_plan.argtypes = [i, i, i, i, i, i, sz, ctypes.POINTER(i), ctypes.POINTER(sz)]
     L.rac_auto_plan.restype = i
+    L.attn_rope_causal_bwd.argtypes = [vp] * 10 + [i] * 5 + [d, i, vp]
+    L.attn_rope_causal_bwd.restype = i
+    L.attn_causal_bwd.argtypes = [vp] * 10 + [i] * 6 + [vp]
+    L.attn_causal_bwd.restype = i
+    L.rope_prerotate_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp]
+    L.rope_prerotate_bwd.restype = i
     L.rac_last_error.argtypes = []
     L.rac_last_error.restype = ctypes.c_char_p
     L.rac_release_tables.argtypes = []
@@ -249,3 +259,65 @@ def attn_rope_causal_auto(q, k, v, rope_base: float, workspace=None, out=None, l
                                          _ptr(workspace), wbytes, _stream(q.device))
     check(rc, "attn_rope_causal_auto")
     return out, lse
+
+
+def _bwd_tensors(q, k, v, out, lse, dout):
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError("%s must be a contiguous tensor like q" % name)
+    if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be the forward's contiguous fp32 [B, Hq, N] log-sum-exp")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    return (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta)
+
+
+def attn_rope_causal_bwd(q, k, v, out, lse, dout, rope_base: float):
+    """Backward of attn_rope_causal_fwd: gradients with respect to the unrotated q, k and
+    to v, from the forward's (out, lse) and dout. Returns (dq, dk, dv, delta)."""
+    (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta) = _bwd_tensors(q, k, v, out, lse, dout)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                        B, Hq, Hkv, N, D, float(rope_base), dt, _stream(q.device))
+    check(rc, "attn_rope_causal_bwd")
+    return dq, dk, dv, delta
+
+
+def attn_causal_bwd(q, k, v, out, lse, dout):
+    """Backward of attn_causal_fwd (q, k already rotated). Returns (dq, dk, dv, delta)."""
+    (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta) = _bwd_tensors(q, k, v, out, lse, dout)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_causal_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                   B, Hq, Hkv, N, D, dt, _stream(q.device))
+    check(rc, "attn_causal_bwd")
+    return dq, dk, dv, delta
+
+
+def rope_prerotate_bwd(dq_rot, dk_rot, rope_base: float, dq=None, dk=None):
+    """Backward of rope_prerotate: (dq, dk) = R(-p) (dq_rot, dk_rot); dq=dq_rot for in place."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(dq_rot, dk_rot, None)
+    dq = torch.empty_like(dq_rot) if dq is None else dq
+    dk = torch.empty_like(dk_rot) if dk is None else dk
+    for src, dst in ((dq_rot, dq), (dk_rot, dk)):
+        if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous() \
+                or dst.device != src.device:
+            raise ValueError("dq/dk must be contiguous tensors like dq_rot/dk_rot")
+    with torch.cuda.device(dq_rot.device):
+        rc = lib().rope_prerotate_bwd(_ptr(dq_rot), _ptr(dk_rot), _ptr(dq), _ptr(dk), B, Hq, Hkv,
+                                      N, D, float(rope_base), dt, _stream(dq_rot.device))
+    check(rc, "rope_prerotate_bwd")
+    return dq, dk
+
+
+def prerotate_path_bwd(q, k, v, out, lse, dout, rope_base: float):
+    """Backward of the pre-rotation path: rope_prerotate (the rotated operands the forward
+    used), attn_causal_bwd on them, rope_prerotate_bwd. Returns (dq, dk, dv, delta)."""
+    q_rot, k_rot = rope_prerotate(q, k, rope_base)
+    dq_rot, dk_rot, dv, delta = attn_causal_bwd(q_rot, k_rot, v, out, lse, dout)
+    dq, dk = rope_prerotate_bwd(dq_rot, dk_rot, rope_base, dq=dq_rot, dk=dk_rot)
+    return dq, dk, dv, delta

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
 CSRC = os.path.join(_HERE, "csrc")
 LIB = os.path.join(_HERE, "librac.so")
-SOURCES = ["rac_api.hip", "attn_fwd.hip", "rope_prerotate.hip"]
+SOURCES = ["rac_api.hip", "attn_fwd.hip", "attn_bwd.hip", "rope_prerotate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -24,7 +24,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract
 
 # Extra flags per source. The attention kernels never see NaNs from finite
 # inputs (masking uses -inf), so fmax needs no NaN-quieting canonicalisation.
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_bwd.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, obj, verbose):

@@ -1,0 +1,527 @@
+// attn_bwd.hip -- causal MHA/GQA attention backward for gfx950, with RoPE
+// fused into the operand loads (RM = ROT_QK) or not (RM = ROT_NONE).
+//
+// Method: the chain rule through the forward's definition ("Fast and Exact
+// Relative-Position Attention via Structure-Aware Kernels", rainbus digest,
+// background "FlashAttention and online softmax"): with P_ij = exp(s_ij - L_i)
+// rebuilt from the forward's log-sum-exp L,
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),   Delta_i = dO_i . O_i,
+//     dQ = tau dS K,   dK = tau dS^T Q,
+// dK and dV of a key/value head summed over the query heads that read it.
+// The schedule is the digest's method section, backward (Algorithm 2): a
+// query-parallel pass rebuilds S, P, dS and accumulates dQ; a key-parallel
+// pass rebuilds them again and accumulates dK, dV. Every gradient element has
+// one writer -- no atomics, deterministic results.
+//
+// RoPE: the forward rotates q and k by their positions (the turn R(p)); its
+// gradient is the inverse turn R(-p) = R(p)^T. Fused, both passes rotate the
+// Q and K operands in the kernel exactly as the forward does (the same
+// rope_rotate8, so the same bf16/fp16 operands) and apply R(-p) to dQ and dK
+// in fp32 before the one rounding to the storage format. "AttnFuse Makes RoPE
+// a First-Class Attention Compilation Operation", paragraph 3, reports a
+// Llama-3-8B training step with RoPE fused; this is that step's attention
+// backward.
+//
+// gfx950 mapping (64-lane waves, v_mfma_f32_32x32x16 bf16/fp16), the same two
+// MFMA patterns as the forward:
+//   * "score" pattern, C[32 x 32] = A B: A = 32 rows of an LDS tile (16-byte
+//     chunk reads), B = the wave's 32 stationary rows held in registers
+//     (lane (n, hh) holds row n, chunks 16c + 8hh). The fp32 result has one
+//     stationary row per lane column.
+//   * "PV" pattern, C^T[D x 32] += X^T Y: A = X^T from an LDS tile through the
+//     transpose read (ds_read_b64_tr_b16), B = score-pattern results packed to
+//     the storage format, rows permuted inside each 16-row step the same way
+//     on both sides.
+//   dQ pass: stationary = 32 query rows (Q, dO); streamed = 64-key tiles of K
+//     and V. S^T = K Q^T and dP^T = V dO^T (score), dQ^T += K^T dS^T (PV).
+//   dK/dV pass: stationary = 32 key rows (K, V); streamed = 64-query tiles of
+//     Q and dO (with their L and Delta) of every query head of the group.
+//     S = Q K^T and dP = dO V^T (score), dV^T += dO^T P and dK^T += Q^T dS (PV).
+//   Tiles are double-buffered in LDS and move straight from global memory
+//   into LDS (buffer_load_dwordx4 ... lds); with RoPE the rotated tile (K in
+//   the dQ pass, Q in the dK/dV pass) is turned in place by the threads that
+//   loaded it before the workgroup's barrier.
+#include <math.h>
+
+#include "rac_device.h"
+#include "rac_internal.h"
+
+namespace rac {
+namespace bwd {
+
+constexpr int BR = 128;  // stationary rows per workgroup (4 waves x 32)
+constexpr int BT = 64;   // rows of a streamed tile
+constexpr int NWAVES = 4;
+constexpr int NXCD = 8;
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposed LDS read: in each 16-lane group, lane i receives element i%4 of
+// the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Position of logical 16-byte chunk c of tile row `row` (XOR swizzle: the
+// score-pattern reads take one chunk column of 16 consecutive rows at once,
+// so rows spread over all chunk positions). Both tiles of a pass use it.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw (unformatted) 32-bit data
+
+// Buffer descriptor of rows t*BT .. N-1 of a [N][row_elems] tensor; rows past
+// N read as zeros.
+template <typename E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const E* base, int row_elems, int t,
+                                                            int N) {
+    const int64_t r0 = (int64_t)t * BT;
+    const int64_t bytes = (N - r0) * row_elems * (int64_t)sizeof(E);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + r0 * row_elems), 0,
+                                             (int)min(bytes, (int64_t)0x7fffffff),
+                                             BUF_RSRC_FLAGS);
+}
+
+// Loads of two streamed [BT][D] tiles (A, rotated in place when ROPE, and B)
+// by the workgroup's 4 waves, global -> LDS; block b of a tile holds chunks
+// 64b .. 64b+63. Optionally also 64 per-row floats x 2 (the tile rows' scaled
+// L and Delta) through registers into LDS.
+template <int DT, int D, bool ROPE>
+struct Streamer {
+    static constexpr int CH = D / 8;
+    static constexpr int INSTR = BT * CH / (64 * NWAVES);
+    f32x4 cs[ROPE ? INSTR : 1][2];
+    f32x4 rowv;  // this lane's 4 row floats (L or Delta), lanes 0..31 of wave 0
+
+    __device__ __forceinline__ void issue(uint16_t* abuf, uint16_t* bbuf,
+                                          __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          __amdgpu_buffer_rsrc_t rt, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) {
+            const int blk = wave * INSTR + j;
+            const int g = blk * 64 + lane;
+            const int row = g / CH;
+            const int el = row * D + 8 * ((g % CH) ^ swz<D>(row));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf + blk * 512), 16, el * 2,
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(bbuf + blk * 512), 16, el * 2,
+                                                     0, 0, 0);
+            if (ROPE) {
+                cs[j][0] = __builtin_bit_cast(f32x4,
+                                              __builtin_amdgcn_raw_buffer_load_b128(rt, el * 4, 0, 0));
+                cs[j][1] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, el * 4 + 16, 0, 0));
+            }
+        }
+    }
+
+    // Row floats of the tile: lanes 0..15 of wave 0 load 4 of L's, lanes
+    // 16..31 4 of Delta's (rows past N read as zeros).
+    __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rl,
+                                               __amdgpu_buffer_rsrc_t rd, int wave, int lane) {
+        if (wave != 0) return;
+        if (lane < 16)
+            rowv = __builtin_bit_cast(f32x4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rl, lane * 16, 0, 0));
+        else if (lane < 32)
+            rowv = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, (lane - 16) * 16, 0, 0));
+    }
+
+    // After this thread's loads landed, before the barrier: rotate its chunks
+    // of tile A (ROPE) and store its row floats (L scaled to base 2).
+    __device__ __forceinline__ void finish(uint16_t* abuf, float* rows, bool with_rows, int wave,
+                                           int lane) {
+        if (ROPE) {
+#pragma unroll
+            for (int j = 0; j < INSTR; ++j) {
+                u32x4* p = reinterpret_cast<u32x4*>(abuf + (wave * INSTR + j) * 512 + lane * 8);
+                *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
+            }
+        }
+        if (with_rows && wave == 0 && lane < 32) {
+            f32x4 x = rowv;
+            if (lane < 16) x = x * LOG2E;
+            *reinterpret_cast<f32x4*>(rows + lane * 4) = x;
+        }
+    }
+};
+
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Per-wave pieces shared by both passes.
+template <int DT, int D>
+struct Wave {
+    typedef Fmt<DT> F;
+    typedef typename F::vec8 vec8;
+    static constexpr int QCH = D / 16;   // 16-deep MFMA steps over the head dim
+    static constexpr int DBLK = D / 32;  // 32-row blocks of a C^T accumulator
+
+    // 32 rows (r0 + n) of a [N][D] tensor as score-pattern B operands,
+    // rotated by their positions when `table` is given.
+    __device__ __forceinline__ static void load_rows(vec8 (&f)[QCH], const uint16_t* base,
+                                                     const float* table, int r0, int N, int n,
+                                                     int hh) {
+        const int row = r0 + n;
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (row < N) {
+                const int d0 = 16 * c + 8 * hh;
+                w = *reinterpret_cast<const u32x4*>(base + (int64_t)row * D + d0);
+                if (table) {
+                    const f32x4* t = reinterpret_cast<const f32x4*>(table + (int64_t)row * D + d0);
+                    w = rope_rotate8<DT>(w, t[0], t[1]);
+                }
+            }
+            f[c] = as_vec8<DT>(w);
+        }
+    }
+
+    // Score pattern: C = X[r0 .. r0+31] (LDS tile rows) times the stationary
+    // rows f, over the head dimension.
+    __device__ __forceinline__ static f32x16 score(const uint16_t* X, int r0, const vec8 (&f)[QCH],
+                                                   int n, int hh) {
+        f32x16 acc = {};
+        const int row = r0 + n;
+        const int sw = swz<D>(row);
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(X + row * D + 8 * ((2 * c + hh) ^ sw));
+            acc = F::mfma(as_vec8<DT>(a), f[c], acc);
+        }
+        return acc;
+    }
+
+    // PV pattern: acc^T (DBLK blocks of 32 d-rows x 32 lanes) += X^T Y for the
+    // 32 tile rows r0 .. r0+31 of LDS tile X, with Y given as the packed
+    // score-pattern values y[e] (e = 16-row step). The transpose-read lane
+    // geometry takes rows r0 + 16e + lrow (and + 8), chunk 4i + lc, elements
+    // le .. le+3, in the same permuted order as the packed registers.
+    __device__ __forceinline__ static void pv(f32x16 (&acc)[DBLK], const uint16_t* X, int r0,
+                                              const u32x4 (&y)[2], int lane) {
+        const int g4 = lane >> 4, j16 = lane & 15;
+        const int lrow = 4 * (g4 >> 1) + (j16 >> 2);
+        const int lc = 2 * (g4 & 1) + ((j16 & 3) >> 1);
+        const int le = 4 * (j16 & 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int rlo = r0 + 16 * e + lrow, rhi = rlo + 8;
+            const int slo = swz<D>(rlo), shi = swz<D>(rhi);
+            const vec8 b = as_vec8<DT>(y[e]);
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i) {
+                const u32x2 lo = __builtin_bit_cast(
+                    u32x2, lds_read_tr16(X + rlo * D + 8 * ((4 * i + lc) ^ slo) + le));
+                const u32x2 hi = __builtin_bit_cast(
+                    u32x2, lds_read_tr16(X + rhi * D + 8 * ((4 * i + lc) ^ shi) + le));
+                const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                acc[i] = F::mfma(as_vec8<DT>(a), b, acc[i]);
+            }
+        }
+    }
+
+    // Packs a score-pattern result into the two 16-row PV operands.
+    __device__ __forceinline__ static void pack(const f32x16& x, u32x4 (&y)[2]) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) y[e][t2] = F::pack2(x[8 * e + 2 * t2], x[8 * e + 2 * t2 + 1]);
+    }
+
+    // Writes C^T (scaled by `scale`) as row `row` of a [N][D] tensor: this
+    // lane's elements d = 32i + 8gq + 4hh + (0..3). With `table`, the pairs
+    // are first turned back by the row's position, R(-p):
+    //   x0 = y0 c + y1 s,  x1 = y1 c - y0 s.
+    __device__ __forceinline__ static void write(const f32x16 (&acc)[DBLK], float scale,
+                                                 uint16_t* orow, const float* trow, int hh) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = 32 * i + 8 * gq + 4 * hh;
+                float y[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) y[t] = acc[i][4 * gq + t] * scale;
+                if (trow) {
+                    const f32x4 cs = *reinterpret_cast<const f32x4*>(trow + d0);
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const float c = cs[2 * pr], s = cs[2 * pr + 1];
+                        const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+                        y[2 * pr] = __builtin_fmaf(y0, c, y1 * s);
+                        y[2 * pr + 1] = __builtin_fmaf(y1, c, -(y0 * s));
+                    }
+                }
+                u32x2 w;
+                w[0] = F::pack2(y[0], y[1]);
+                w[1] = F::pack2(y[2], y[3]);
+                *reinterpret_cast<u32x2*>(orow + d0) = w;
+            }
+    }
+};
+
+// 1-D work-unit index, XCD-aware order (the hardware deals workgroup ids
+// round-robin over 8 XCDs; consecutive units on one XCD share a head), then
+// (outer, tile) with the heaviest tile first.
+__device__ __forceinline__ void decode(int per_outer, int& outer, int& idx) {
+    const int units = gridDim.x;
+    int u = blockIdx.x;
+    if (units % NXCD == 0) u = (u % NXCD) * (units / NXCD) + u / NXCD;
+    idx = u % per_outer;
+    outer = u / per_outer;
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass: one workgroup per (b, query head, 128-row query tile), heaviest
+// first. Also writes Delta = rowsum(dO * O) for the dK/dV pass.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int RM>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
+    float* __restrict__ delta, const float* __restrict__ table, int Hq, int Hkv, int N,
+    int n_qtiles, float scale_log2, float scale) {
+    constexpr bool ROPE = RM == ROT_QK;
+    typedef Wave<DT, D> W;
+    typedef Streamer<DT, D, ROPE> S;
+    constexpr int TILE = BT * D;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K0 V0 K1 V1
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    int bh, slot;
+    decode(n_qtiles, bh, slot);
+    const int qt = n_qtiles - 1 - slot;
+    const int b = bh / Hq, h = bh % Hq;
+    const int g = h / (Hq / Hkv);
+    const int qw0 = qt * BR + 32 * wave;
+    const int row = qw0 + n;
+    const int64_t qhead = ((int64_t)b * Hq + h) * N;
+    const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
+    const uint16_t* kbase = k + kvhead * D;
+    const uint16_t* vbase = v + kvhead * D;
+    const int n_tiles = (min(qt * BR + BR, N) - 1) / BT + 1;
+    const int wave_tiles = qw0 < N ? min(qw0 + 31, N - 1) / BT + 1 : 0;
+
+    typename W::vec8 qf[W::QCH], dof[W::QCH];
+    W::load_rows(qf, q + qhead * D, ROPE ? table : nullptr, qw0, N, n, hh);
+    W::load_rows(dof, dout + qhead * D, nullptr, qw0, N, n, hh);
+    // Delta_i = dO_i . O_i (this lane's half of the head dim, then the other's)
+    float dl = 0.f, l2 = 0.f;
+    if (row < N) {
+        const uint16_t* orow = out + (qhead + row) * D;
+#pragma unroll
+        for (int c = 0; c < W::QCH; ++c) {
+            const u32x4 o = *reinterpret_cast<const u32x4*>(orow + 16 * c + 8 * hh);
+            const u32x4 d = __builtin_bit_cast(u32x4, dof[c]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dl += W::F::lo(o[t]) * W::F::lo(d[t]) + W::F::hi(o[t]) * W::F::hi(d[t]);
+        }
+        l2 = lse[qhead + row] * LOG2E;
+    }
+    dl += __shfl_xor(dl, 32);
+    if (row < N && hh == 0) delta[qhead + row] = dl;
+
+    f32x16 acc[W::DBLK];
+#pragma unroll
+    for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
+
+    S st;
+    auto rt = [&](int t) { return rows_rsrc(table, ROPE ? D : 0, t, N); };
+    st.issue(smem, smem + TILE, rows_rsrc(kbase, D, 0, N), rows_rsrc(vbase, D, 0, N), rt(0), wave,
+             lane);
+    for (int t = 0; t < n_tiles; ++t) {
+        uint16_t* Ks = smem + (t & 1) * 2 * TILE;
+        const uint16_t* Vs = Ks + TILE;
+        wait_all_loads();
+        st.finish(Ks, nullptr, false, wave, lane);
+        __syncthreads();  // tile t complete; the other buffers are no longer read
+        if (t + 1 < n_tiles) {
+            uint16_t* nk = smem + ((t + 1) & 1) * 2 * TILE;
+            st.issue(nk, nk + TILE, rows_rsrc(kbase, D, t + 1, N), rows_rsrc(vbase, D, t + 1, N),
+                     rt(t + 1), wave, lane);
+        }
+        if (t >= wave_tiles) continue;
+        const int k0 = t * BT;
+        const bool diag = k0 + BT - 1 > qw0;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // S^T and dP^T for keys k0 + 32kb .. +31 (lane column = query row)
+            f32x16 s = W::score(Ks, 32 * kb, qf, n, hh);
+            const f32x16 dp = W::score(Vs, 32 * kb, dof, n, hh);
+            f32x16 ds;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -l2));
+                if (diag && key > row) p = 0.f;
+                ds[j] = p * (dp[j] - dl);
+            }
+            u32x4 y[2];
+            W::pack(ds, y);
+            W::pv(acc, Ks, 32 * kb, y, lane);
+        }
+    }
+    if (row < N)
+        W::write(acc, scale, dq + (qhead + row) * D, ROPE ? table + (int64_t)row * D : nullptr, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV pass: one workgroup per (b, key/value head, 128-row key tile),
+// heaviest first; it walks the 64-row query tiles at or after its keys for
+// every query head of the group.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int RM>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ lse,
+    const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, const float* __restrict__ table, int Hq, int Hkv, int N,
+    int n_ktiles, float scale_log2, float scale) {
+    constexpr bool ROPE = RM == ROT_QK;
+    typedef Wave<DT, D> W;
+    typedef Streamer<DT, D, ROPE> S;
+    constexpr int TILE = BT * D;
+    // Q0 dO0 Q1 dO1, then per buffer 64 scaled L and 64 Delta values
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+    __shared__ __attribute__((aligned(16))) float rows_lds[2][2 * BT];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    int bg, slot;
+    decode(n_ktiles, bg, slot);
+    const int kt = slot;  // heaviest first: key tile 0 sees every query
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int group = Hq / Hkv;
+    const int kw0 = kt * BR + 32 * wave;
+    const int key = kw0 + n;
+    const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
+
+    typename W::vec8 kf[W::QCH], vf[W::QCH];
+    W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
+    W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
+    f32x16 ak[W::DBLK], av[W::DBLK];
+#pragma unroll
+    for (int i = 0; i < W::DBLK; ++i) ak[i] = av[i] = f32x16{};
+
+    // the query tiles of one head that see the workgroup's keys, all heads
+    const int t0 = (kt * BR) / BT;
+    const int per_head = (N - 1) / BT + 1 - t0;
+    const int steps = per_head * group;
+    auto job = [&](int i, int& qh, int& tq) {
+        qh = g * group + i / per_head;
+        tq = t0 + i % per_head;
+    };
+    S st;
+    auto start = [&](int i) {
+        int qh, tq;
+        job(i, qh, tq);
+        const int64_t qhead = ((int64_t)b * Hq + qh) * N;
+        uint16_t* a = smem + (i & 1) * 2 * TILE;
+        st.issue(a, a + TILE, rows_rsrc(q + qhead * D, D, tq, N),
+                 rows_rsrc(dout + qhead * D, D, tq, N),
+                 rows_rsrc(table, ROPE ? D : 0, tq, N), wave, lane);
+        st.issue_rows(rows_rsrc(lse + qhead, 1, tq, N), rows_rsrc(delta + qhead, 1, tq, N), wave,
+                      lane);
+    };
+    start(0);
+    for (int i = 0; i < steps; ++i) {
+        int qh, tq;
+        job(i, qh, tq);
+        uint16_t* Qs = smem + (i & 1) * 2 * TILE;
+        const uint16_t* dOs = Qs + TILE;
+        float* rl = rows_lds[i & 1];
+        wait_all_loads();
+        st.finish(Qs, rl, true, wave, lane);
+        __syncthreads();  // step i complete; the other buffers are no longer read
+        if (i + 1 < steps) start(i + 1);
+        const int q0 = tq * BT;
+        if (kw0 >= N) continue;              // the wave has no keys
+        if (q0 + BT - 1 < kw0) continue;     // every query of the tile precedes the wave's keys
+        const bool diag = q0 < kw0 + 31;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S and dP for queries q0 + 32qb .. +31 (lane column = key)
+            const f32x16 s = W::score(Qs, 32 * qb, kf, n, hh);
+            const f32x16 dp = W::score(dOs, 32 * qb, vf, n, hh);
+            f32x16 p, ds;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int r = 32 * qb + 8 * gq + 4 * hh;  // this lane's 4 query rows in the tile
+                const f32x4 lq = *reinterpret_cast<const f32x4*>(rl + r);
+                const f32x4 dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * gq + jj;
+                    const int qrow = q0 + r + jj;
+                    float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -lq[jj]));
+                    if ((diag && qrow < key) || qrow >= N) pj = 0.f;
+                    p[j] = pj;
+                    ds[j] = pj * (dp[j] - dq4[jj]);
+                }
+            }
+            u32x4 yp[2], yd[2];
+            W::pack(p, yp);
+            W::pack(ds, yd);
+            W::pv(av, dOs, 32 * qb, yp, lane);
+            W::pv(ak, Qs, 32 * qb, yd, lane);
+        }
+    }
+    if (key < N) {
+        W::write(ak, scale, dk + (kvhead + key) * D, ROPE ? table + (int64_t)key * D : nullptr, hh);
+        W::write(av, 1.f, dv + (kvhead + key) * D, nullptr, hh);
+    }
+}
+
+template <int DT, int D, int RM>
+static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
+    const float scale = (float)(1.0 / sqrt((double)D));
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const int n_qtiles = (a.N + BR - 1) / BR;
+    const int n_ktiles = (a.N + BR - 1) / BR;
+    const int64_t q_units = (int64_t)n_qtiles * a.Hq * a.B;
+    const int64_t k_units = (int64_t)n_ktiles * a.Hkv * a.B;
+    if (q_units > 0x7fffffff || k_units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    const uint16_t* out = static_cast<const uint16_t*>(a.out);
+    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+    // the dQ pass writes Delta, which the dK/dV pass reads: same stream, in order
+    attn_bwd_dq_kernel<DT, D, RM><<<dim3((unsigned)q_units), 256, 0, stream>>>(
+        q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq, a.Hkv,
+        a.N, n_qtiles, scale_log2, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_bwd_dkdv_kernel<DT, D, RM><<<dim3((unsigned)k_units), 256, 0, stream>>>(
+        q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv),
+        a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+    return hipGetLastError();
+}
+
+template <int DT, int RM>
+static hipError_t launch_dt(const BwdArgs& a, hipStream_t stream) {
+    return a.D == 64 ? launch_typed<DT, 64, RM>(a, stream) : launch_typed<DT, 128, RM>(a, stream);
+}
+
+}  // namespace bwd
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream) {
+    if (a.dtype == DT_BF16)
+        return rot == ROT_QK ? bwd::launch_dt<DT_BF16, ROT_QK>(a, stream)
+                             : bwd::launch_dt<DT_BF16, ROT_NONE>(a, stream);
+    return rot == ROT_QK ? bwd::launch_dt<DT_FP16, ROT_QK>(a, stream)
+                         : bwd::launch_dt<DT_FP16, ROT_NONE>(a, stream);
+}
+
+}  // namespace rac

@@ -145,6 +145,24 @@ int check_attn_ptrs(const void* q, const void* k, const void* v, const void* out
     return RAC_OK;
 }
 
+// The pre-rotation pass and its inverse: x (q or dq_rot), y (k or dk_rot) in,
+// x_out, y_out written. Exact in-place use is allowed; any other overlap is not.
+int check_pass_ptrs(const void* x, const void* y, const void* x_out, const void* y_out, int B,
+                    int Hq, int Hkv, int N, int D) {
+    if (!x || !y || !x_out || !y_out)
+        return fail(RAC_ERR_ARG, "input and output tensors must be non-null");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(x_out) || !aligned16(y_out))
+        return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int64_t xb = (int64_t)B * Hq * N * D * 2;
+    const int64_t yb = (int64_t)B * Hkv * N * D * 2;
+    if ((x_out != x && overlap(x_out, xb, x, xb)) || overlap(x_out, xb, y, yb) ||
+        (y_out != y && overlap(y_out, yb, y, yb)) || overlap(y_out, yb, x, xb) ||
+        overlap(x_out, xb, y_out, yb))
+        return fail(RAC_ERR_ARG,
+                    "outputs may alias their inputs exactly, and must not overlap otherwise");
+    return RAC_OK;
+}
+
 // RAC_ATTN_SHAPE=pair|tile forces the attention launch shape (default: by size).
 int attn_shape_from_env() {
     const char* e = getenv("RAC_ATTN_SHAPE");
@@ -192,6 +210,47 @@ int plan_path(int B, int Hq, int Hkv, int N, int D, size_t workspace_bytes) {
 int hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(RAC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+
+// Backward arguments: inputs q, k, v, out, lse, dout; outputs dq, dk, dv, delta.
+int check_bwd_ptrs(const rac::BwdArgs& a) {
+    if (!a.q || !a.k || !a.v || !a.out || !a.lse || !a.dout || !a.dq || !a.dk || !a.dv || !a.delta)
+        return fail(RAC_ERR_ARG, "q, k, v, out, lse, dout, dq, dk, dv and delta must be non-null");
+    const void* all[] = {a.q, a.k, a.v, a.out, a.lse, a.dout, a.dq, a.dk, a.dv, a.delta};
+    for (const void* p : all)
+        if (!aligned16(p)) return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const int64_t qb = (int64_t)a.B * a.Hq * a.N * a.D * 2;
+    const int64_t kb = (int64_t)a.B * a.Hkv * a.N * a.D * 2;
+    const int64_t rb = (int64_t)a.B * a.Hq * a.N * 4;
+    const void* in[] = {a.q, a.k, a.v, a.out, a.lse, a.dout};
+    const int64_t in_bytes[] = {qb, kb, kb, qb, rb, qb};
+    const void* outs[] = {a.dq, a.dk, a.dv, a.delta};
+    const int64_t out_bytes[] = {qb, kb, kb, rb};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[o], out_bytes[o], in[i], in_bytes[i]))
+                return fail(RAC_ERR_ARG, "dq, dk, dv and delta must not overlap any input");
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2]))
+                return fail(RAC_ERR_ARG, "dq, dk, dv and delta must not overlap each other");
+    }
+    return RAC_OK;
+}
+
+int attn_bwd_common(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
+                    int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype, int rot,
+                    void* stream, const char* what) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if (rot == rac::ROT_QK && (rc = check_base(rope_base)) != RAC_OK) return rc;
+    if (empty) return ok();
+    rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype};
+    if ((rc = check_bwd_ptrs(a)) != RAC_OK) return rc;
+    if (rot == rac::ROT_QK && (rc = get_table(D, rope_base, N, &a.table)) != RAC_OK) return rc;
+    return hip_status(rac::launch_attn_bwd(a, rot, static_cast<hipStream_t>(stream)), what);
 }
 
 }  // namespace
@@ -251,22 +310,45 @@ int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B
     if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)
         return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280");
     if (empty) return ok();
-    if (!q || !k || !q_rot || !k_rot)
-        return fail(RAC_ERR_ARG, "q, k, q_rot and k_rot must be non-null");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(q_rot) || !aligned16(k_rot))
-        return fail(RAC_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
-    const int64_t kbytes = (int64_t)B * Hkv * N * D * 2;
-    // exact in-place use is allowed; any other overlap is not
-    if ((q_rot != q && overlap(q_rot, qbytes, q, qbytes)) || overlap(q_rot, qbytes, k, kbytes) ||
-        (k_rot != k && overlap(k_rot, kbytes, k, kbytes)) || overlap(k_rot, kbytes, q, qbytes) ||
-        overlap(q_rot, qbytes, k_rot, kbytes))
-        return fail(RAC_ERR_ARG, "q_rot/k_rot may alias q/k exactly, and must not overlap otherwise");
+    if ((rc = check_pass_ptrs(q, k, q_rot, k_rot, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
     return hip_status(rac::launch_rope_prerotate(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D,
                                                  dtype, static_cast<hipStream_t>(stream)),
                       "rope_prerotate launch");
+}
+
+int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
+                       int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)
+        return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280");
+    if (empty) return ok();
+    if ((rc = check_pass_ptrs(dq_rot, dk_rot, dq, dk, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    const float* table = nullptr;
+    if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    return hip_status(rac::launch_rope_unrotate(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D,
+                                                dtype, static_cast<hipStream_t>(stream)),
+                      "rope_prerotate_bwd launch");
+}
+
+
+int attn_rope_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* delta, int B, int Hq, int Hkv, int N, int D, double rope_base,
+                         int dtype, void* stream) {
+    return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                           rope_base, dtype, rac::ROT_QK, stream, "attn_rope_causal_bwd launch");
+}
+
+int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    float* delta, int B, int Hq, int Hkv, int N, int D, int dtype, void* stream) {
+    return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D, 1.0,
+                           dtype, rac::ROT_NONE, stream, "attn_causal_bwd launch");
 }
 
 int rope_prerotate_k(const void* k, void* k_rot, int B, int Hkv, int N, int D, double rope_base,

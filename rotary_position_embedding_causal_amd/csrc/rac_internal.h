@@ -30,9 +30,35 @@ enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2 };
 // Causal attention forward; `rot` is a ROT_* mode.
 hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream);
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;     // the forward's output
+    const float* lse;    // the forward's log-sum-exp (natural log), [B, Hq, N]
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;        // written: rowsum(dout * out), [B, Hq, N]
+    const float* table;  // cos/sin table (ROT_QK only)
+    int B, Hq, Hkv, N, D;
+    int dtype;
+};
+
+// Causal attention backward (ROT_QK: RoPE fused, gradients with respect to
+// the unrotated q and k; ROT_NONE: inputs already rotated).
+hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream);
+
 // q_rot = RoPE(q), k_rot = RoPE(k).
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
                                  const float* table, int B, int Hq, int Hkv, int N, int D,
                                  int dtype, hipStream_t stream);
+
+// The inverse turn R(-p) of the same pass: dq = R(-p) dq_rot, dk = R(-p)
+// dk_rot (the gradient of the pre-rotation).
+hipError_t launch_rope_unrotate(const void* dq_rot, const void* dk_rot, void* dq, void* dk,
+                                const float* table, int B, int Hq, int Hkv, int N, int D,
+                                int dtype, hipStream_t stream);
 
 }  // namespace rac

@@ -26,8 +26,26 @@ namespace rac {
 
 constexpr int PR_THREADS = 256;
 
-// PR_HEADS slabs per lane: that many independent 16-byte loads in flight
-template <int DT, int D, int PR_HEADS>
+// The inverse turn R(-p) = R(p)^T of rope_rotate8 on 8 elements (4 pairs),
+// same table entries: x0 = y0*c + y1*s, x1 = y1*c - y0*s, in fp32 with one
+// fused multiply-add each, then one rounding to the storage format.
+template <int DT>
+__device__ __forceinline__ u32x4 rope_unrotate8(u32x4 y, f32x4 cs_lo, f32x4 cs_hi) {
+    typedef Fmt<DT> F;
+    u32x4 x;
+    const float c[4] = {cs_lo[0], cs_lo[2], cs_hi[0], cs_hi[2]};
+    const float s[4] = {cs_lo[1], cs_lo[3], cs_hi[1], cs_hi[3]};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float y0 = F::lo(y[t]), y1 = F::hi(y[t]);
+        x[t] = F::pack2(__builtin_fmaf(y0, c[t], y1 * s[t]), __builtin_fmaf(y1, c[t], -(y0 * s[t])));
+    }
+    return x;
+}
+
+// PR_HEADS slabs per lane: that many independent 16-byte loads in flight.
+// INV: turn by -p instead of +p (the gradient of the pass).
+template <int DT, int D, int PR_HEADS, bool INV>
 __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* q_rot,
     uint16_t* k_rot, const float* __restrict__ table, int N, int64_t q_slabs,
@@ -60,18 +78,19 @@ __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
         if (slab < total_slabs) {
             uint16_t* dst = slab < q_slabs ? q_rot + slab * slab_elems
                                            : k_rot + (slab - q_slabs) * slab_elems;
-            __builtin_nontemporal_store(rope_rotate8<DT>(x[s], cs_lo, cs_hi),
+            __builtin_nontemporal_store(INV ? rope_unrotate8<DT>(x[s], cs_lo, cs_hi)
+                                            : rope_rotate8<DT>(x[s], cs_lo, cs_hi),
                                         reinterpret_cast<u32x4*>(dst + within));
         }
     }
 }
 
-template <int DT, int D, int H>
+template <int DT, int D, int H, bool INV>
 static hipError_t launch_heads(const void* q, const void* k, void* q_rot, void* k_rot,
                                const float* table, int N, int64_t q_slabs, int64_t total,
                                unsigned gx, hipStream_t stream) {
     dim3 grid(gx, (unsigned)((total + H - 1) / H));
-    rope_prerotate_kernel<DT, D, H><<<grid, PR_THREADS, 0, stream>>>(
+    rope_prerotate_kernel<DT, D, H, INV><<<grid, PR_THREADS, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
         static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N, q_slabs, total);
     return hipGetLastError();
@@ -91,7 +110,7 @@ inline int prerotate_heads(int64_t total) {
     return h;
 }
 
-template <int DT, int D>
+template <int DT, int D, bool INV>
 static hipError_t launch_typed(const void* q, const void* k, void* q_rot, void* k_rot,
                                const float* table, int B, int Hq, int Hkv, int N,
                                hipStream_t stream) {
@@ -100,21 +119,34 @@ static hipError_t launch_typed(const void* q, const void* k, void* q_rot, void* 
     const int64_t total = q_slabs + (int64_t)B * Hkv;
     const unsigned gx = (unsigned)((lanes + PR_THREADS - 1) / PR_THREADS);
     switch (prerotate_heads(total)) {
-        case 8: return launch_heads<DT, D, 8>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        case 4: return launch_heads<DT, D, 4>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        case 2: return launch_heads<DT, D, 2>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        default: return launch_heads<DT, D, 1>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 8: return launch_heads<DT, D, 8, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 4: return launch_heads<DT, D, 4, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 2: return launch_heads<DT, D, 2, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        default: return launch_heads<DT, D, 1, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
     }
+}
+
+template <bool INV>
+static hipError_t launch_any(const void* q, const void* k, void* q_rot, void* k_rot,
+                             const float* table, int B, int Hq, int Hkv, int N, int D, int dtype,
+                             hipStream_t stream) {
+    if (dtype == DT_BF16)
+        return D == 64 ? launch_typed<DT_BF16, 64, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                       : launch_typed<DT_BF16, 128, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return D == 64 ? launch_typed<DT_FP16, 64, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                   : launch_typed<DT_FP16, 128, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
 }
 
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
                                  const float* table, int B, int Hq, int Hkv, int N, int D,
                                  int dtype, hipStream_t stream) {
-    if (dtype == DT_BF16)
-        return D == 64 ? launch_typed<DT_BF16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
-                       : launch_typed<DT_BF16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
-    return D == 64 ? launch_typed<DT_FP16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
-                   : launch_typed<DT_FP16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return launch_any<false>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D, dtype, stream);
+}
+
+hipError_t launch_rope_unrotate(const void* dq_rot, const void* dk_rot, void* dq, void* dk,
+                                const float* table, int B, int Hq, int Hkv, int N, int D,
+                                int dtype, hipStream_t stream) {
+    return launch_any<true>(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D, dtype, stream);
 }
 
 }  // namespace rac

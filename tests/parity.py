@@ -81,3 +81,23 @@ def oracle_rows(q_bits, k_bits, v_bits, dtype, base, Hq, Hkv, rows_by_head, vari
             kr = oracle.decode(oracle.encode(kr, dtype), dtype)
         res[(b, h)] = oracle.attention(qr, kr, v, rows=rows)
     return res
+
+
+# Backward bounds (gradients against the fp64 oracle). The forward's O bounds
+# carried over, with the max-abs bound scaled by the tensor's largest
+# magnitude: gradients, unlike O (a convex combination of N(0,1) values), are
+# not of unit size (dv_j sums dO over every row that sees key j). The error
+# sources are the bf16/fp16 roundings of P and dS before the matrix products
+# and of the outputs (unit roundoff 2^-9 for bf16): rel-L2 1e-2 is ~5 of them.
+G_MAXABS_REL = 2e-2
+G_RELL2 = 1e-2
+
+
+def assert_grad(got, ref, what=""):
+    d = got - ref
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    mx = float(np.max(np.abs(d)))
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    assert mx <= G_MAXABS_REL * scale and (rel <= G_RELL2 or np.linalg.norm(ref) < 1e-30), \
+        "%s: max|d|=%.3e (bound %.3e) relL2=%.3e" % (what, mx, G_MAXABS_REL * scale, rel)
+    return mx, rel

@@ -214,3 +214,54 @@ def test_auto_plan_paths():
         rac.auto_plan(1, 4, 4, 64, 96, 0, 0)
     with pytest.raises(ValueError):
         rac.auto_plan(1, 4, 3, 64, 64, 0, 0)
+
+
+def bwd(fused=True, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, do=ctypes.c_void_p(P * 6), dq=ctypes.c_void_p(P * 7),
+             dk=ctypes.c_void_p(P * 8), dv=ctypes.c_void_p(P * 9), delta=ctypes.c_void_p(P * 10),
+             B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    args = [a[x] for x in ("q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "delta", "B",
+                           "Hq", "Hkv", "N", "D")]
+    if fused:
+        return rac.lib().attn_rope_causal_bwd(*args, a["base"], a["dtype"], None)
+    return rac.lib().attn_causal_bwd(*args, a["dtype"], None)
+
+
+# shape and type errors of the forward list apply unchanged (every pointer
+# here is a fake, never-dereferenced address: each case must fail validation)
+BAD_BWD = BAD[:10]
+
+
+@pytest.mark.parametrize("kw,code", BAD_BWD, ids=[str(b[0]) for b in BAD_BWD])
+def test_backward_rejects_bad_arguments(kw, code):
+    assert bwd(True, **kw) == code
+    assert bwd(False, **kw) == code
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "delta"])
+def test_backward_requires_every_pointer(name):
+    assert bwd(True, **{name: None}) == rac.RAC_ERR_ARG
+    assert bwd(False, **{name: None}) == rac.RAC_ERR_ARG
+    assert bwd(True, **{name: ctypes.c_void_p(P * 11 + 8)}) == rac.RAC_ERR_ALIGN
+
+
+def test_backward_overlap_and_empty_rules():
+    assert bwd(dq=ctypes.c_void_p(P * 1 + 64)) == rac.RAC_ERR_ARG    # dq over q
+    assert bwd(delta=ctypes.c_void_p(P * 9)) == rac.RAC_ERR_ARG      # delta over dv
+    assert bwd(False, dk=ctypes.c_void_p(P * 7 + 16)) == rac.RAC_ERR_ARG  # dk over dq
+    assert bwd(base=0.0) == rac.RAC_ERR_ARG
+    assert bwd(base=float("nan")) == rac.RAC_ERR_ARG
+    assert bwd(B=0) == rac.RAC_OK and bwd(N=0, q=None) == rac.RAC_OK
+    assert bwd(False, B=0) == rac.RAC_OK
+
+
+def test_rope_prerotate_bwd_argument_rules():
+    f = rac.lib().rope_prerotate_bwd
+    assert f(Q, K, None, L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
+    assert f(Q, K, ctypes.c_void_p(P + 16), L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
+    assert f(Q, K, ctypes.c_void_p(P * 3 + 8), L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ALIGN
+    assert f(Q, K, O, L, 1, 4, 2, 64, 96, 1e4, 0, None) == rac.RAC_ERR_UNSUPPORTED
+    assert f(Q, K, O, L, 1, 4, 2, 64, 64, -1.0, 0, None) == rac.RAC_ERR_ARG
+    assert f(Q, K, O, L, 1, 4, 3, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
+    assert f(Q, K, O, L, 0, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_OK

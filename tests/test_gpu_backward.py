@@ -1,0 +1,174 @@
+"""GPU parity of the backward: the HIP kernels, called through the C ABI,
+against the fp64 oracle's gradients on the same seeded inputs.
+
+Cases: the fused backward (attn_rope_causal_bwd) and the pre-rotation path's
+backward (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd) on small shapes
+spanning several tiles with ragged tails, GQA ratios 1-8, D = 64 and 128,
+bf16 and fp16; the inverse rotation pass on its own; determinism; and one key/
+value group of the Llama-3-8B-shaped layer at full length (N = 2048) in the
+launch configuration the bench times. Bounds: parity.assert_grad.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotary_position_embedding_causal_amd as rac
+from rotary_position_embedding_causal_amd import inputs
+from parity import assert_grad, bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    rac.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+SHAPES = [  # B, Hq, Hkv, N, D, dtype, base
+    (1, 4, 4, 512, 64, "bf16", 10000.0),
+    (1, 8, 2, 300, 128, "bf16", 500000.0),
+    (2, 4, 1, 129, 64, "fp16", 10000.0),
+    (1, 8, 1, 65, 128, "fp16", 500000.0),
+    (1, 2, 2, 1, 64, "bf16", 10000.0),
+    (1, 6, 3, 17, 128, "bf16", 10000.0),
+    (1, 4, 2, 1000, 128, "bf16", 500000.0),
+]
+
+
+def _id(s):
+    return "B%d_Hq%d_Hkv%d_N%d_D%d_%s" % s[:6]
+
+
+def _case(B, Hq, Hkv, N, D, dt, base, key):
+    q, k, v = inputs.qkv(B, Hq, Hkv, N, D, dt, key=key)
+    do = inputs.draw((B, Hq, N, D), dt, key, 3)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    return (q, k, v, do), (qd, kd, vd, dod, o, lse)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+@pytest.mark.parametrize("path", ["fused", "prerotate"])
+def test_backward_matches_oracle(shape, path):
+    B, Hq, Hkv, N, D, dt, base = shape
+    print("backward %s %s" % (path, _id(shape)), flush=True)
+    (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (401, N, D))
+    fn = rac.attn_rope_causal_bwd if path == "fused" else rac.prerotate_path_bwd
+    dq, dk, dv, delta = fn(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    for variant in ("rounded", "exact"):
+        rdq, rdk, rdv, rdelta, _ = oracle.rope_attention_bwd(
+            inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), dt, base, variant)
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad(to_f64(got), ref, "%s %s vs %s oracle" % (path, name, variant))
+        assert_grad(delta.cpu().double().numpy(), rdelta, "%s delta" % path)
+
+
+@pytest.mark.parametrize("shape", SHAPES[:4], ids=_id)
+def test_paths_agree_and_are_deterministic(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    _, (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (402, N, D))
+    f1 = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    f2 = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    p = rac.prerotate_path_bwd(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    for a, b in zip(f1, f2):
+        assert torch.equal(a, b)  # one writer per element: no run-to-run variation
+    # dv and delta see the same rotated operands on both paths; dq and dk
+    # differ by the pre-rotation path's extra rounding of dq', dk'
+    assert torch.equal(f1[2], p[2]) and torch.equal(f1[3], p[3])
+    for a, b, name in ((f1[0], p[0], "dq"), (f1[1], p[1], "dk")):
+        assert_grad(to_f64(b), to_f64(a), "prerotate vs fused " + name)
+
+
+@pytest.mark.parametrize("shape", SHAPES[1:4], ids=_id)
+def test_attn_causal_bwd_on_rotated_inputs(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    (q, k, v, do), (qd, kd, vd, dod, _, _) = _case(B, Hq, Hkv, N, D, dt, base, (403, N, D))
+    qr, kr = rac.rope_prerotate(qd, kd, base)
+    o, lse = rac.attn_causal_fwd(qr, kr, vd)
+    dq, dk, dv, delta = rac.attn_causal_bwd(qr, kr, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    dec = lambda t: oracle.decode(bits(t), dt)  # noqa: E731
+    rdq, rdk, rdv, _, rdelta = oracle.attention_bwd(dec(qr), dec(kr), dec(vd), dec(dod))
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad(to_f64(got), ref, "attn_causal_bwd " + name)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 300, 128, "bf16", 500000.0),
+                                   (2, 2, 2, 4096, 64, "fp16", 10000.0)], ids=_id)
+def test_rope_prerotate_bwd_is_the_inverse_rotation(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    gq = inputs.draw((B, Hq, N, D), dt, (404, N), 0)
+    gk = inputs.draw((B, Hkv, N, D), dt, (404, N), 1)
+    dq, dk = rac.rope_prerotate_bwd(gq.to(DEV), gk.to(DEV), base)
+    g2 = gq.to(DEV).clone()
+    rac.rope_prerotate_bwd(g2, gk.to(DEV), base, dq=g2, dk=torch.empty_like(gk, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(g2, dq)  # in place
+    neg = -np.arange(N)
+    for src, got in ((gq, dq), (gk, dk)):
+        y = oracle.rope(oracle.decode(inputs.bits(src), dt), neg, base)
+        ref = oracle.encode(y, dt)
+        g = bits(got)
+        exact = float(np.mean(g == ref))
+        assert exact >= 0.999, "bit-exact fraction %.5f" % exact
+        x = oracle.decode(inputs.bits(src), dt)
+        pair = np.repeat(np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]), 2, axis=-1)
+        gv = oracle.decode(g, dt)
+        spacing = np.spacing(np.abs(gv).astype(np.float16 if dt == "fp16" else np.float32))
+        ulp = spacing.astype(np.float64) * (65536.0 if dt == "bf16" else 1.0)
+        assert np.all(np.abs(gv - y) <= ulp + 8 * 2.0 ** -24 * pair)
+
+
+@pytest.mark.parametrize("N", [2, 63, 64, 65, 127, 129])
+@pytest.mark.parametrize("ratio", [1, 4, 8])
+def test_ragged_lengths_and_gqa(N, ratio):
+    B, Hkv, D, dt, base = 1, 1, 128, "bf16", 10000.0
+    Hq = Hkv * ratio
+    (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (405, N, ratio))
+    dq, dk, dv, delta = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rdelta, _ = oracle.rope_attention_bwd(
+        inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), dt, base, "rounded")
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad(to_f64(got), ref, "N=%d ratio=%d %s" % (N, ratio, name))
+
+
+def test_full_length_one_group():
+    """The Llama-3-8B-shaped layer at N = 2048 in the bench's launch
+    configuration; the oracle checks one key/value group (4 query heads and
+    their key/value head), which the other groups do not influence."""
+    w = inputs.WORKLOADS["llama3_8b_gqa_n2048"]
+    B, Hq, Hkv, N, D, dt, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"], w["base"]
+    q, k, v = inputs.workload_qkv("llama3_8b_gqa_n2048")
+    do = inputs.draw((B, Hq, N, D), dt, (406,), 3)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    dq, dk, dv, _ = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    group = Hq // Hkv
+    g = 5
+    hs = slice(g * group, (g + 1) * group)
+    rdq, rdk, rdv, _, _ = oracle.rope_attention_bwd(
+        inputs.bits(q)[:, hs], inputs.bits(k)[:, g:g + 1], inputs.bits(v)[:, g:g + 1],
+        inputs.bits(do)[:, hs], dt, base, "rounded")
+    assert_grad(to_f64(dq[:, hs]), rdq, "full-length dq")
+    assert_grad(to_f64(dk[:, g:g + 1]), rdk, "full-length dk")
+    assert_grad(to_f64(dv[:, g:g + 1]), rdv, "full-length dv")
+
+
+def test_empty_inputs():
+    for shape in ((0, 2, 8, 64), (1, 2, 0, 64)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        l = torch.empty(shape[:3], dtype=torch.float32, device=DEV)
+        dq, dk, dv, delta = rac.attn_rope_causal_bwd(x, x, x, x, l, x, 10000.0)
+        dq2, dk2, dv2, _ = rac.attn_causal_bwd(x, x, x, x, l, x)
+        a, b = rac.rope_prerotate_bwd(x, x, 10000.0)
+        assert dq.shape == shape and dv2.shape == shape and a.shape == shape

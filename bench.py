@@ -313,11 +313,37 @@ def main():
         "paths": paths,
     }
 
+    result["backward"] = backward(torch, rac, w, qd, kd, vd, out_f, lse_f, ev, args.steps)
     if not args.no_sweep:
         result["crossover"] = crossover(torch, rac, inputs, dev, ev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(inputs, w)
     print(json.dumps(result), flush=True)
+
+
+def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):
+    """The backward of both paths on the bench workload, after the timed region
+    (not part of `value`): fused (attn_rope_causal_bwd) and pre-rotation
+    (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd). TFLOP/s count the
+    algorithmic backward work, 2.5 x the forward's (five N^2 products: S, dP,
+    dV, dK, dQ); the two-pass kernels rebuild S and dP once more."""
+    gen = torch.Generator(device=qd.device).manual_seed(20260913)
+    dout = torch.randn(qd.shape, generator=gen, device=qd.device, dtype=torch.float32).to(qd.dtype)
+    base = w["base"]
+    fns = {"fused": lambda: rac.attn_rope_causal_bwd(qd, kd, vd, out, lse, dout, base),
+           "prerotate": lambda: rac.prerotate_path_bwd(qd, kd, vd, out, lse, dout, base)}
+    res = {"flops_per_call": 2.5 * attn_flops(w), "dout": "N(0,1) from a seeded torch generator"}
+    for key, fn in fns.items():
+        warm(fn, 3, WARM_SECONDS, torch.cuda.synchronize)
+        pairs = [(ev(), ev()) for _ in range(reps)]
+        for a, b in pairs:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in pairs)
+        ms = ts[len(ts) // 2]
+        res[key] = {"ms": ms, "tflops": res["flops_per_call"] / ms / 1e9,
+                    "mfma_frac": res["flops_per_call"] / ms / 1e9 / MFMA_PEAK_TFLOPS[w["dtype"]]}
+    return res
 
 
 def crossover(torch, rac, inputs, dev, ev, reps=15):

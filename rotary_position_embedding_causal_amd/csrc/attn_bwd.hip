@@ -43,15 +43,16 @@
 //   loaded it before the workgroup's barrier.
 #include <math.h>
 
+#include <type_traits>
+
 #include "rac_device.h"
 #include "rac_internal.h"
 
 namespace rac {
 namespace bwd {
 
-constexpr int BR = 128;  // stationary rows per workgroup (4 waves x 32)
+constexpr int BR = 128;  // stationary query rows per dQ-pass workgroup (4 waves x 32)
 constexpr int BT = 64;   // rows of a streamed tile
-constexpr int NWAVES = 4;
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -88,13 +89,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const E* base, int r
 }
 
 // Loads of two streamed [BT][D] tiles (A, rotated in place when ROPE, and B)
-// by the workgroup's 4 waves, global -> LDS; block b of a tile holds chunks
+// by the workgroup's NW waves, global -> LDS; block b of a tile holds chunks
 // 64b .. 64b+63. Optionally also 64 per-row floats x 2 (the tile rows' scaled
 // L and Delta) through registers into LDS.
-template <int DT, int D, bool ROPE>
+template <int DT, int D, bool ROPE, int NW>
 struct Streamer {
     static constexpr int CH = D / 8;
-    static constexpr int INSTR = BT * CH / (64 * NWAVES);
+    static constexpr int INSTR = BT * CH / (64 * NW);
     f32x4 cs[ROPE ? INSTR : 1][2];
     f32x4 rowv;  // this lane's 4 row floats (L or Delta), lanes 0..31 of wave 0
 
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     int n_qtiles, float scale_log2, float scale) {
     constexpr bool ROPE = RM == ROT_QK;
     typedef Wave<DT, D> W;
-    typedef Streamer<DT, D, ROPE> S;
+    typedef Streamer<DT, D, ROPE, 4> S;
     constexpr int TILE = BT * D;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K0 V0 K1 V1
 
@@ -376,20 +377,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV pass: one workgroup per (b, key/value head, 128-row key tile),
+// dK/dV pass: one workgroup per (b, key/value head, 32*RW-key tile),
 // heaviest first; it walks the 64-row query tiles at or after its keys for
-// every query head of the group.
+// every query head of the group. Its 2*RW waves take two roles on the same
+// keys and the same streamed tiles: waves 0 .. RW-1 accumulate dV (they need
+// only S and P), waves RW .. 2RW-1 accumulate dK (S, dP and dS). Split this
+// way each wave holds one D-wide accumulator and at most two stationary
+// operands, so two waves fit on a SIMD (wave w and w + 4 share one), where a
+// wave holding both accumulators would run alone; S is computed by both
+// roles.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int RM>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
+template <int DT, int D, int RM, int RW>
+__global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, const float* __restrict__ table, int Hq, int Hkv, int N,
     int n_ktiles, float scale_log2, float scale) {
     constexpr bool ROPE = RM == ROT_QK;
+    constexpr int KW = 32 * RW;  // keys per workgroup
     typedef Wave<DT, D> W;
-    typedef Streamer<DT, D, ROPE> S;
+    typedef Streamer<DT, D, ROPE, 2 * RW> S;
     constexpr int TILE = BT * D;
     // Q0 dO0 Q1 dO1, then per buffer 64 scaled L and 64 Delta values
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
@@ -397,31 +405,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dk_role = wave >= RW;
     const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int bg, slot;
     decode(n_ktiles, bg, slot);
     const int kt = slot;  // heaviest first: key tile 0 sees every query
     const int b = bg / Hkv, g = bg % Hkv;
     const int group = Hq / Hkv;
-    const int kw0 = kt * BR + 32 * wave;
+    const int kw0 = kt * KW + 32 * (wave % RW);
     const int key = kw0 + n;
     const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
 
-    typename W::vec8 kf[W::QCH], vf[W::QCH];
-    W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
-    W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
-    f32x16 ak[W::DBLK], av[W::DBLK];
-#pragma unroll
-    for (int i = 0; i < W::DBLK; ++i) ak[i] = av[i] = f32x16{};
-
     // the query tiles of one head that see the workgroup's keys, all heads
-    const int t0 = (kt * BR) / BT;
+    const int t0 = (kt * KW) / BT;
     const int per_head = (N - 1) / BT + 1 - t0;
     const int steps = per_head * group;
     auto job = [&](int i, int& qh, int& tq) {
         qh = g * group + i / per_head;
         tq = t0 + i % per_head;
     };
+
     S st;
     auto start = [&](int i) {
         int qh, tq;
@@ -434,53 +437,70 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         st.issue_rows(rows_rsrc(lse + qhead, 1, tq, N), rows_rsrc(delta + qhead, 1, tq, N), wave,
                       lane);
     };
-    start(0);
-    for (int i = 0; i < steps; ++i) {
-        int qh, tq;
-        job(i, qh, tq);
-        uint16_t* Qs = smem + (i & 1) * 2 * TILE;
-        const uint16_t* dOs = Qs + TILE;
-        float* rl = rows_lds[i & 1];
-        wait_all_loads();
-        st.finish(Qs, rl, true, wave, lane);
-        __syncthreads();  // step i complete; the other buffers are no longer read
-        if (i + 1 < steps) start(i + 1);
-        const int q0 = tq * BT;
-        if (kw0 >= N) continue;              // the wave has no keys
-        if (q0 + BT - 1 < kw0) continue;     // every query of the tile precedes the wave's keys
-        const bool diag = q0 < kw0 + 31;
+
+    // The whole loop of one role (the same barriers in the same order for
+    // both, so the workgroup stays in step), compiled separately per role.
+    auto run = [&](auto dk_tag) {
+        constexpr bool DK = decltype(dk_tag)::value;
+        typename W::vec8 kf[W::QCH], vf[W::QCH];
+        W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
+        if (DK) W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
+        f32x16 acc[W::DBLK];  // dK^T (DK) or dV^T
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            // S and dP for queries q0 + 32qb .. +31 (lane column = key)
-            const f32x16 s = W::score(Qs, 32 * qb, kf, n, hh);
-            const f32x16 dp = W::score(dOs, 32 * qb, vf, n, hh);
-            f32x16 p, ds;
+        for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
+        start(0);
+        for (int i = 0; i < steps; ++i) {
+            int qh, tq;
+            job(i, qh, tq);
+            uint16_t* Qs = smem + (i & 1) * 2 * TILE;
+            const uint16_t* dOs = Qs + TILE;
+            float* rl = rows_lds[i & 1];
+            wait_all_loads();
+            st.finish(Qs, rl, true, wave, lane);
+            __syncthreads();  // step i complete; the other buffers are no longer read
+            if (i + 1 < steps) start(i + 1);
+            const int q0 = tq * BT;
+            if (kw0 >= N) continue;           // the wave has no keys
+            if (q0 + BT - 1 < kw0) continue;  // every query of the tile precedes the wave's keys
+            const bool diag = q0 < kw0 + 31;
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int r = 32 * qb + 8 * gq + 4 * hh;  // this lane's 4 query rows in the tile
-                const f32x4 lq = *reinterpret_cast<const f32x4*>(rl + r);
-                const f32x4 dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r);
+            for (int qb = 0; qb < 2; ++qb) {
+                // S (and for dK, dP) for queries q0 + 32qb .. +31 (lane column = key)
+                f32x16 x = W::score(Qs, 32 * qb, kf, n, hh);
+                f32x16 dp;
+                if (DK) dp = W::score(dOs, 32 * qb, vf, n, hh);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int j = 4 * gq + jj;
-                    const int qrow = q0 + r + jj;
-                    float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -lq[jj]));
-                    if ((diag && qrow < key) || qrow >= N) pj = 0.f;
-                    p[j] = pj;
-                    ds[j] = pj * (dp[j] - dq4[jj]);
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int r = 32 * qb + 8 * gq + 4 * hh;  // the lane's 4 query rows in the tile
+                    const f32x4 lq = *reinterpret_cast<const f32x4*>(rl + r);
+                    f32x4 dq4;
+                    if (DK) dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int j = 4 * gq + jj;
+                        const int qrow = q0 + r + jj;
+                        float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, -lq[jj]));
+                        if ((diag && qrow < key) || qrow >= N) pj = 0.f;
+                        x[j] = DK ? pj * (dp[j] - dq4[jj]) : pj;  // dS or P
+                    }
                 }
+                u32x4 y[2];
+                W::pack(x, y);
+                W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
             }
-            u32x4 yp[2], yd[2];
-            W::pack(p, yp);
-            W::pack(ds, yd);
-            W::pv(av, dOs, 32 * qb, yp, lane);
-            W::pv(ak, Qs, 32 * qb, yd, lane);
         }
-    }
-    if (key < N) {
-        W::write(ak, scale, dk + (kvhead + key) * D, ROPE ? table + (int64_t)key * D : nullptr, hh);
-        W::write(av, 1.f, dv + (kvhead + key) * D, nullptr, hh);
-    }
+        if (key < N) {
+            if (DK)
+                W::write(acc, scale, dk + (kvhead + key) * D,
+                         ROPE ? table + (int64_t)key * D : nullptr, hh);
+            else
+                W::write(acc, 1.f, dv + (kvhead + key) * D, nullptr, hh);
+        }
+    };
+    if (dk_role)
+        run(std::integral_constant<bool, true>());
+    else
+        run(std::integral_constant<bool, false>());
 }
 
 template <int DT, int D, int RM>
@@ -488,7 +508,11 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     const float scale = (float)(1.0 / sqrt((double)D));
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int n_qtiles = (a.N + BR - 1) / BR;
-    const int n_ktiles = (a.N + BR - 1) / BR;
+    // dK/dV pass: 128 keys per workgroup (8 waves), or 64 (4 waves) when that
+    // leaves fewer workgroups than CUs
+    const int64_t k_units_128 = (int64_t)((a.N + 127) / 128) * a.Hkv * a.B;
+    const int rw = k_units_128 >= 256 ? 4 : 2;
+    const int n_ktiles = (a.N + 32 * rw - 1) / (32 * rw);
     const int64_t q_units = (int64_t)n_qtiles * a.Hq * a.B;
     const int64_t k_units = (int64_t)n_ktiles * a.Hkv * a.B;
     if (q_units > 0x7fffffff || k_units > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -503,9 +527,14 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
         a.N, n_qtiles, scale_log2, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_bwd_dkdv_kernel<DT, D, RM><<<dim3((unsigned)k_units), 256, 0, stream>>>(
-        q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv),
-        a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+    if (rw == 4)
+        attn_bwd_dkdv_kernel<DT, D, RM, 4><<<dim3((unsigned)k_units), 512, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
+            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+    else
+        attn_bwd_dkdv_kernel<DT, D, RM, 2><<<dim3((unsigned)k_units), 256, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
+            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
     return hipGetLastError();
 }
 

@@ -157,12 +157,13 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
 /*
  * Dispatcher: out/lse of attn_rope_causal_fwd (bit-identical: every path hands
  * the same rotated operands to the same attention arithmetic), computed by the
- * path measured fastest on MI355X for this shape -- pre-rotation of Q and K
- * for short sequences, the split path for long ones, never the fused kernel
- * when a workspace is given (rotating every key tile in the kernel cost
- * 28-43 % over plain attention, more than the streaming pass). The choice of
- * pre-rotation versus in-kernel rotation is the one the AttnFuse report,
- * paragraphs 3 and 5, says depends on the GPU and the shape.
+ * path measured fastest on MI355X for this shape -- with GQA the split path
+ * at every length; with MHA pre-rotation of Q and K up to N = 6144 and the
+ * split path beyond -- never the fused kernel when a workspace is given
+ * (rotating every key tile in the kernel cost 16-43 % over plain attention,
+ * more than the streaming pass). The choice of pre-rotation versus in-kernel
+ * rotation is the one the AttnFuse report, paragraphs 3 and 5, says depends
+ * on the GPU and the shape.
  *
  * workspace: caller-owned device memory for the rotated copies (Q' and K',
  * or K' alone), 16-byte aligned, not overlapping any tensor argument; the

@@ -45,7 +45,11 @@
 //     the same work, so a grid of one workgroup per CU finishes together.
 //   * attn_fwd_kernel: one 4-wave workgroup per query tile, heaviest first;
 //     used when there are too few tile pairs to fill the chip.
-//   Both use a 1-D grid whose consecutive workgroups on one XCD (the hardware
+//   * attn_pair_heads_kernel: an 8-wave workgroup takes the 64-row query
+//     tiles T-1-p and p of two query heads of one GQA group (heavy rows on
+//     waves 0-3, light rows on waves 4-7); all four row blocks share every key
+//     tile. Chosen only when forced (RAC_ATTN_SHAPE=pairheads).
+//   All use a 1-D grid whose consecutive workgroups on one XCD (the hardware
 //   deals workgroup ids round-robin over 8 XCDs) share a key/value head, so
 //   each XCD's L2 serves one K/V head to all its readers.
 #include <math.h>
@@ -515,6 +519,75 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
 }
 
 // ---------------------------------------------------------------------------
+// Paired query tiles of two GQA heads: one 8-wave workgroup takes the 64-row
+// query tiles T-1-p (heavy) and p (light) of two query heads of one GQA
+// group. Waves 0-3 hold the heavy tile's rows (2 waves per head), waves 4-7
+// the light tile's, so each SIMD (waves w and w + 4) runs one heavy and one
+// light wave and every workgroup does the same work. All four row blocks read
+// the same key/value tiles: each tile is loaded (and, with RoPE, rotated)
+// once for 256 query rows while the light rows are still active, and the
+// causal imbalance needs no merge of partial results.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int RM>
+__global__ __launch_bounds__(512, 1) void attn_pair_heads_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ table, int Hq, int Hkv, int N, int n_tiles64, int n_pairs,
+    float scale_log2) {
+    typedef Tile<D> T;
+    typedef WaveAttn<DT, D, RM, 1, 8> W;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+
+    const Unit un = decode_unit(Hq, Hkv, n_pairs, 2);
+    const int t_heavy = n_tiles64 - 1 - un.idx;
+    const int t_light = un.idx < t_heavy ? un.idx : -1;  // none for the middle tile of an odd count
+    const int tile = wave < 4 ? t_heavy : t_light;
+    const int qw0 = tile * 64 + 32 * (wave & 1);  // the wave's first row
+    const int64_t q_head = ((int64_t)un.b * Hq + un.h + ((wave >> 1) & 1)) * N;
+    const int64_t kv_head = ((int64_t)un.b * Hkv + un.g) * N;
+    const uint16_t* kbase = k + kv_head * D;
+    const uint16_t* vbase = v + kv_head * D;
+
+    W st;
+    const bool has_rows = tile >= 0 && qw0 < N;
+    if (has_rows) st.load_q(q + q_head * D, table, qw0, N, n, hh);
+    st.reset();
+
+    const int n_tiles = (min(t_heavy * 64 + 64, N) - 1) / BN + 1;
+    const int wave_tiles = has_rows ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
+
+    typename W::Stage stage;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
+    stage.issue(smem, tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
+    for (int t = 0; t < n_tiles; ++t) {
+        uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
+        wait_all_loads();              // this wave's part of tile t has landed
+        stage.rotate(Ks, uwave, lane);  // RoPE on the K chunks this thread loaded
+        __syncthreads();               // tile t complete; the other buffer is no longer read
+        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS,
+                             tile_rsrc<D>(kbase, vbase, table, t + 1, N), uwave, lane};
+        if (t < wave_tiles) {
+            if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
+                st.template step<true>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
+            else
+                st.template step<false>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
+        } else if (next.active) {
+            stage.issue(next.buf, next.rs, uwave, lane);
+        }
+    }
+    if (wave_tiles == 0) return;
+    const int row = qw0 + n;
+    const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
+    if (row < N) st.write(0, out + (q_head + row) * D, lse ? lse + q_head + row : nullptr, l_tot, hh);
+}
+
+// ---------------------------------------------------------------------------
 // Paired, split, load-balanced launch: two halves of 4 / QB waves each.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int RM, int QB>
@@ -695,9 +768,26 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     // workgroups per CU; with more, the heaviest-first tile launch balances as
     // well and keeps more workgroups resident per CU.
     bool pair = tile_units < 4 * NUM_CUS && pair_units >= NUM_CUS / 2 && n_qtiles >= 2;
+    const bool heads_ok = (a.Hq / a.Hkv) % 2 == 0;
+    // pair_heads (two GQA heads sharing every key tile) only when forced: with
+    // K rotated in the kernel it beat the split pair by 3.5 % at N = 2048
+    // (0.0616 vs 0.0638 ms), without rotation it lost (0.0512 vs 0.0448 ms),
+    // and the automatic choice must not depend on the rotation mode: every
+    // path then runs the same attention arithmetic on the same rotated
+    // operands, so the paths agree bit for bit.
+    bool pair_heads = false;
     if (a.shape == ATTN_SHAPE_PAIR) pair = true;
-    if (a.shape == ATTN_SHAPE_TILE) pair = false;
-    if (pair) {
+    if (a.shape == ATTN_SHAPE_TILE) pair = false, pair_heads = false;
+    if (a.shape == ATTN_SHAPE_PAIR_HEADS && heads_ok) pair = false, pair_heads = true;
+    if (pair_heads) {
+        const int n_t64 = (a.N + 63) / 64;
+        const int n_pairs64 = (n_t64 + 1) / 2;
+        const int64_t units = (int64_t)n_pairs64 * (a.Hq / 2) * a.B;
+        attn_pair_heads_kernel<DT, D, RM><<<dim3((unsigned)units), 512, 0, stream>>>(
+            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
+            a.Hq, a.Hkv, a.N, n_t64, n_pairs64, scale_log2);
+    } else if (pair) {
         attn_pair_kernel<DT, D, RM, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,

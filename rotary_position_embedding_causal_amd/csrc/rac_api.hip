@@ -163,12 +163,13 @@ int check_pass_ptrs(const void* x, const void* y, const void* x_out, const void*
     return RAC_OK;
 }
 
-// RAC_ATTN_SHAPE=pair|tile forces the attention launch shape (default: by size).
+// RAC_ATTN_SHAPE=pair|tile|pairheads forces the attention launch shape (default: by size).
 int attn_shape_from_env() {
     const char* e = getenv("RAC_ATTN_SHAPE");
     if (!e) return rac::ATTN_SHAPE_AUTO;
     if (!strcmp(e, "pair")) return rac::ATTN_SHAPE_PAIR;
     if (!strcmp(e, "tile")) return rac::ATTN_SHAPE_TILE;
+    if (!strcmp(e, "pairheads")) return rac::ATTN_SHAPE_PAIR_HEADS;
     return rac::ATTN_SHAPE_AUTO;
 }
 
@@ -176,14 +177,15 @@ int attn_shape_from_env() {
 //
 // All three paths give bit-identical results (they hand the same rotated
 // operands to the same attention arithmetic), so the choice is about time
-// only. Measured on MI355X (bench crossover rows, bf16 D=128 GQA 4:1 at
-// N = 2048 / 4096 (B=4) / 8192 and fp16 D=64 MHA at N = 2048 .. 32768): the
-// fused kernel was never the fastest -- rotating every K tile in the kernel
-// costs 28-43 % over plain attention, more than the streaming pass costs at
-// 8 TB/s; pre-rotation of Q and K was fastest up to N = 2048 (GQA) and
-// N = 6144 (MHA); the split path (K pre-rotated, Q rotated in the kernel) was
-// fastest beyond, where the in-kernel Q rotation is amortised over more key
-// tiles and moving Q through the pass costs more.
+// only. Measured on MI355X (bench crossover rows, median of 15 calls after a
+// 50 ms warm-up; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) / 8192 and fp16
+// D=64 MHA at N = 2048 .. 32768): the fused kernel was never the fastest --
+// rotating every K tile in the kernel costs 16-43 % over plain attention,
+// more than the streaming pass costs; with GQA the split path (K pre-rotated,
+// Q rotated once per row in the kernel) was fastest at every N, by 1-5 % over
+// pre-rotation of Q and K; with MHA pre-rotation was fastest up to N = 6144
+// and the split path from N = 8192, where the in-kernel Q rotation is
+// amortised over more key tiles.
 size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
     const size_t q = (size_t)B * Hq * N * D * 2, k = (size_t)B * Hkv * N * D * 2;
     const size_t q16 = (q + 255) & ~(size_t)255;  // K' starts 256-byte aligned
@@ -193,7 +195,7 @@ size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
 }
 
 int preferred_path(int Hq, int Hkv, int N) {
-    const int n_split = Hq / Hkv >= 2 ? 3072 : 7168;  // between the measured crossings
+    const int n_split = Hq / Hkv >= 2 ? 0 : 7168;  // MHA: between the measured crossings
     return N >= n_split ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
 }
 

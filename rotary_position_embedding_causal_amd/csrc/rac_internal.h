@@ -9,7 +9,7 @@ namespace rac {
 
 // Launch shape of the attention kernels: chosen from the problem size, or
 // forced (tests cover both shapes on small problems; tuning).
-enum { ATTN_SHAPE_AUTO = 0, ATTN_SHAPE_PAIR = 1, ATTN_SHAPE_TILE = 2 };
+enum { ATTN_SHAPE_AUTO = 0, ATTN_SHAPE_PAIR = 1, ATTN_SHAPE_TILE = 2, ATTN_SHAPE_PAIR_HEADS = 3 };
 
 struct AttnArgs {
     const void* q;

@@ -193,19 +193,19 @@ def test_dispatcher_workspace_rules():
 
 def test_auto_plan_paths():
     B, Hq, Hkv, D = 1, 32, 8, 128
-    for N in (1, 512, 2048):
-        path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 40)
-        assert path == rac.RAC_PATH_PREROTATE
-        q = B * Hq * N * D * 2
-        assert need == ((q + 255) // 256) * 256 + B * Hkv * N * D * 2
-        # too small for Q' and K': K' alone (split), then nothing (fused)
-        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_SPLIT
-        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, B * Hkv * N * D * 2 - 1)[0] == rac.RAC_PATH_FUSED
-        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
-    for N in (4096, 8192):
+    # GQA: the split path (K' only) at every length, else the fused kernel
+    for N in (1, 512, 2048, 4096, 8192):
         path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 40)
         assert path == rac.RAC_PATH_SPLIT and need == B * Hkv * N * D * 2
         assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_FUSED
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
+    # MHA short sequences: Q' and K' (pre-rotation); too small for both: K' alone, then none
+    H, N = 16, 2048
+    path, need = rac.auto_plan(B, H, H, N, 64, rac.RAC_FP16, 1 << 40)
+    q = B * H * N * 64 * 2
+    assert path == rac.RAC_PATH_PREROTATE and need == ((q + 255) // 256) * 256 + q
+    assert rac.auto_plan(B, H, H, N, 64, 1, need - 1)[0] == rac.RAC_PATH_SPLIT
+    assert rac.auto_plan(B, H, H, N, 64, 1, q - 1)[0] == rac.RAC_PATH_FUSED
     # MHA: pre-rotation up to 6144, the split path from 8192
     assert rac.auto_plan(1, 16, 16, 6144, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_PREROTATE
     assert rac.auto_plan(1, 16, 16, 8192, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_SPLIT

@@ -31,7 +31,7 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["auto", "pair", "tile"])
+@pytest.fixture(params=["auto", "pair", "tile", "pairheads"])
 def launch_shape(request, monkeypatch):
     """Runs a test under each attention launch shape (RAC_ATTN_SHAPE)."""
     monkeypatch.setenv("RAC_ATTN_SHAPE", request.param)

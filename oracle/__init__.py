@@ -56,6 +56,8 @@ class Oracle:
         lib.oracle_rope.argtypes = [f64p, i64p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                     f64p]
         lib.oracle_rope.restype = None
+        lib.oracle_rope_half.argtypes = lib.oracle_rope.argtypes
+        lib.oracle_rope_half.restype = None
         lib.oracle_attn_rows.argtypes = [f64p, f64p, f64p] + [ctypes.c_int] * 5 + [
             i64p, ctypes.c_int64, f64p, f64p]
         lib.oracle_attn_rows.restype = ctypes.c_int
@@ -86,10 +88,11 @@ class Oracle:
                                _ptr(out, ctypes.c_uint16))
         return out
 
-    def rope(self, x: np.ndarray, positions, base: float) -> np.ndarray:
+    def rope(self, x: np.ndarray, positions, base: float, pairing: str = "adjacent") -> np.ndarray:
         """Rotate rows of ``x`` (shape [..., D], fp64) by their absolute positions.
 
-        ``positions`` broadcasts against ``x.shape[:-1]``.
+        ``positions`` broadcasts against ``x.shape[:-1]``. ``pairing`` is
+        "adjacent" (pairs (2i, 2i+1)) or "half" (pairs (i, i + D/2)).
         """
         a = np.ascontiguousarray(x, dtype=np.float64)
         D = a.shape[-1]
@@ -99,13 +102,14 @@ class Oracle:
                                                    a.shape[:-1]))
         out = np.empty_like(a)
         rows = a.size // D if D else 0
-        self.lib.oracle_rope(_ptr(a, ctypes.c_double), _ptr(pos, ctypes.c_int64), rows, D,
-                             float(base), _ptr(out, ctypes.c_double))
+        fn = {"adjacent": self.lib.oracle_rope, "half": self.lib.oracle_rope_half}[pairing]
+        fn(_ptr(a, ctypes.c_double), _ptr(pos, ctypes.c_int64), rows, D, float(base),
+           _ptr(out, ctypes.c_double))
         return out
 
-    def rope_bhnd(self, x: np.ndarray, base: float) -> np.ndarray:
+    def rope_bhnd(self, x: np.ndarray, base: float, pairing: str = "adjacent") -> np.ndarray:
         """RoPE on a [B, H, N, D] tensor: row n of every (b, h) sits at position n."""
-        return self.rope(x, np.arange(x.shape[-2], dtype=np.int64), base)
+        return self.rope(x, np.arange(x.shape[-2], dtype=np.int64), base, pairing)
 
     def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, rows=None):
         """Causal softmax attention, fp64, two-pass.
@@ -139,7 +143,7 @@ class Oracle:
         return o, lse
 
     def rope_attention(self, q_bits, k_bits, v_bits, dtype: str, base: float, rows=None,
-                       variant: str = "rounded"):
+                       variant: str = "rounded", pairing: str = "adjacent"):
         """RoPE then causal attention, from bf16/fp16 bit patterns.
 
         ``variant="exact"`` feeds the fp64 rotation straight into attention;
@@ -149,8 +153,8 @@ class Oracle:
         q = self.decode(q_bits, dtype)
         k = self.decode(k_bits, dtype)
         v = self.decode(v_bits, dtype)
-        qr = self.rope_bhnd(q, base)
-        kr = self.rope_bhnd(k, base)
+        qr = self.rope_bhnd(q, base, pairing)
+        kr = self.rope_bhnd(k, base, pairing)
         if variant == "rounded":
             qr = self.decode(self.encode(qr, dtype), dtype)
             kr = self.decode(self.encode(kr, dtype), dtype)
@@ -240,20 +244,21 @@ def encode(x, dtype):
     return default().encode(x, dtype)
 
 
-def rope(x, positions, base):
-    return default().rope(x, positions, base)
+def rope(x, positions, base, pairing="adjacent"):
+    return default().rope(x, positions, base, pairing)
 
 
-def rope_bhnd(x, base):
-    return default().rope_bhnd(x, base)
+def rope_bhnd(x, base, pairing="adjacent"):
+    return default().rope_bhnd(x, base, pairing)
 
 
 def attention(q, k, v, rows=None):
     return default().attention(q, k, v, rows)
 
 
-def rope_attention(q_bits, k_bits, v_bits, dtype, base, rows=None, variant="rounded"):
-    return default().rope_attention(q_bits, k_bits, v_bits, dtype, base, rows, variant)
+def rope_attention(q_bits, k_bits, v_bits, dtype, base, rows=None, variant="rounded",
+                   pairing="adjacent"):
+    return default().rope_attention(q_bits, k_bits, v_bits, dtype, base, rows, variant, pairing)
 
 
 def attention_bwd(q, k, v, dout):

@@ -19,7 +19,8 @@
  *   clockwise by p*theta_i:
  *       x' = x cos(p theta_i) - y sin(p theta_i)
  *       y' = x sin(p theta_i) + y cos(p theta_i)
- *   Values are not rotated.
+ *   Values are not rotated. A second pairing, the half-split (x_i, x_{i+D/2})
+ *   used by many checkpoints ("rotate_half"), is provided as its own routine.
  *
  *   Causal attention. Same digest, background section "FlashAttention and
  *   online softmax" and its method section (forward, Algorithm 1): scores
@@ -153,6 +154,28 @@ void oracle_rope(const double* x, const int64_t* pos, int64_t rows, int D,
             double x0 = xr[2 * i], x1 = xr[2 * i + 1];
             yr[2 * i] = x0 * c - x1 * s;
             yr[2 * i + 1] = x0 * s + x1 * c;
+        }
+    }
+}
+
+/* The half-split pairing (the "rotate_half" convention): pair i is
+ * (x_i, x_{i+D/2}) instead of (x_2i, x_2i+1), same frequency theta_i and the
+ * same counter-clockwise turn by p*theta_i. out may equal x. */
+void oracle_rope_half(const double* x, const int64_t* pos, int64_t rows, int D,
+                      double base, double* out) {
+    const double log_base = log(base);
+    const int half = D / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * D;
+        double* yr = out + r * D;
+        for (int i = 0; i < half; ++i) {
+            const double freq = exp(-(2.0 * i / D) * log_base);
+            const double turn = (double)pos[r] * freq;
+            const double cs = cos(turn), sn = sin(turn);
+            double a = xr[i], b = xr[i + half];
+            yr[i] = a * cs - b * sn;
+            yr[i + half] = a * sn + b * cs;
         }
     }
 }

@@ -481,4 +481,55 @@ def pin_rope_attention_bwd_finite_differences(orc):
             assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
 
 
+# --------------------------------------------------------------------------
+# RoPE, half-split pairing (i, i + D/2)
+# --------------------------------------------------------------------------
+
+def pin_rope_half_complex_form(orc):
+    # pair i is the complex number x_i + 1j*x_{i+D/2}, turned by p * base**(-2i/D)
+    rng = _rng(23)
+    for D in (2, 8, 64, 128):
+        for base in (10000.0, 500000.0):
+            x = rng.standard_normal((40, D))
+            pos = np.concatenate([np.arange(8), rng.integers(0, 32768, 32)])
+            freq = np.power(base, -np.arange(0, D, 2, dtype=np.float64) / D)
+            z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * np.exp(1j * pos[:, None] * freq)
+            ref = np.concatenate([z.real, z.imag], axis=1)
+            got = orc.rope(x, pos, base, "half")
+            assert np.max(np.abs(got - ref)) < 1e-10, (D, base)
+
+
+def pin_rope_half_is_permuted_adjacent(orc):
+    # interleaving the two halves turns pairs (i, i+D/2) into (2i, 2i+1)
+    rng = _rng(24)
+    D = 128
+    x = rng.standard_normal((30, D))
+    pos = rng.integers(0, 32768, 30)
+    perm = np.empty(D, dtype=np.int64)
+    perm[0::2] = np.arange(D // 2)
+    perm[1::2] = np.arange(D // 2) + D // 2
+    inv = np.argsort(perm)
+    via_adjacent = orc.rope(x[:, perm], pos, 500000.0)[:, inv]
+    assert np.max(np.abs(orc.rope(x, pos, 500000.0, "half") - via_adjacent)) < 1e-13
+
+
+def pin_rope_half_invariants(orc):
+    rng = _rng(25)
+    D = 64
+    x = rng.standard_normal((16, D))
+    assert np.array_equal(orc.rope(x, np.zeros(16, np.int64), 10000.0, "half"), x)
+    pos = rng.integers(0, 32768, 16)
+    y = orc.rope(x, pos, 10000.0, "half")
+    nx = np.hypot(x[:, :D // 2], x[:, D // 2:])
+    ny = np.hypot(y[:, :D // 2], y[:, D // 2:])
+    assert np.max(np.abs(ny - nx) / nx) < 1e-14
+    # dot products after rotation depend only on the position difference
+    q, k = rng.standard_normal((2, D))
+    scale = np.linalg.norm(q) * np.linalg.norm(k)
+    for m, n, t in ((5, 3, 1000), (100, 7, 16000), (0, 0, 16384)):
+        a = orc.rope(q, m, 10000.0, "half") @ orc.rope(k, n, 10000.0, "half")
+        b = orc.rope(q, m + t, 10000.0, "half") @ orc.rope(k, n + t, 10000.0, "half")
+        assert abs(a - b) / scale < 1e-11
+
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

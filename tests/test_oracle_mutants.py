@@ -43,6 +43,13 @@ MUTANTS = {
     "bwd_dv_uses_ds": ("dvj[d] += p * doi[d];", "dvj[d] += ds * doi[d];"),
     "bwd_key_pass_strict": ("for (int64_t i = j; i < N; ++i) {", "for (int64_t i = j + 1; i < N; ++i) {"),
     "bwd_delta_drops_p": ("dl += exp(s[j] - L) * dp;", "dl += dp;"),
+    "half_rotation_sign": ("yr[i] = a * cs - b * sn;", "yr[i] = a * cs + b * sn;"),
+    "half_partner_index": ("double a = xr[i], b = xr[i + half];",
+                           "double a = xr[i], b = xr[half - 1 - i + half];"),
+    "half_frequency_index": ("const double freq = exp(-(2.0 * i / D) * log_base);",
+                             "const double freq = exp(-(2.0 * (half - 1 - i) / D) * log_base);"),
+    "half_direction": ("const double cs = cos(turn), sn = sin(turn);",
+                       "const double cs = cos(turn), sn = -sin(turn);"),
     "bwd_scale_one_over_d": ("pow((double)D, -0.5)", "pow((double)D, -1.0)"),
     "bwd_gqa_modulo": ("const int64_t kv_head = b * Hkv + h / group;",
                        "const int64_t kv_head = b * Hkv + h % Hkv;"),

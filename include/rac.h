@@ -152,6 +152,33 @@ int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void
                            float* lse, int B, int Hq, int Hkv, int N, int D,
                            double rope_base, int dtype, void* stream);
 
+enum { RAC_PAIR_ADJACENT = 0, RAC_PAIR_HALF = 1 };
+
+/*
+ * RoPE with a choice of which coordinates turn together (`pairing`):
+ *   RAC_PAIR_ADJACENT  (2i, 2i+1), the pairing of every other entry point;
+ *   RAC_PAIR_HALF      (i, i + D/2), the "rotate half" layout;
+ * both with pair i turned by n * theta_i, theta_i = rope_base^(-2i/D),
+ * 0 <= i < D/2, and the same fp32 arithmetic and rounding. The background on
+ * RoPE in "Fast and Exact Relative-Position Attention via Structure-Aware
+ * Kernels" (rainbus digest) fixes the rotation by absolute position but not
+ * the pairing; the two give different results for the same inputs, so both
+ * are offered.
+ *
+ * rope_prerotate_ex and attn_rope_causal_fwd_ex are rope_prerotate and
+ * attn_rope_causal_fwd with that argument; with RAC_PAIR_ADJACENT they give
+ * exactly those functions' results. For either pairing,
+ * attn_causal_fwd(rope_prerotate_ex(q, k)) equals attn_rope_causal_fwd_ex
+ * bit for bit. Any other value of `pairing` is RAC_ERR_ARG. Same layouts,
+ * limits and rules as the functions they extend.
+ */
+int rope_prerotate_ex(const void* q, const void* k, void* q_rot, void* k_rot,
+                      int B, int Hq, int Hkv, int N, int D, double rope_base,
+                      int pairing, int dtype, void* stream);
+int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int N, int D, double rope_base,
+                            int pairing, int dtype, void* stream);
+
 enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
 
 /*

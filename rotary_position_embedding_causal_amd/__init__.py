@@ -36,7 +36,10 @@ RAC_MAX_N = 1 << 22
 EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_prerotate_k",
             "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
+            "rope_prerotate_ex", "attn_rope_causal_fwd_ex",
             "rac_last_error", "rac_release_tables")
+RAC_PAIR_ADJACENT, RAC_PAIR_HALF = 0, 1
+PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF}
 RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
 PATH_NAMES = {RAC_PATH_FUSED: "fused", RAC_PATH_PREROTATE: "prerotate", RAC_PATH_SPLIT: "split"}
 
@@ -80,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.attn_causal_bwd.restype = i
     L.rope_prerotate_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp]
     L.rope_prerotate_bwd.restype = i
+    L.rope_prerotate_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp]
+    L.rope_prerotate_ex.restype = i
+    L.attn_rope_causal_fwd_ex.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, i, vp]
+    L.attn_rope_causal_fwd_ex.restype = i
     L.rac_last_error.argtypes = []
     L.rac_last_error.restype = ctypes.c_char_p
     L.rac_release_tables.argtypes = []
@@ -151,6 +158,15 @@ def _outputs(q, out, lse, want_lse):
     return out, lse
 
 
+def _pairing(pairing) -> int:
+    """RAC_PAIR_* from a name ("adjacent", "half") or the integer itself."""
+    if isinstance(pairing, str):
+        if pairing not in PAIRINGS:
+            raise ValueError("pairing must be one of %s" % sorted(PAIRINGS))
+        return PAIRINGS[pairing]
+    return int(pairing)
+
+
 def attn_rope_causal_fwd(q, k, v, rope_base: float, out=None, lse=None, want_lse: bool = True):
     """Fused path: RoPE on Q/K inside the causal attention kernel. Returns (out, lse)."""
     B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
@@ -163,19 +179,49 @@ def attn_rope_causal_fwd(q, k, v, rope_base: float, out=None, lse=None, want_lse
     return out, lse
 
 
-def rope_prerotate(q, k, rope_base: float, q_rot=None, k_rot=None):
-    """Pre-rotation pass. Returns (q_rot, k_rot); pass q_rot=q, k_rot=k for in place."""
-    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, None)
+def attn_rope_causal_fwd_ex(q, k, v, rope_base: float, pairing="adjacent", out=None, lse=None,
+                            want_lse: bool = True):
+    """The fused path with a choice of RoPE pairing ("adjacent" or "half"). Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           B, Hq, Hkv, N, D, float(rope_base), _pairing(pairing),
+                                           dt, _stream(q.device))
+    check(rc, "attn_rope_causal_fwd_ex")
+    return out, lse
+
+
+def _rot_outputs(q, k, q_rot, k_rot):
     q_rot = torch.empty_like(q) if q_rot is None else q_rot
     k_rot = torch.empty_like(k) if k_rot is None else k_rot
     for src, dst in ((q, q_rot), (k, k_rot)):
         if dst.shape != src.shape or dst.dtype != src.dtype or not dst.is_contiguous() \
                 or dst.device != src.device:
             raise ValueError("q_rot/k_rot must be contiguous tensors like q/k")
+    return q_rot, k_rot
+
+
+def rope_prerotate(q, k, rope_base: float, q_rot=None, k_rot=None):
+    """Pre-rotation pass. Returns (q_rot, k_rot); pass q_rot=q, k_rot=k for in place."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, None)
+    q_rot, k_rot = _rot_outputs(q, k, q_rot, k_rot)
     with torch.cuda.device(q.device):
         rc = lib().rope_prerotate(_ptr(q), _ptr(k), _ptr(q_rot), _ptr(k_rot), B, Hq, Hkv, N, D,
                                   float(rope_base), dt, _stream(q.device))
     check(rc, "rope_prerotate")
+    return q_rot, k_rot
+
+
+def rope_prerotate_ex(q, k, rope_base: float, pairing="adjacent", q_rot=None, k_rot=None):
+    """The pre-rotation pass with a choice of RoPE pairing. Returns (q_rot, k_rot)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, None)
+    q_rot, k_rot = _rot_outputs(q, k, q_rot, k_rot)
+    with torch.cuda.device(q.device):
+        rc = lib().rope_prerotate_ex(_ptr(q), _ptr(k), _ptr(q_rot), _ptr(k_rot), B, Hq, Hkv, N,
+                                     D, float(rope_base), _pairing(pairing), dt,
+                                     _stream(q.device))
+    check(rc, "rope_prerotate_ex")
     return q_rot, k_rot
 
 
@@ -190,9 +236,12 @@ def attn_causal_fwd(q, k, v, out=None, lse=None, want_lse: bool = True):
     return out, lse
 
 
-def prerotate_path(q, k, v, rope_base: float, want_lse: bool = True):
+def prerotate_path(q, k, v, rope_base: float, want_lse: bool = True, pairing="adjacent"):
     """The pre-rotation path: rope_prerotate then attn_causal_fwd. Returns (out, lse)."""
-    q_rot, k_rot = rope_prerotate(q, k, rope_base)
+    if _pairing(pairing) == RAC_PAIR_ADJACENT:
+        q_rot, k_rot = rope_prerotate(q, k, rope_base)
+    else:
+        q_rot, k_rot = rope_prerotate_ex(q, k, rope_base, pairing)
     return attn_causal_fwd(q_rot, k_rot, v, want_lse=want_lse)
 
 

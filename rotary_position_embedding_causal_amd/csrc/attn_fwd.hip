@@ -1,6 +1,7 @@
 // attn_fwd.hip -- causal MHA/GQA attention forward for gfx950, with RoPE fused
-// into the loads of both Q and K (RM = ROT_QK), of Q only (RM = ROT_Q: the
-// GQA split path, K rotated beforehand) or of neither (RM = ROT_NONE).
+// into the loads of both Q and K (RM = ROT_QK, or ROT_QK_HALF for the
+// half-split pairing), of Q only (RM = ROT_Q: the GQA split path, K rotated
+// beforehand) or of neither (RM = ROT_NONE).
 //
 // Method: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (rainbus digest), background "FlashAttention and online softmax"
@@ -138,7 +139,13 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const uint16_t* kbase, const uint1
 // With ROPE the K chunks land unrotated; each thread prefetches the cos/sin
 // entries of the chunks it loaded and, once its loads have landed, rotates
 // those chunks in place before the block's barrier.
-template <int DT, int D, bool ROPE, int NW>
+// ROPE: 0 = K not rotated, 1 = adjacent pairs (2i, 2i+1), 2 = half-split
+// pairs (d, d + D/2). With the half-split pairing a chunk's partner (same row,
+// logical chunk XOR D/16) lands in the same 1 KiB block, loaded by lane
+// XOR D/16 of the same instruction; each of the two lanes prefetches half of
+// the pair's 16 table floats, they swap halves, and each rotates its own chunk
+// from both chunks in LDS.
+template <int DT, int D, int ROPE, int NW>
 struct TileStage {
     typedef Tile<D> T;
     static constexpr int INSTR = BN * T::CH / (64 * NW);  // 1 KiB blocks per wave and tensor
@@ -153,17 +160,22 @@ struct TileStage {
         const int g = blk * 64 + lane;          // chunk index inside the tile
         const int row = g / T::CH;
         const int pc = g % T::CH;               // physical chunk position
-        const int kel = row * D + 8 * (pc ^ kswz<D>(row));  // element offsets in the tile
+        const int lc = pc ^ kswz<D>(row);       // logical chunk
+        const int kel = row * D + 8 * lc;       // element offsets in the tile
         const int vel = row * D + 8 * (pc ^ vswz<D>(row));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void*)(buf + blk * 512), 16, kel * 2,
                                                  0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(buf + T::K_ELEMS + blk * 512),
                                                  16, vel * 2, 0, 0, 0);
         if (ROPE) {
+            // adjacent: the 8 floats of this chunk's 4 pairs; half-split: this
+            // lane's half (8 floats) of the 16 of frequencies 8 (lc mod CH/2) ..
+            const int tel = ROPE == 1 ? kel
+                                      : row * D + 16 * (lc % (T::CH / 2)) + 8 * (lc / (T::CH / 2));
             cs[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rs.t, kel * 4, 0, 0));
+                                                     rs.t, tel * 4, 0, 0));
             cs[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rs.t, kel * 4 + 16, 0, 0));
+                                                     rs.t, tel * 4 + 16, 0, 0));
         }
     }
 
@@ -175,11 +187,32 @@ struct TileStage {
     // ROPE only: rotate the K chunks this thread loaded. Call after its loads
     // have completed (s_waitcnt) and before the block's barrier.
     __device__ __forceinline__ void rotate(uint16_t* buf, int wave, int lane) {
-        if (!ROPE) return;
+        if (ROPE == 0) return;
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) {
-            u32x4* p = reinterpret_cast<u32x4*>(buf + (wave * INSTR + j) * 512 + lane * 8);
-            *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
+            const int blk = wave * INSTR + j;
+            u32x4* p = reinterpret_cast<u32x4*>(buf + blk * 512 + lane * 8);
+            if (ROPE == 1) {
+                *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
+            } else {
+                constexpr int X = T::CH / 2;  // partner lane / chunk offset
+                const int g = blk * 64 + lane;
+                const bool lo = ((g % T::CH) ^ kswz<D>(g / T::CH)) < X;
+                f32x4 other[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        other[h][e] = __shfl_xor(cs[j][h][e], X);
+                const f32x4 tab[4] = {lo ? cs[j][0] : other[0], lo ? cs[j][1] : other[1],
+                                      lo ? other[0] : cs[j][0], lo ? other[1] : cs[j][1]};
+                const u32x4 own = *p;
+                const u32x4 partner =
+                    *reinterpret_cast<const u32x4*>(buf + blk * 512 + (lane ^ X) * 8);
+                u32x4 a, b;
+                rope_rotate_half8<DT>(lo ? own : partner, lo ? partner : own, tab, a, b);
+                *p = lo ? a : b;
+            }
         }
     }
 };
@@ -206,7 +239,9 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 template <int DT, int D, int RM, int QB, int NW = 4 / QB>
 struct WaveAttn {
     static constexpr bool ROPE_Q = RM != ROT_NONE;  // rotate Q rows when loading them
-    static constexpr bool ROPE_K = RM == ROT_QK;    // rotate every K tile in LDS
+    static constexpr bool HALF = RM == ROT_QK_HALF;  // half-split pairs (d, d + D/2)
+    // rotate every K tile in LDS: 0 no, 1 adjacent pairs, 2 half-split pairs
+    static constexpr int ROPE_K = RM == ROT_QK ? 1 : (RM == ROT_QK_HALF ? 2 : 0);
     typedef Fmt<DT> F;
     typedef typename F::vec8 vec8;
     typedef Tile<D> T;
@@ -241,20 +276,36 @@ struct WaveAttn {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             const int row = q_first + 32 * b + n;
+            u32x4 w[QCH];
 #pragma unroll
             for (int c = 0; c < QCH; ++c) {
-                u32x4 w = {0u, 0u, 0u, 0u};
+                w[c] = u32x4{0u, 0u, 0u, 0u};
                 if (row < N) {
                     const int d0 = 16 * c + 8 * hh;
-                    w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)row * D + d0);
-                    if (ROPE_Q) {
+                    w[c] = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)row * D + d0);
+                    if (ROPE_Q && !HALF) {
                         const f32x4* t =
                             reinterpret_cast<const f32x4*>(table + (int64_t)row * D + d0);
-                        w = rope_rotate8<DT>(w, t[0], t[1]);
+                        w[c] = rope_rotate8<DT>(w[c], t[0], t[1]);
                     }
                 }
-                qf[b][c] = as_vec8<DT>(w);
             }
+            if (HALF && row < N) {
+                // chunk d0 of the first half pairs with chunk d0 + D/2 = step c + QCH/2
+#pragma unroll
+                for (int c = 0; c < QCH / 2; ++c) {
+                    const int d0 = 16 * c + 8 * hh;
+                    const f32x4* t =
+                        reinterpret_cast<const f32x4*>(table + (int64_t)row * D + 2 * d0);
+                    const f32x4 tab[4] = {t[0], t[1], t[2], t[3]};
+                    u32x4 lo, hi;
+                    rope_rotate_half8<DT>(w[c], w[c + QCH / 2], tab, lo, hi);
+                    w[c] = lo;
+                    w[c + QCH / 2] = hi;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < QCH; ++c) qf[b][c] = as_vec8<DT>(w[c]);
         }
     }
 
@@ -815,7 +866,8 @@ static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
 
 template <int DT>
 static hipError_t launch_rot(const AttnArgs& a, int rot, hipStream_t stream) {
-    if (rot == ROT_QK) return launch_dt<DT, ROT_QK>(a, stream);
+    if (rot == ROT_QK) return a.half_pairs ? launch_dt<DT, ROT_QK_HALF>(a, stream)
+                                           : launch_dt<DT, ROT_QK>(a, stream);
     if (rot == ROT_Q) return launch_dt<DT, ROT_Q>(a, stream);
     return launch_dt<DT, ROT_NONE>(a, stream);
 }

@@ -125,6 +125,12 @@ int check_base(double base) {
     return RAC_OK;
 }
 
+int check_pairing(int pairing) {
+    if (pairing != RAC_PAIR_ADJACENT && pairing != RAC_PAIR_HALF)
+        return fail(RAC_ERR_ARG, "pairing must be RAC_PAIR_ADJACENT or RAC_PAIR_HALF");
+    return RAC_OK;
+}
+
 int check_attn_ptrs(const void* q, const void* k, const void* v, const void* out, const float* lse,
                     int B, int Hq, int Hkv, int N, int D) {
     if (!q || !k || !v || !out) return fail(RAC_ERR_ARG, "q, k, v and out must be non-null");
@@ -259,20 +265,29 @@ int attn_bwd_common(const void* q, const void* k, const void* v, const void* out
 
 extern "C" {
 
-int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                         int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
-                         void* stream) {
+int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int N, int D, double rope_base, int pairing,
+                            int dtype, void* stream) {
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
     if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((rc = check_pairing(pairing)) != RAC_OK) return rc;
     if (empty) return ok();
     if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
-    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
+    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env(),
+                    pairing == RAC_PAIR_HALF};
     return hip_status(rac::launch_attn_fwd(a, rac::ROT_QK, static_cast<hipStream_t>(stream)),
                       "attn_rope_causal_fwd launch");
+}
+
+int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
+                         void* stream) {
+    return attn_rope_causal_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, N, D, rope_base,
+                                   RAC_PAIR_ADJACENT, dtype, stream);
 }
 
 int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void* out,
@@ -303,21 +318,32 @@ int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, floa
                       "attn_causal_fwd launch");
 }
 
-int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B, int Hq,
-                   int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+int rope_prerotate_ex(const void* q, const void* k, void* q_rot, void* k_rot, int B, int Hq,
+                      int Hkv, int N, int D, double rope_base, int pairing, int dtype,
+                      void* stream) {
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
     if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((rc = check_pairing(pairing)) != RAC_OK) return rc;
     if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)
         return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280");
     if (empty) return ok();
     if ((rc = check_pass_ptrs(q, k, q_rot, k_rot, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
-    return hip_status(rac::launch_rope_prerotate(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D,
-                                                 dtype, static_cast<hipStream_t>(stream)),
-                      "rope_prerotate launch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(
+        pairing == RAC_PAIR_HALF
+            ? rac::launch_rope_prerotate_half(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D, dtype, st)
+            : rac::launch_rope_prerotate(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D, dtype, st),
+        "rope_prerotate launch");
+}
+
+int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B, int Hq,
+                   int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+    return rope_prerotate_ex(q, k, q_rot, k_rot, B, Hq, Hkv, N, D, rope_base, RAC_PAIR_ADJACENT,
+                             dtype, stream);
 }
 
 int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,

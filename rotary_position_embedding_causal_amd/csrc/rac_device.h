@@ -83,4 +83,38 @@ __device__ __forceinline__ u32x4 rope_rotate8(u32x4 x, f32x4 cs_lo, f32x4 cs_hi)
     return y;
 }
 
+// Half-split pairing ("rotate_half"): element d of the first half pairs with
+// element d + D/2. lo, hi: the 8 elements d0 .. d0+7 (d0 < D/2) and their
+// partners d0 + D/2 .. +7; cs: the table entries of frequencies d0 .. d0+7,
+// (cos, sin) interleaved, 16 floats. Each pair (a, b) = (lo[j], hi[j]) turns
+// counter-clockwise exactly as in rope_rotate8:
+//   a' = a*c - b*s,  b' = a*s + b*c
+// in fp32 with one fused multiply-add each, then rounds to the storage format.
+template <int DT>
+__device__ __forceinline__ void rope_rotate_half8(u32x4 lo, u32x4 hi, const f32x4 (&cs)[4],
+                                                  u32x4& lo_out, u32x4& hi_out) {
+    typedef Fmt<DT> F;
+    float a[8], b[8], c[8], s[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        a[2 * t] = F::lo(lo[t]);
+        a[2 * t + 1] = F::hi(lo[t]);
+        b[2 * t] = F::lo(hi[t]);
+        b[2 * t + 1] = F::hi(hi[t]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        c[j] = cs[j >> 1][2 * (j & 1)];
+        s[j] = cs[j >> 1][2 * (j & 1) + 1];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int j0 = 2 * t, j1 = 2 * t + 1;
+        lo_out[t] = F::pack2(__builtin_fmaf(a[j0], c[j0], -(b[j0] * s[j0])),
+                             __builtin_fmaf(a[j1], c[j1], -(b[j1] * s[j1])));
+        hi_out[t] = F::pack2(__builtin_fmaf(a[j0], s[j0], b[j0] * c[j0]),
+                             __builtin_fmaf(a[j1], s[j1], b[j1] * c[j1]));
+    }
+}
+
 }  // namespace rac

@@ -21,11 +21,12 @@ struct AttnArgs {
     int B, Hq, Hkv, N, D;
     int dtype;
     int shape;           // ATTN_SHAPE_*
+    int half_pairs;      // 1: RoPE pairs (d, d + D/2) instead of (2i, 2i+1)
 };
 
 // Rotation applied inside the attention kernel: none (inputs already
 // rotated), Q and K (the fused path), or Q only (K rotated beforehand).
-enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2 };
+enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2, ROT_QK_HALF = 3 };
 
 // Causal attention forward; `rot` is a ROT_* mode.
 hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream);
@@ -54,6 +55,11 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream);
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
                                  const float* table, int B, int Hq, int Hkv, int N, int D,
                                  int dtype, hipStream_t stream);
+
+// The same pass with the half-split pairing (elements d, d + D/2).
+hipError_t launch_rope_prerotate_half(const void* q, const void* k, void* q_rot, void* k_rot,
+                                      const float* table, int B, int Hq, int Hkv, int N, int D,
+                                      int dtype, hipStream_t stream);
 
 // The inverse turn R(-p) of the same pass: dq = R(-p) dq_rot, dk = R(-p)
 // dk_rot (the gradient of the pre-rotation).

@@ -85,6 +85,51 @@ __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
     }
 }
 
+// The half-split pairing: a lane owns chunk c < D/16 of a row and its
+// partner chunk c + D/16 (elements d and d + D/2 pair), with the 16 table
+// floats of frequencies 8c .. 8c+7, for PR_HEADS slabs.
+template <int DT, int D, int PR_HEADS>
+__global__ __launch_bounds__(PR_THREADS) void rope_prerotate_half_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* q_rot,
+    uint16_t* k_rot, const float* __restrict__ table, int N, int64_t q_slabs,
+    int64_t total_slabs) {
+    constexpr int HALF_CHUNKS = D / 16;  // chunk pairs per row
+    const int64_t idx = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
+    const int64_t row = idx / HALF_CHUNKS;
+    const int chunk = (int)(idx % HALF_CHUNKS);
+    if (row >= N) return;
+    const f32x4* tab = reinterpret_cast<const f32x4*>(table + row * D + chunk * 16);
+    const f32x4 cs[4] = {tab[0], tab[1], tab[2], tab[3]};
+    const int64_t slab0 = (int64_t)blockIdx.y * PR_HEADS;
+    const int64_t lo_off = row * D + chunk * 8;  // element offsets inside a slab
+    const int64_t hi_off = lo_off + D / 2;
+    const int64_t slab_elems = (int64_t)N * D;
+
+    u32x4 lo[PR_HEADS], hi[PR_HEADS];
+#pragma unroll
+    for (int s = 0; s < PR_HEADS; ++s) {
+        const int64_t slab = slab0 + s;
+        if (slab < total_slabs) {
+            const uint16_t* src = slab < q_slabs ? q + slab * slab_elems
+                                                 : k + (slab - q_slabs) * slab_elems;
+            lo[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + lo_off));
+            hi[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + hi_off));
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < PR_HEADS; ++s) {
+        const int64_t slab = slab0 + s;
+        if (slab < total_slabs) {
+            uint16_t* dst = slab < q_slabs ? q_rot + slab * slab_elems
+                                           : k_rot + (slab - q_slabs) * slab_elems;
+            u32x4 a, b;
+            rope_rotate_half8<DT>(lo[s], hi[s], cs, a, b);
+            __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(dst + lo_off));
+            __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(dst + hi_off));
+        }
+    }
+}
+
 template <int DT, int D, int H, bool INV>
 static hipError_t launch_heads(const void* q, const void* k, void* q_rot, void* k_rot,
                                const float* table, int N, int64_t q_slabs, int64_t total,
@@ -147,6 +192,44 @@ hipError_t launch_rope_unrotate(const void* dq_rot, const void* dk_rot, void* dq
                                 const float* table, int B, int Hq, int Hkv, int N, int D,
                                 int dtype, hipStream_t stream) {
     return launch_any<true>(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D, dtype, stream);
+}
+
+template <int DT, int D, int H>
+static hipError_t launch_half_heads(const void* q, const void* k, void* q_rot, void* k_rot,
+                                    const float* table, int N, int64_t q_slabs, int64_t total,
+                                    unsigned gx, hipStream_t stream) {
+    dim3 grid(gx, (unsigned)((total + H - 1) / H));
+    rope_prerotate_half_kernel<DT, D, H><<<grid, PR_THREADS, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N, q_slabs, total);
+    return hipGetLastError();
+}
+
+// Same grid policy as the adjacent pairing, with one lane per chunk pair.
+template <int DT, int D>
+static hipError_t launch_half(const void* q, const void* k, void* q_rot, void* k_rot,
+                              const float* table, int B, int Hq, int Hkv, int N,
+                              hipStream_t stream) {
+    const int64_t lanes = (int64_t)N * (D / 16);
+    const int64_t q_slabs = (int64_t)B * Hq;
+    const int64_t total = q_slabs + (int64_t)B * Hkv;
+    const unsigned gx = (unsigned)((lanes + PR_THREADS - 1) / PR_THREADS);
+    switch (prerotate_heads(total)) {
+        case 8: return launch_half_heads<DT, D, 8>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 4: return launch_half_heads<DT, D, 4>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 2: return launch_half_heads<DT, D, 2>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        default: return launch_half_heads<DT, D, 1>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+    }
+}
+
+hipError_t launch_rope_prerotate_half(const void* q, const void* k, void* q_rot, void* k_rot,
+                                      const float* table, int B, int Hq, int Hkv, int N, int D,
+                                      int dtype, hipStream_t stream) {
+    if (dtype == DT_BF16)
+        return D == 64 ? launch_half<DT_BF16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                       : launch_half<DT_BF16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return D == 64 ? launch_half<DT_FP16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                   : launch_half<DT_FP16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
 }
 
 }  // namespace rac

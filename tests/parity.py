@@ -63,7 +63,8 @@ def sampled_rows(B, H, N, rng, per_head=24):
     return out
 
 
-def oracle_rows(q_bits, k_bits, v_bits, dtype, base, Hq, Hkv, rows_by_head, variant):
+def oracle_rows(q_bits, k_bits, v_bits, dtype, base, Hq, Hkv, rows_by_head, variant,
+                pairing="adjacent"):
     """Oracle output and LSE for selected rows of selected (b, h).
 
     Rotates only the heads involved; returns {(b, h): (o [r, D], lse [r])}."""
@@ -74,8 +75,8 @@ def oracle_rows(q_bits, k_bits, v_bits, dtype, base, Hq, Hkv, rows_by_head, vari
         q = oracle.decode(q_bits[b, h], dtype)[None, None]
         k = oracle.decode(k_bits[b, g], dtype)[None, None]
         v = oracle.decode(v_bits[b, g], dtype)[None, None]
-        qr = oracle.rope_bhnd(q, base)
-        kr = oracle.rope_bhnd(k, base)
+        qr = oracle.rope_bhnd(q, base, pairing)
+        kr = oracle.rope_bhnd(k, base, pairing)
         if variant == "rounded":
             qr = oracle.decode(oracle.encode(qr, dtype), dtype)
             kr = oracle.decode(oracle.encode(kr, dtype), dtype)

@@ -265,3 +265,60 @@ def test_rope_prerotate_bwd_argument_rules():
     assert f(Q, K, O, L, 1, 4, 2, 64, 64, -1.0, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, O, L, 1, 4, 3, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, O, L, 0, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_OK
+
+
+def fused_ex(pairing=1, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().attn_rope_causal_fwd_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                             a["Hq"], a["Hkv"], a["N"], a["D"], a["base"],
+                                             pairing, a["dtype"], None)
+
+
+def prerot_ex(pairing=1, **kw):
+    a = dict(q=Q, k=K, qr=O, kr=L, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    return rac.lib().rope_prerotate_ex(a["q"], a["k"], a["qr"], a["kr"], a["B"], a["Hq"],
+                                       a["Hkv"], a["N"], a["D"], a["base"], pairing, a["dtype"],
+                                       None)
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_pairing_entry_points_reject_bad_arguments(kw, code, pairing):
+    assert fused_ex(pairing, **kw) == code
+    assert rac.last_error() != ""
+
+
+@pytest.mark.parametrize("pairing", [-1, 2, 7])
+def test_unknown_pairing_is_rejected(pairing):
+    assert fused_ex(pairing) == rac.RAC_ERR_ARG
+    assert "pairing" in rac.last_error()
+    assert prerot_ex(pairing) == rac.RAC_ERR_ARG
+    assert "pairing" in rac.last_error()
+    # checked before the empty-problem shortcut, like every other argument
+    assert fused_ex(pairing, B=0) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, N=0) == rac.RAC_ERR_ARG
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_pairing_prerotate_rules(pairing):
+    assert prerot_ex(pairing, qr=None) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, qr=K) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, qr=ctypes.c_void_p(P + 16)) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, q=ctypes.c_void_p(P + 2)) == rac.RAC_ERR_ALIGN
+    assert prerot_ex(pairing, D=32) == rac.RAC_ERR_UNSUPPORTED
+    assert prerot_ex(pairing, base=0.0) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, B=65535, Hq=8, Hkv=8) == rac.RAC_ERR_ARG
+    assert fused_ex(pairing, base=float("nan")) == rac.RAC_ERR_ARG
+    assert prerot_ex(pairing, B=0) == rac.RAC_OK
+    assert fused_ex(pairing, N=0, q=None, k=None, v=None, out=None, lse=None) == rac.RAC_OK
+    assert rac.last_error() == ""
+
+
+def test_binding_pairing_names():
+    assert rac._pairing("adjacent") == rac.RAC_PAIR_ADJACENT
+    assert rac._pairing("half") == rac.RAC_PAIR_HALF
+    assert rac._pairing(1) == rac.RAC_PAIR_HALF
+    with pytest.raises(ValueError):
+        rac._pairing("interleaved")

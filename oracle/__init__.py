@@ -61,6 +61,9 @@ class Oracle:
         lib.oracle_attn_rows.argtypes = [f64p, f64p, f64p] + [ctypes.c_int] * 5 + [
             i64p, ctypes.c_int64, f64p, f64p]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_alibi_rows.argtypes = [f64p, f64p, f64p] + [ctypes.c_int] * 5 + [
+            f64p, i64p, ctypes.c_int64, f64p, f64p]
+        lib.oracle_attn_alibi_rows.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [f64p] * 4 + [ctypes.c_int] * 5 + [f64p] * 5
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
@@ -111,13 +114,15 @@ class Oracle:
         """RoPE on a [B, H, N, D] tensor: row n of every (b, h) sits at position n."""
         return self.rope(x, np.arange(x.shape[-2], dtype=np.int64), base, pairing)
 
-    def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, rows=None):
+    def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, rows=None, slopes=None):
         """Causal softmax attention, fp64, two-pass.
 
         q [B, Hq, N, D]; k, v [B, Hkv, N, D]. ``rows`` (optional) lists the
-        flattened query rows (b*Hq + h)*N + i to compute. Returns (o, lse): with
-        ``rows=None`` o is [B, Hq, N, D] and lse [B, Hq, N]; otherwise o is
-        [len(rows), D] and lse [len(rows)].
+        flattened query rows (b*Hq + h)*N + i to compute. ``slopes``
+        (optional, Hq values) adds the ALiBi penalty -slopes[h] * (i - j) to
+        the scaled scores. Returns (o, lse): with ``rows=None`` o is
+        [B, Hq, N, D] and lse [B, Hq, N]; otherwise o is [len(rows), D] and
+        lse [len(rows)].
         """
         q = np.ascontiguousarray(q, dtype=np.float64)
         k = np.ascontiguousarray(k, dtype=np.float64)
@@ -135,32 +140,46 @@ class Oracle:
             o = np.empty((r.size, D), dtype=np.float64)
             lse = np.empty((r.size,), dtype=np.float64)
             rp, nrows = _ptr(r, ctypes.c_int64), r.size
-        rc = self.lib.oracle_attn_rows(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
-                                       _ptr(v, ctypes.c_double), B, Hq, Hkv, N, D, rp, nrows,
-                                       _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+        if slopes is None:
+            rc = self.lib.oracle_attn_rows(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                           _ptr(v, ctypes.c_double), B, Hq, Hkv, N, D, rp, nrows,
+                                           _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+        else:
+            sl = np.ascontiguousarray(slopes, dtype=np.float64)
+            if sl.shape != (Hq,):
+                raise ValueError("slopes must hold one value per query head")
+            rc = self.lib.oracle_attn_alibi_rows(
+                _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                B, Hq, Hkv, N, D, _ptr(sl, ctypes.c_double), rp, nrows,
+                _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
         if rc != 0:
-            raise ValueError("oracle_attn_rows: bad arguments")
+            raise ValueError("oracle attention: bad arguments")
         return o, lse
 
     def rope_attention(self, q_bits, k_bits, v_bits, dtype: str, base: float, rows=None,
-                       variant: str = "rounded", pairing: str = "adjacent"):
+                       variant: str = "rounded", pairing: str = "adjacent", slopes=None):
         """RoPE then causal attention, from bf16/fp16 bit patterns.
 
         ``variant="exact"`` feeds the fp64 rotation straight into attention;
         ``variant="rounded"`` first rounds the rotated q and k to ``dtype``.
+        ``base=None`` skips the rotation (plain causal attention on the
+        decoded inputs); ``slopes`` as in attention().
         Returns (o, lse, q_rot, k_rot) with q_rot/k_rot the fp64 operands used.
         """
         q = self.decode(q_bits, dtype)
         k = self.decode(k_bits, dtype)
         v = self.decode(v_bits, dtype)
-        qr = self.rope_bhnd(q, base, pairing)
-        kr = self.rope_bhnd(k, base, pairing)
+        if base is None:
+            qr, kr = q, k
+        else:
+            qr = self.rope_bhnd(q, base, pairing)
+            kr = self.rope_bhnd(k, base, pairing)
         if variant == "rounded":
             qr = self.decode(self.encode(qr, dtype), dtype)
             kr = self.decode(self.encode(kr, dtype), dtype)
         elif variant != "exact":
             raise ValueError("variant must be 'exact' or 'rounded'")
-        o, lse = self.attention(qr, kr, v, rows)
+        o, lse = self.attention(qr, kr, v, rows, slopes)
         return o, lse, qr, kr
 
 

@@ -235,6 +235,64 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
     return bad ? -1 : 0;
 }
 
+/* ---- causal attention with a linear distance penalty (ALiBi) ------------ */
+
+/* The attention of oracle_attn_rows with one post-product term: the score of
+ * key j for query i of query head h is lowered in proportion to how far back
+ * the key lies, slopes[h] * (i - j) ("Fast and Exact Relative-Position
+ * Attention via Structure-Aware Kernels", rainbus digest, background "RoPE and
+ * parameter-free position encodings": ALiBi adds a linear penalty by
+ * distance). The penalty is added to the scaled product:
+ *     s_ij = q_i . k_j / sqrt(D) - slopes[h] * (i - j),
+ * one slope per QUERY head (slopes has Hq entries), then the same causal
+ * softmax, output and natural-log LSE as oracle_attn_rows. */
+int oracle_attn_alibi_rows(const double* q, const double* k, const double* v,
+                           int B, int Hq, int Hkv, int N, int D, const double* slopes,
+                           const int64_t* rows, int64_t nrows, double* o, double* lse) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv != 0 || !slopes) return -1;
+    const int64_t all_rows = (int64_t)B * Hq * N;
+    if (!rows) nrows = all_rows;
+    const int heads_per_kv = Hq / Hkv;
+    const double inv_sqrt_d = sqrt(1.0 / (double)D);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* score = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t flat = rows ? rows[r] : r;
+            if (!score || flat < 0 || flat >= all_rows) { bad = 1; continue; }
+            const int64_t qpos = flat % N;
+            const int64_t qhead = (flat / N) % Hq, batch = flat / N / Hq;
+            const int64_t kvh = batch * Hkv + qhead / heads_per_kv;
+            const double slope = slopes[qhead];
+            const double* qv = q + flat * D;
+            const double* keys = k + kvh * (int64_t)N * D;
+            const double* vals = v + kvh * (int64_t)N * D;
+            double top = -INFINITY;
+            for (int64_t kpos = 0; kpos <= qpos; ++kpos) {
+                double qk = 0.0;
+                for (int d = 0; d < D; ++d) qk += qv[d] * keys[kpos * D + d];
+                const double distance = (double)(qpos - kpos);
+                score[kpos] = inv_sqrt_d * qk - slope * distance;
+                top = score[kpos] > top ? score[kpos] : top;
+            }
+            double denom = 0.0;
+            double* out = o + r * D;
+            for (int d = 0; d < D; ++d) out[d] = 0.0;
+            for (int64_t kpos = 0; kpos <= qpos; ++kpos) {
+                const double w = exp(score[kpos] - top);
+                denom += w;
+                for (int d = 0; d < D; ++d) out[d] += w * vals[kpos * D + d];
+            }
+            for (int d = 0; d < D; ++d) out[d] = out[d] / denom;
+            lse[r] = top + log(denom);
+        }
+        free(score);
+    }
+    return bad ? -1 : 0;
+}
+
 /* ---- causal attention, backward ------------------------------------------ */
 
 /* The scores of query row `row` (flattened (b*Hq + h)*N + i) against the

@@ -532,4 +532,76 @@ def pin_rope_half_invariants(orc):
         assert abs(a - b) / scale < 1e-11
 
 
+# --------------------------------------------------------------------------
+# ALiBi: a linear penalty by distance added to the scaled scores
+# --------------------------------------------------------------------------
+
+def _alibi_slopes(H):
+    """The geometric slope sequence 2^(-8(h+1)/H) of the ALiBi method."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)])
+
+
+def pin_alibi_torch_sdpa_float_mask(orc):
+    # torch adds a float attn_mask to the scaled scores: the bias -m_h (i - j)
+    # with -inf above the diagonal, one slope per query head, GQA by repeat
+    rng = _rng(40)
+    for (B, Hq, Hkv, N, D) in ((1, 4, 4, 33, 16), (2, 8, 2, 48, 32), (1, 6, 3, 17, 64)):
+        q, k, v = _qkv(rng, B, Hq, Hkv, N, D, sigma=1.5)
+        slopes = _alibi_slopes(Hq) * rng.uniform(0.5, 2.0, Hq)
+        o, lse = orc.attention(q, k, v, slopes=slopes)
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        bias = -slopes[:, None, None] * (i - j)[None].astype(np.float64)
+        bias = np.where((j > i)[None], -np.inf, bias)
+        rep = Hq // Hkv
+        tk = torch.from_numpy(k).repeat_interleave(rep, dim=1)
+        tv = torch.from_numpy(v).repeat_interleave(rep, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), tk, tv, attn_mask=torch.from_numpy(bias)[None]).numpy()
+        assert np.max(np.abs(o - ref)) < 1e-12
+        S = np.matmul(q, np.swapaxes(tk.numpy(), -1, -2)) / np.sqrt(D) + bias[None]
+        assert np.max(np.abs(lse - scipy.special.logsumexp(S, axis=-1))) < 1e-12
+
+
+def pin_alibi_zero_queries_geometric(orc):
+    # q = 0: every score is the penalty alone, so the weights of keys t back
+    # are e^(-m t): a geometric series with closed-form sums
+    N, D, H = 60, 16, 4
+    q = np.zeros((1, H, N, D))
+    k = _rng(41).standard_normal((1, H, N, D))
+    v = np.zeros((1, H, N, D))
+    v[0, :, 0, 0] = 1.0                      # picks out key 0's weight
+    v[0, :, :, 1] = np.arange(N)             # the mean key position
+    slopes = _alibi_slopes(H)
+    o, lse = orc.attention(q, k, v, slopes=slopes)
+    i = np.arange(N, dtype=np.float64)
+    for h, m in enumerate(slopes):
+        r = math.exp(-m)
+        total = (1.0 - r ** (i + 1)) / (1.0 - r)          # sum_{t=0..i} r^t
+        assert np.max(np.abs(lse[0, h] - np.log(total))) < 1e-13
+        assert np.max(np.abs(o[0, h, :, 0] - r ** i / total)) < 1e-14
+        # mean position i - E[t], E[t] = sum t r^t / sum r^t
+        et = (r * (1 - (i + 1) * r ** i + i * r ** (i + 1)) / (1 - r) ** 2) / total
+        assert np.max(np.abs(o[0, h, :, 1] - (i - et))) < 1e-11
+
+
+def pin_alibi_zero_slopes_is_plain_attention(orc):
+    rng = _rng(42)
+    q, k, v = _qkv(rng, 2, 4, 2, 31, 32, sigma=2.0)
+    o, lse = orc.attention(q, k, v)
+    o2, lse2 = orc.attention(q, k, v, slopes=np.zeros(4))
+    assert np.max(np.abs(o - o2)) < 1e-13 and np.max(np.abs(lse - lse2)) < 1e-13
+
+
+def pin_alibi_steep_slope_keeps_the_diagonal(orc):
+    # a slope far above the spread of the scores leaves only key j = i
+    rng = _rng(43)
+    q, k, v = _qkv(rng, 1, 2, 1, 20, 16, sigma=0.5)
+    o, lse = orc.attention(q, k, v, slopes=np.array([80.0, 120.0]))
+    for h in range(2):
+        assert np.max(np.abs(o[0, h] - v[0, 0])) < 1e-20 + 1e-25
+        sii = np.einsum("nd,nd->n", q[0, h], k[0, 0]) / 4.0
+        assert np.max(np.abs(lse[0, h] - sii)) < 1e-14
+
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

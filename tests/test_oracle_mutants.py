@@ -53,6 +53,19 @@ MUTANTS = {
     "bwd_scale_one_over_d": ("pow((double)D, -0.5)", "pow((double)D, -1.0)"),
     "bwd_gqa_modulo": ("const int64_t kv_head = b * Hkv + h / group;",
                        "const int64_t kv_head = b * Hkv + h % Hkv;"),
+    "alibi_scale_one_over_d": ("sqrt(1.0 / (double)D)", "(1.0 / (double)D)"),
+    "alibi_sign": ("score[kpos] = inv_sqrt_d * qk - slope * distance;",
+                   "score[kpos] = inv_sqrt_d * qk + slope * distance;"),
+    "alibi_scaled_penalty": ("score[kpos] = inv_sqrt_d * qk - slope * distance;",
+                             "score[kpos] = inv_sqrt_d * (qk - slope * distance);"),
+    "alibi_slope_per_kv_head": ("const double slope = slopes[qhead];",
+                                "const double slope = slopes[qhead / heads_per_kv];"),
+    "alibi_distance_offset": ("const double distance = (double)(qpos - kpos);",
+                              "const double distance = (double)(qpos - kpos + 1);"),
+    "alibi_gqa_modulo": ("const int64_t kvh = batch * Hkv + qhead / heads_per_kv;",
+                         "const int64_t kvh = batch * Hkv + qhead % Hkv;"),
+    "alibi_mask_strict": ("for (int64_t kpos = 0; kpos <= qpos; ++kpos) {\n                const double w",
+                          "for (int64_t kpos = 0; kpos < qpos; ++kpos) {\n                const double w"),
 }
 
 

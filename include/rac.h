@@ -152,7 +152,7 @@ int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void
                            float* lse, int B, int Hq, int Hkv, int N, int D,
                            double rope_base, int dtype, void* stream);
 
-enum { RAC_PAIR_ADJACENT = 0, RAC_PAIR_HALF = 1 };
+enum { RAC_PAIR_ADJACENT = 0, RAC_PAIR_HALF = 1, RAC_ROPE_NONE = 2 };
 
 /*
  * RoPE with a choice of which coordinates turn together (`pairing`):
@@ -169,8 +169,8 @@ enum { RAC_PAIR_ADJACENT = 0, RAC_PAIR_HALF = 1 };
  * attn_rope_causal_fwd with that argument; with RAC_PAIR_ADJACENT they give
  * exactly those functions' results. For either pairing,
  * attn_causal_fwd(rope_prerotate_ex(q, k)) equals attn_rope_causal_fwd_ex
- * bit for bit. Any other value of `pairing` is RAC_ERR_ARG. Same layouts,
- * limits and rules as the functions they extend.
+ * bit for bit. Any other value of `pairing` (RAC_ROPE_NONE included) is
+ * RAC_ERR_ARG. Same layouts, limits and rules as the functions they extend.
  */
 int rope_prerotate_ex(const void* q, const void* k, void* q_rot, void* k_rot,
                       int B, int Hq, int Hkv, int N, int D, double rope_base,
@@ -178,6 +178,32 @@ int rope_prerotate_ex(const void* q, const void* k, void* q_rot, void* k_rot,
 int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                             int B, int Hq, int Hkv, int N, int D, double rope_base,
                             int pairing, int dtype, void* stream);
+
+/*
+ * Causal attention with the ALiBi distance penalty, a score modification
+ * applied after the QK product: the score of key j for query i of query head
+ * h is
+ *     q_i . k_j / sqrt(D) - slopes[h] * (i - j)
+ * ("Fast and Exact Relative-Position Attention via Structure-Aware Kernels",
+ * rainbus digest, background "RoPE and parameter-free position encodings":
+ * ALiBi penalises attention linearly with distance), then the same causal
+ * softmax, out and lse as attn_causal_fwd. The penalty enters the score
+ * accumulators before the product, in fp32.
+ *
+ * slopes: DEVICE pointer to Hq fp32 values, one per query head, finite (the
+ *   ALiBi method's own choice is the geometric sequence 2^(-8(h+1)/Hq));
+ *   4-byte aligned; must not overlap out or lse.
+ * pairing: RAC_ROPE_NONE for no rotation (rope_base is then ignored), or
+ *   RAC_PAIR_ADJACENT / RAC_PAIR_HALF to rotate q and k in the kernel as
+ *   attn_rope_causal_fwd_ex does, composing RoPE (before the product) with
+ *   ALiBi (after it).
+ * With every slope zero the results equal attn_causal_fwd (RAC_ROPE_NONE) or
+ * attn_rope_causal_fwd_ex (a RoPE pairing) bit for bit. Same layouts, limits
+ * and rules as attn_rope_causal_fwd.
+ */
+int attn_alibi_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int N, int D, const float* slopes,
+                          double rope_base, int pairing, int dtype, void* stream);
 
 enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
 

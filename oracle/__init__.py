@@ -271,13 +271,14 @@ def rope_bhnd(x, base, pairing="adjacent"):
     return default().rope_bhnd(x, base, pairing)
 
 
-def attention(q, k, v, rows=None):
-    return default().attention(q, k, v, rows)
+def attention(q, k, v, rows=None, slopes=None):
+    return default().attention(q, k, v, rows, slopes)
 
 
 def rope_attention(q_bits, k_bits, v_bits, dtype, base, rows=None, variant="rounded",
-                   pairing="adjacent"):
-    return default().rope_attention(q_bits, k_bits, v_bits, dtype, base, rows, variant, pairing)
+                   pairing="adjacent", slopes=None):
+    return default().rope_attention(q_bits, k_bits, v_bits, dtype, base, rows, variant, pairing,
+                                    slopes)
 
 
 def attention_bwd(q, k, v, dout):

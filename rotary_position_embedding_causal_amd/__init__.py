@@ -36,10 +36,10 @@ RAC_MAX_N = 1 << 22
 EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_prerotate_k",
             "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
-            "rope_prerotate_ex", "attn_rope_causal_fwd_ex",
+            "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
             "rac_last_error", "rac_release_tables")
-RAC_PAIR_ADJACENT, RAC_PAIR_HALF = 0, 1
-PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF}
+RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
+PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
 RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
 PATH_NAMES = {RAC_PATH_FUSED: "fused", RAC_PATH_PREROTATE: "prerotate", RAC_PATH_SPLIT: "split"}
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.rope_prerotate_ex.restype = i
     L.attn_rope_causal_fwd_ex.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, i, vp]
     L.attn_rope_causal_fwd_ex.restype = i
+    L.attn_alibi_causal_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, vp, d, i, i, vp]
+    L.attn_alibi_causal_fwd.restype = i
     L.rac_last_error.argtypes = []
     L.rac_last_error.restype = ctypes.c_char_p
     L.rac_release_tables.argtypes = []
@@ -189,6 +191,25 @@ def attn_rope_causal_fwd_ex(q, k, v, rope_base: float, pairing="adjacent", out=N
                                            B, Hq, Hkv, N, D, float(rope_base), _pairing(pairing),
                                            dt, _stream(q.device))
     check(rc, "attn_rope_causal_fwd_ex")
+    return out, lse
+
+
+def attn_alibi_causal_fwd(q, k, v, slopes, rope_base=None, pairing="adjacent", out=None,
+                          lse=None, want_lse: bool = True):
+    """Causal attention with the ALiBi penalty -slopes[h] * (i - j) on the scaled
+    scores; slopes: fp32 tensor [Hq] on q's device. With rope_base given, RoPE
+    (``pairing``) is fused as well. Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    if slopes.shape != (Hq,) or slopes.dtype != torch.float32 or slopes.device != q.device \
+            or not slopes.is_contiguous():
+        raise ValueError("slopes must be a contiguous fp32 tensor [Hq] on q's device")
+    out, lse = _outputs(q, out, lse, want_lse)
+    pr = RAC_ROPE_NONE if rope_base is None else _pairing(pairing)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_alibi_causal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         B, Hq, Hkv, N, D, _ptr(slopes),
+                                         float(rope_base or 0.0), pr, dt, _stream(q.device))
+    check(rc, "attn_alibi_causal_fwd")
     return out, lse
 
 

@@ -238,10 +238,12 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 // PV MFMAs overlap the second block's softmax, inside one wave.
 template <int DT, int D, int RM, int QB, int NW = 4 / QB>
 struct WaveAttn {
-    static constexpr bool ROPE_Q = RM != ROT_NONE;  // rotate Q rows when loading them
-    static constexpr bool HALF = RM == ROT_QK_HALF;  // half-split pairs (d, d + D/2)
+    static constexpr int ROT = RM & 3;                // rotation part of the mode
+    static constexpr bool ALIBI = (RM & MOD_ALIBI) != 0;  // linear distance penalty
+    static constexpr bool ROPE_Q = ROT != ROT_NONE;   // rotate Q rows when loading them
+    static constexpr bool HALF = ROT == ROT_QK_HALF;  // half-split pairs (d, d + D/2)
     // rotate every K tile in LDS: 0 no, 1 adjacent pairs, 2 half-split pairs
-    static constexpr int ROPE_K = RM == ROT_QK ? 1 : (RM == ROT_QK_HALF ? 2 : 0);
+    static constexpr int ROPE_K = ROT == ROT_QK ? 1 : (ROT == ROT_QK_HALF ? 2 : 0);
     typedef Fmt<DT> F;
     typedef typename F::vec8 vec8;
     typedef Tile<D> T;
@@ -256,6 +258,13 @@ struct WaveAttn {
     float l_run[QB];    // this lane half's share of the denominator
     float alpha[QB];    // rescale factor of acc still to apply (1 = none)
     u32x4 pw[QB][2][2];  // the tile's probabilities, packed as PV B operands
+    float slope_raw;     // ALIBI: the head's slope in raw-score units, m * sqrt(D)
+
+    // ALIBI: the slope of query head `head` (slopes[head] is m in the
+    // penalty -m (i - j) on the scaled scores; raw scores are sqrt(D) larger).
+    __device__ __forceinline__ void set_slope(const float* __restrict__ slopes, int64_t head) {
+        if (ALIBI) slope_raw = slopes[head] * __builtin_sqrtf((float)D);
+    }
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -314,14 +323,23 @@ struct WaveAttn {
     // chain issues at full rate through accumulator forwarding). With LOADS,
     // one block of the next tile's loads follows every second MFMA of the
     // second half, so their issue overlaps matrix work.
+    // With ALIBI the accumulators start at the penalty in raw-score units,
+    // m sqrt(D) (key - row) for this lane's row and keys (key k0 + 32 kb +
+    // 8 (j >> 2) + 4 hh + (j & 3) for element j), so the scores leave the
+    // matrix cores with the penalty added and the softmax is unchanged.
     template <bool LOADS>
-    __device__ __forceinline__ void score(int b, const uint16_t* Ks, int n, int hh,
-                                          Stage& stage, const NextLoads& next) {
+    __device__ __forceinline__ void score(int b, const uint16_t* Ks, int n, int hh, int k0,
+                                          int row, Stage& stage, const NextLoads& next) {
+        float base = 0.f;
+        if (ALIBI) base = slope_raw * (float)(k0 + 4 * hh - row);
         __builtin_amdgcn_s_setprio(1);  // matrix phase first when waves share a SIMD
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[b][kb][j] = 0.f;
+            for (int j = 0; j < 16; ++j)
+                s[b][kb][j] = ALIBI ? __builtin_fmaf(slope_raw,
+                                                     (float)(32 * kb + 8 * (j >> 2) + (j & 3)), base)
+                                    : 0.f;
 #pragma unroll
             for (int c = 0; c < QCH; ++c) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(
@@ -443,13 +461,13 @@ struct WaveAttn {
                                          const NextLoads& next) {
         const uint16_t* Vs = Ks + T::K_ELEMS;
         if (QB == 1) {
-            score<true>(0, Ks, n, hh, stage, next);
+            score<true>(0, Ks, n, hh, k0, q_first + n, stage, next);
             softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
             rescale(0);
             pv(0, Vs, lane);
         } else {
-            score<false>(0, Ks, n, hh, stage, next);
-            score<true>(1, Ks, n, hh, stage, next);
+            score<false>(0, Ks, n, hh, k0, q_first + n, stage, next);
+            score<true>(1, Ks, n, hh, k0, q_first + 32 + n, stage, next);
             softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
             rescale(0);
             pv(0, Vs, lane);
@@ -512,7 +530,8 @@ template <int DT, int D, int RM, int QB, int HG>
 __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, float scale_log2) {
+    const float* __restrict__ table, const float* __restrict__ slopes, int Hq, int Hkv, int N,
+    int n_qtiles, float scale_log2) {
     typedef Tile<D> T;
     constexpr int WPH = 4 / QB;  // waves per head
     typedef WaveAttn<DT, D, RM, QB, WPH * HG> W;
@@ -536,6 +555,7 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
     W st;
     st.load_q(q + q_head * D, table, qw0, N, n, hh);
     st.reset();
+    st.set_slope(slopes, un.h + wave / WPH);
 
     const int n_tiles = kv_tiles_of(qtile, N);
     const int wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
@@ -583,8 +603,8 @@ template <int DT, int D, int RM>
 __global__ __launch_bounds__(512, 1) void attn_pair_heads_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ table, int Hq, int Hkv, int N, int n_tiles64, int n_pairs,
-    float scale_log2) {
+    const float* __restrict__ table, const float* __restrict__ slopes, int Hq, int Hkv, int N,
+    int n_tiles64, int n_pairs, float scale_log2) {
     typedef Tile<D> T;
     typedef WaveAttn<DT, D, RM, 1, 8> W;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
@@ -609,6 +629,7 @@ __global__ __launch_bounds__(512, 1) void attn_pair_heads_kernel(
     const bool has_rows = tile >= 0 && qw0 < N;
     if (has_rows) st.load_q(q + q_head * D, table, qw0, N, n, hh);
     st.reset();
+    st.set_slope(slopes, un.h + ((wave >> 1) & 1));
 
     const int n_tiles = (min(t_heavy * 64 + 64, N) - 1) / BN + 1;
     const int wave_tiles = has_rows ? (min(qw0 + 31, N - 1)) / BN + 1 : 0;
@@ -645,8 +666,8 @@ template <int DT, int D, int RM, int QB>
 __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ table, int Hq, int Hkv, int N, int n_qtiles, int n_pairs,
-    float scale_log2) {
+    const float* __restrict__ table, const float* __restrict__ slopes, int Hq, int Hkv, int N,
+    int n_qtiles, int n_pairs, float scale_log2) {
     typedef Tile<D> T;
     typedef WaveAttn<DT, D, RM, QB> W;
     constexpr int HT = 256 / QB;  // threads per half
@@ -694,6 +715,7 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
 
     W st;
     st.reset();
+    st.set_slope(slopes, un.h);
     int cur_qt = -1;   // query tile whose rows this wave holds
     int qw0 = 0, wave_tiles = 0;
 
@@ -837,24 +859,24 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
         attn_pair_heads_kernel<DT, D, RM><<<dim3((unsigned)units), 512, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.Hq, a.Hkv, a.N, n_t64, n_pairs64, scale_log2);
+            a.slopes, a.Hq, a.Hkv, a.N, n_t64, n_pairs64, scale_log2);
     } else if (pair) {
         attn_pair_kernel<DT, D, RM, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
+            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
     } else if ((a.Hq / a.Hkv) % 2 == 0) {
         // GQA: two query heads of a group per workgroup share every key tile
         attn_fwd_kernel<DT, D, RM, QB, 2><<<dim3((unsigned)(tile_units / 2)), 512 / QB, 0,
                                              stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
+            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
     } else {
         attn_fwd_kernel<DT, D, RM, QB, 1><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
             static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
+            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
     }
     return hipGetLastError();
 }
@@ -866,6 +888,13 @@ static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
 
 template <int DT>
 static hipError_t launch_rot(const AttnArgs& a, int rot, hipStream_t stream) {
+    if (a.slopes != nullptr) {  // ALiBi: with RoPE on Q and K (either pairing) or none
+        if (rot == ROT_QK)
+            return a.half_pairs ? launch_dt<DT, ROT_QK_HALF | MOD_ALIBI>(a, stream)
+                                : launch_dt<DT, ROT_QK | MOD_ALIBI>(a, stream);
+        if (rot == ROT_NONE) return launch_dt<DT, ROT_NONE | MOD_ALIBI>(a, stream);
+        return hipErrorInvalidValue;
+    }
     if (rot == ROT_QK) return a.half_pairs ? launch_dt<DT, ROT_QK_HALF>(a, stream)
                                            : launch_dt<DT, ROT_QK>(a, stream);
     if (rot == ROT_Q) return launch_dt<DT, ROT_Q>(a, stream);

@@ -283,6 +283,34 @@ int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* o
                       "attn_rope_causal_fwd launch");
 }
 
+int attn_alibi_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int N, int D, const float* slopes,
+                          double rope_base, int pairing, int dtype, void* stream) {
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    const bool rope = pairing != RAC_ROPE_NONE;
+    if (rope && (rc = check_pairing(pairing)) != RAC_OK) return rc;
+    if (rope && (rc = check_base(rope_base)) != RAC_OK) return rc;
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    if (!slopes) return fail(RAC_ERR_ARG, "slopes must be non-null");
+    if (reinterpret_cast<uintptr_t>(slopes) % 4 != 0)
+        return fail(RAC_ERR_ALIGN, "slopes must be 4-byte aligned");
+    const int64_t slope_bytes = (int64_t)Hq * 4;
+    const int64_t out_bytes = (int64_t)B * Hq * N * D * 2;
+    if (overlap(slopes, slope_bytes, out, out_bytes) ||
+        (lse && overlap(slopes, slope_bytes, lse, (int64_t)B * Hq * N * 4)))
+        return fail(RAC_ERR_ARG, "slopes must not overlap out or lse");
+    const float* table = nullptr;
+    if (rope && (rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
+    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env(),
+                    pairing == RAC_PAIR_HALF, slopes};
+    return hip_status(rac::launch_attn_fwd(a, rope ? rac::ROT_QK : rac::ROT_NONE,
+                                           static_cast<hipStream_t>(stream)),
+                      "attn_alibi_causal_fwd launch");
+}
+
 int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                          int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
                          void* stream) {

@@ -22,11 +22,14 @@ struct AttnArgs {
     int dtype;
     int shape;           // ATTN_SHAPE_*
     int half_pairs;      // 1: RoPE pairs (d, d + D/2) instead of (2i, 2i+1)
+    const float* slopes = nullptr;  // ALiBi slope per query head [Hq], or null for none
 };
 
 // Rotation applied inside the attention kernel: none (inputs already
 // rotated), Q and K (the fused path), or Q only (K rotated beforehand).
 enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2, ROT_QK_HALF = 3 };
+// Added to a rotation mode: the ALiBi distance penalty on the scores.
+enum { MOD_ALIBI = 4 };
 
 // Causal attention forward; `rot` is a ROT_* mode.
 hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream);

@@ -322,3 +322,38 @@ def test_binding_pairing_names():
     assert rac._pairing(1) == rac.RAC_PAIR_HALF
     with pytest.raises(ValueError):
         rac._pairing("interleaved")
+
+
+S_ = ctypes.c_void_p(P * 7)  # fake slopes address
+
+
+def alibi(pairing=2, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, slopes=S_, B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4,
+             dtype=0)
+    a.update(kw)
+    return rac.lib().attn_alibi_causal_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                           a["Hq"], a["Hkv"], a["N"], a["D"], a["slopes"],
+                                           a["base"], pairing, a["dtype"], None)
+
+
+@pytest.mark.parametrize("pairing", [0, 1, 2])
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_alibi_rejects_bad_arguments(kw, code, pairing):
+    assert alibi(pairing, **kw) == code
+    assert rac.last_error() != ""
+
+
+def test_alibi_argument_rules():
+    assert alibi(slopes=None) == rac.RAC_ERR_ARG
+    assert "slopes" in rac.last_error()
+    assert alibi(slopes=ctypes.c_void_p(P * 7 + 2)) == rac.RAC_ERR_ALIGN
+    assert alibi(slopes=ctypes.c_void_p(4 * P + 64)) == rac.RAC_ERR_ARG      # inside out
+    assert alibi(slopes=ctypes.c_void_p(5 * P + 16)) == rac.RAC_ERR_ARG      # inside lse
+    assert alibi(3) == rac.RAC_ERR_ARG and "pairing" in rac.last_error()
+    assert alibi(-1) == rac.RAC_ERR_ARG
+    # rope_base matters only with a rotation
+    assert alibi(0, base=0.0) == rac.RAC_ERR_ARG and "rope_base" in rac.last_error()
+    assert alibi(1, base=float("nan")) == rac.RAC_ERR_ARG
+    assert alibi(2, base=0.0, B=0) == rac.RAC_OK
+    assert alibi(2, N=0, slopes=None, q=None) == rac.RAC_OK
+    assert rac.last_error() == ""

@@ -142,9 +142,11 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const uint16_t* kbase, const uint1
 // ROPE: 0 = K not rotated, 1 = adjacent pairs (2i, 2i+1), 2 = half-split
 // pairs (d, d + D/2). With the half-split pairing a chunk's partner (same row,
 // logical chunk XOR D/16) lands in the same 1 KiB block, loaded by lane
-// XOR D/16 of the same instruction; each of the two lanes prefetches half of
-// the pair's 16 table floats, they swap halves, and each rotates its own chunk
-// from both chunks in LDS.
+// XOR D/16 of the same instruction. The two lanes split the chunk pair's 8
+// element pairs: the lane of the first-half chunk turns pairs 0-3, its partner
+// lane pairs 4-7, each prefetching exactly the 8 table floats of its 4
+// frequencies and reading and writing only its own 8-byte halves of the two
+// chunks, so the lanes share no data.
 template <int DT, int D, int ROPE, int NW>
 struct TileStage {
     typedef Tile<D> T;
@@ -198,20 +200,14 @@ struct TileStage {
                 constexpr int X = T::CH / 2;  // partner lane / chunk offset
                 const int g = blk * 64 + lane;
                 const bool lo = ((g % T::CH) ^ kswz<D>(g / T::CH)) < X;
-                f32x4 other[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        other[h][e] = __shfl_xor(cs[j][h][e], X);
-                const f32x4 tab[4] = {lo ? cs[j][0] : other[0], lo ? cs[j][1] : other[1],
-                                      lo ? other[0] : cs[j][0], lo ? other[1] : cs[j][1]};
-                const u32x4 own = *p;
-                const u32x4 partner =
-                    *reinterpret_cast<const u32x4*>(buf + blk * 512 + (lane ^ X) * 8);
-                u32x4 a, b;
-                rope_rotate_half8<DT>(lo ? own : partner, lo ? partner : own, tab, a, b);
-                *p = lo ? a : b;
+                // first-half chunk's lane: pairs 0-3; partner lane: pairs 4-7
+                uint16_t* blk0 = buf + blk * 512;
+                u32x2* pa = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? 0 : X)) * 8 + (lo ? 0 : 4));
+                u32x2* pb = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? X : 0)) * 8 + (lo ? 0 : 4));
+                u32x2 a = *pa, b = *pb;
+                rope_rotate_half4<DT>(a, b, cs[j][0], cs[j][1]);
+                *pa = a;
+                *pb = b;
             }
         }
     }

@@ -60,6 +60,17 @@ __device__ __forceinline__ typename Fmt<DT>::vec8 as_vec8(u32x4 w) {
     return __builtin_bit_cast(typename Fmt<DT>::vec8, w);
 }
 
+// One RoPE turn of the pair (a, b) by the angle with cosine c and sine s,
+// counter-clockwise, in fp32 with one fused multiply-add per output:
+//   a' = a*c - b*s,  b' = a*s + b*c.
+// Every rotation routine below is built from it, so all of them (and every
+// kernel that uses them) produce the same bits for the same pair.
+__device__ __forceinline__ void rope_turn(float a, float b, float c, float s, float& a2,
+                                          float& b2) {
+    a2 = __builtin_fmaf(a, c, -(b * s));
+    b2 = __builtin_fmaf(a, s, b * c);
+}
+
 // RoPE on 8 consecutive elements (4 adjacent pairs) of one row.
 // x: the 8 elements as 4 packed words; cs: the row's table entries for these
 // pairs, (cos, sin) interleaved. Pair (x0, x1) turns counter-clockwise:
@@ -75,9 +86,8 @@ __device__ __forceinline__ u32x4 rope_rotate8(u32x4 x, f32x4 cs_lo, f32x4 cs_hi)
     const float s[4] = {cs_lo[1], cs_lo[3], cs_hi[1], cs_hi[3]};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        float x0 = F::lo(x[t]), x1 = F::hi(x[t]);
-        float a = __builtin_fmaf(x0, c[t], -(x1 * s[t]));
-        float b = __builtin_fmaf(x0, s[t], x1 * c[t]);
+        float a, b;
+        rope_turn(F::lo(x[t]), F::hi(x[t]), c[t], s[t], a, b);
         y[t] = F::pack2(a, b);
     }
     return y;
@@ -109,12 +119,34 @@ __device__ __forceinline__ void rope_rotate_half8(u32x4 lo, u32x4 hi, const f32x
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const int j0 = 2 * t, j1 = 2 * t + 1;
-        lo_out[t] = F::pack2(__builtin_fmaf(a[j0], c[j0], -(b[j0] * s[j0])),
-                             __builtin_fmaf(a[j1], c[j1], -(b[j1] * s[j1])));
-        hi_out[t] = F::pack2(__builtin_fmaf(a[j0], s[j0], b[j0] * c[j0]),
-                             __builtin_fmaf(a[j1], s[j1], b[j1] * c[j1]));
+        float a0, b0, a1, b1;
+        rope_turn(a[2 * t], b[2 * t], c[2 * t], s[2 * t], a0, b0);
+        rope_turn(a[2 * t + 1], b[2 * t + 1], c[2 * t + 1], s[2 * t + 1], a1, b1);
+        lo_out[t] = F::pack2(a0, a1);
+        hi_out[t] = F::pack2(b0, b1);
     }
+}
+
+// Half of rope_rotate_half8: 4 elements d0 .. d0+3 of the first half (lo)
+// and their partners d0 + D/2 .. +3 (hi), with the table entries of those 4
+// frequencies, (cos, sin) interleaved in cs_lo, cs_hi; rotated in place.
+template <int DT>
+__device__ __forceinline__ void rope_rotate_half4(u32x2& lo, u32x2& hi, f32x4 cs_lo,
+                                                  f32x4 cs_hi) {
+    typedef Fmt<DT> F;
+    const float c[4] = {cs_lo[0], cs_lo[2], cs_hi[0], cs_hi[2]};
+    const float s[4] = {cs_lo[1], cs_lo[3], cs_hi[1], cs_hi[3]};
+    u32x2 a_out, b_out;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float a0, b0, a1, b1;
+        rope_turn(F::lo(lo[t]), F::lo(hi[t]), c[2 * t], s[2 * t], a0, b0);
+        rope_turn(F::hi(lo[t]), F::hi(hi[t]), c[2 * t + 1], s[2 * t + 1], a1, b1);
+        a_out[t] = F::pack2(a0, a1);
+        b_out[t] = F::pack2(b0, b1);
+    }
+    lo = a_out;
+    hi = b_out;
 }
 
 }  // namespace rac

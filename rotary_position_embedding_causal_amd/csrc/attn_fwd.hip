@@ -154,10 +154,10 @@ struct TileStage {
     f32x4 cs[ROPE ? INSTR : 1][2];
 
     // Loads block j (0 <= j < INSTR) of this wave's share: one 1 KiB block of
-    // K, one of V, and (ROPE) the cos/sin entries of the K block. `wave` must
-    // be wave-uniform.
-    __device__ __forceinline__ void issue_part(int j, uint16_t* buf, const TileRsrc& rs,
-                                               int wave, int lane) {
+    // K into kbuf, one of V into vbuf, and (ROPE) the cos/sin entries of the K
+    // block. `wave` must be wave-uniform.
+    __device__ __forceinline__ void issue_part(int j, uint16_t* kbuf, uint16_t* vbuf,
+                                               const TileRsrc& rs, int wave, int lane) {
         const int blk = wave * INSTR + j;
         const int g = blk * 64 + lane;          // chunk index inside the tile
         const int row = g / T::CH;
@@ -165,10 +165,10 @@ struct TileStage {
         const int lc = pc ^ kswz<D>(row);       // logical chunk
         const int kel = row * D + 8 * lc;       // element offsets in the tile
         const int vel = row * D + 8 * (pc ^ vswz<D>(row));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void*)(buf + blk * 512), 16, kel * 2,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void*)(kbuf + blk * 512), 16, kel * 2,
                                                  0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(buf + T::K_ELEMS + blk * 512),
-                                                 16, vel * 2, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(vbuf + blk * 512), 16, vel * 2,
+                                                 0, 0, 0);
         if (ROPE) {
             // adjacent: the 8 floats of this chunk's 4 pairs; half-split: this
             // lane's half (8 floats) of the 16 of frequencies 8 (lc mod CH/2) ..
@@ -181,9 +181,10 @@ struct TileStage {
         }
     }
 
-    __device__ __forceinline__ void issue(uint16_t* buf, const TileRsrc& rs, int wave, int lane) {
+    __device__ __forceinline__ void issue(uint16_t* kbuf, uint16_t* vbuf, const TileRsrc& rs,
+                                          int wave, int lane) {
 #pragma unroll
-        for (int j = 0; j < INSTR; ++j) issue_part(j, buf, rs, wave, lane);
+        for (int j = 0; j < INSTR; ++j) issue_part(j, kbuf, vbuf, rs, wave, lane);
     }
 
     // ROPE only: rotate the K chunks this thread loaded. Call after its loads
@@ -218,7 +219,8 @@ struct TileStage {
 // matrix work instead of stalling the wave between tiles.
 struct NextLoads {
     bool active;  // false: nothing to load
-    uint16_t* buf;
+    uint16_t* kbuf;
+    uint16_t* vbuf;
     TileRsrc rs;
     int wave, lane;
 };
@@ -319,6 +321,9 @@ struct WaveAttn {
     // chain issues at full rate through accumulator forwarding). With LOADS,
     // one block of the next tile's loads follows every second MFMA of the
     // second half, so their issue overlaps matrix work.
+    // The K operands are read from LDS two MFMA steps ahead of their use, and
+    // the two 32-key halves form two independent accumulator chains, so a
+    // single wave keeps the matrix pipe busy on its own.
     // With ALIBI the accumulators start at the penalty in raw-score units,
     // m sqrt(D) (key - row) for this lane's row and keys (key k0 + 32 kb +
     // 8 (j >> 2) + 4 hh + (j & 3) for element j), so the scores leave the
@@ -330,25 +335,37 @@ struct WaveAttn {
         if (ALIBI) base = slope_raw * (float)(k0 + 4 * hh - row);
         __builtin_amdgcn_s_setprio(1);  // matrix phase first when waves share a SIMD
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 s[b][kb][j] = ALIBI ? __builtin_fmaf(slope_raw,
                                                      (float)(32 * kb + 8 * (j >> 2) + (j & 3)), base)
                                     : 0.f;
+        constexpr int PD = 2;  // MFMA steps the operand reads run ahead
+        u32x4 fk[QCH][2];
+        auto read_k = [&](int c) {
 #pragma unroll
-            for (int c = 0; c < QCH; ++c) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(
+            for (int kb = 0; kb < 2; ++kb)
+                fk[c][kb] = *reinterpret_cast<const u32x4*>(
                     Ks + (32 * kb + n) * D + 8 * ((2 * c + hh) ^ kswz<D>(n)));
-                s[b][kb] = F::mfma(as_vec8<DT>(a), qf[b][c], s[b][kb]);
-                if (LOADS && kb == 1 && next.active) {
-                    // Stage::INSTR / QCH blocks per MFMA step
-                    constexpr int PER = (Stage::INSTR + QCH - 1) / QCH;
+        };
 #pragma unroll
-                    for (int j = 0; j < PER; ++j)
-                        if (c * PER + j < Stage::INSTR)
-                            stage.issue_part(c * PER + j, next.buf, next.rs, next.wave, next.lane);
-                }
+        for (int c = 0; c < PD; ++c) read_k(c);
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            if (c + PD < QCH) read_k(c + PD);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[b][kb] = F::mfma(as_vec8<DT>(fk[c][kb]), qf[b][c], s[b][kb]);
+            if (LOADS && next.active) {
+                // Stage::INSTR / QCH blocks per MFMA step
+                constexpr int PER = (Stage::INSTR + QCH - 1) / QCH;
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (c * PER + j < Stage::INSTR)
+                        stage.issue_part(c * PER + j, next.kbuf, next.vbuf, next.rs, next.wave,
+                                         next.lane);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -421,7 +438,8 @@ struct WaveAttn {
         }
     }
 
-    // O^T += V^T P^T for block b (V tile at Vs).
+    // O^T += V^T P^T for block b (V tile at Vs). The V^T operands are read two
+    // MFMAs ahead of their use; the D/32 output blocks are independent chains.
     __device__ __forceinline__ void pv(int b, const uint16_t* Vs, int lane) {
         // transpose-read lane geometry (see lds_read_tr16): each 16-lane group
         // reads 4 rows x 4 elements; rows repeat every 8, so the swizzle is fixed
@@ -430,32 +448,36 @@ struct WaveAttn {
         const int v_lane_c = 2 * (grp & 1) + ((j16 & 3) >> 1);
         const int v_lane_e = 4 * (j16 & 1);
         const int v_lane_sw = vswz<D>(v_lane_row);
+        constexpr int NM = 4 * DBLK;  // MFMAs: key step (kb, e) major, output block i minor
+        constexpr int PD = 2;         // MFMAs the operand reads run ahead
+        u32x4 fv[NM];
+        auto read_v = [&](int m) {
+            const int kb = m / (2 * DBLK), e = (m / DBLK) & 1, i = m % DBLK;
+            const uint16_t* vp = Vs + (32 * kb + 16 * e) * D;
+            const int off = v_lane_row * D + 8 * ((4 * i + v_lane_c) ^ v_lane_sw) + v_lane_e;
+            const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + off));
+            const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * D + off));
+            fv[m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int m = 0; m < PD; ++m) read_v(m);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const vec8 pb = as_vec8<DT>(pw[b][kb][e]);
-                const uint16_t* vp = Vs + (32 * kb + 16 * e) * D;
-#pragma unroll
-                for (int i = 0; i < DBLK; ++i) {
-                    const int off = v_lane_row * D + 8 * ((4 * i + v_lane_c) ^ v_lane_sw) + v_lane_e;
-                    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vp + off));
-                    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vp + 8 * D + off));
-                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                    acc[b][i] = F::mfma(as_vec8<DT>(a), pb, acc[b][i]);
-                }
-            }
+        for (int m = 0; m < NM; ++m) {
+            if (m + PD < NM) read_v(m + PD);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+            const int kb = m / (2 * DBLK), e = (m / DBLK) & 1, i = m % DBLK;
+            acc[b][i] = F::mfma(as_vec8<DT>(fv[m]), as_vec8<DT>(pw[b][kb][e]), acc[b][i]);
+        }
         __builtin_amdgcn_s_setprio(0);
     }
 
-    // One key tile for all blocks: keys k0 .. k0+63, K at Ks, V at Ks + K_ELEMS;
+    // One key tile for all blocks: keys k0 .. k0+63, K at Ks, V at Vs;
     // q_first = the wave's first row. MASK: the tile reaches past q_first.
     template <bool MASK>
-    __device__ __forceinline__ void step(const uint16_t* Ks, int k0, int q_first, int n, int hh,
-                                         int lane, float scale_log2, Stage& stage,
-                                         const NextLoads& next) {
-        const uint16_t* Vs = Ks + T::K_ELEMS;
+    __device__ __forceinline__ void step(const uint16_t* Ks, const uint16_t* Vs, int k0,
+                                         int q_first, int n, int hh, int lane, float scale_log2,
+                                         Stage& stage, const NextLoads& next) {
         if (QB == 1) {
             score<true>(0, Ks, n, hh, k0, q_first + n, stage, next);
             softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
@@ -471,6 +493,24 @@ struct WaveAttn {
             rescale(1);
             pv(1, Vs, lane);
         }
+    }
+
+    // The same tile half a step later (one 32-row block): first PV of the
+    // previous tile's probabilities (V at Vprev, if `prev`), then this tile's
+    // scores and softmax; its PV is left for the next call (or a final pv()).
+    // A wave that runs this schedule while the other wave on its SIMD runs
+    // step() does its matrix work while that wave computes its softmax, and
+    // the other way round.
+    template <bool MASK>
+    __device__ __forceinline__ void step_lag(const uint16_t* Ks, const uint16_t* Vprev, bool prev,
+                                             int k0, int q_first, int n, int hh, int lane,
+                                             float scale_log2, Stage& stage,
+                                             const NextLoads& next) {
+        static_assert(QB == 1, "the lagged schedule takes one row block per wave");
+        if (prev) pv(0, Vprev, lane);
+        score<true>(0, Ks, n, hh, k0, q_first + n, stage, next);
+        softmax<MASK>(0, k0, q_first + n, hh, scale_log2);
+        rescale(0);
     }
 
     // O = acc / l and LSE = ln2 * (m + log2 l) for block b's row of this
@@ -531,7 +571,15 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
     typedef Tile<D> T;
     constexpr int WPH = 4 / QB;  // waves per head
     typedef WaveAttn<DT, D, RM, QB, WPH * HG> W;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
+    // With two heads, the second head's waves (which share SIMDs with the
+    // first head's) run the lagged schedule; they still read the previous
+    // tile's V while the next tile loads, hence three V buffers.
+    constexpr bool LAG = HG == 2 && QB == 1;
+    constexpr int NVB = LAG ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::K_ELEMS + NVB * T::V_ELEMS];
+    auto kbuf = [&](int t) { return smem + (t & 1) * T::K_ELEMS; };
+    auto vbuf = [&](int t) { return smem + 2 * T::K_ELEMS + (t % NVB) * T::V_ELEMS; };
+    auto vprev = [&](int t) { return vbuf(t + NVB - 1); };  // tile t - 1's V buffer
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;         // 0 .. WPH * HG - 1: every wave loads a share of each tile
@@ -558,23 +606,40 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
 
     typename W::Stage stage;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
-    stage.issue(smem, tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
+    // (from the thread index, not the wave-uniform copy: as a divergent-looking
+    // branch both schedules share one register allocation, which fits in 256
+    // VGPRs; as a scalar branch the compiler allocates them apart and spills)
+    const bool lag = LAG && wave >= WPH;
+    stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
     for (int t = 0; t < n_tiles; ++t) {
-        uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
+        uint16_t* Ks = kbuf(t);
         wait_all_loads();              // this wave's part of tile t has landed
         stage.rotate(Ks, uwave, lane);  // RoPE on the K chunks this thread loaded
-        __syncthreads();               // tile t complete; the other buffer is no longer read
-        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS,
+        __syncthreads();               // tile t complete; the buffers tile t+1 takes are free
+        const NextLoads next{t + 1 < n_tiles, kbuf(t + 1), vbuf(t + 1),
                              tile_rsrc<D>(kbase, vbase, table, t + 1, N), uwave, lane};
+        const bool mask = t * BN + BN - 1 > qw0;  // tile reaches past the wave's first row
         if (t < wave_tiles) {
-            if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
-            else
-                st.template step<false>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
-        } else if (next.active) {
-            stage.issue(next.buf, next.rs, uwave, lane);
+            if (lag) {
+                if (mask)
+                    st.template step_lag<true>(Ks, vprev(t), t > 0, t * BN, qw0, n, hh, lane,
+                                               scale_log2, stage, next);
+                else
+                    st.template step_lag<false>(Ks, vprev(t), t > 0, t * BN, qw0, n, hh, lane,
+                                                scale_log2, stage, next);
+            } else if (mask) {
+                st.template step<true>(Ks, vbuf(t), t * BN, qw0, n, hh, lane, scale_log2, stage,
+                                       next);
+            } else {
+                st.template step<false>(Ks, vbuf(t), t * BN, qw0, n, hh, lane, scale_log2, stage,
+                                        next);
+            }
+        } else {
+            if (lag && t == wave_tiles && t > 0) st.pv(0, vprev(t), lane);  // pending PV
+            if (next.active) stage.issue(next.kbuf, next.vbuf, next.rs, uwave, lane);
         }
     }
+    if (lag && wave_tiles == n_tiles && n_tiles > 0) st.pv(0, vbuf(n_tiles - 1), lane);
     if (wave_tiles == 0) return;
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -604,6 +669,8 @@ __global__ __launch_bounds__(512, 1) void attn_pair_heads_kernel(
     typedef Tile<D> T;
     typedef WaveAttn<DT, D, RM, 1, 8> W;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::BUF_ELEMS];
+    auto kbuf = [&](int t) { return smem + (t & 1) * T::BUF_ELEMS; };
+    auto vbuf = [&](int t) { return smem + (t & 1) * T::BUF_ELEMS + T::K_ELEMS; };
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -632,21 +699,23 @@ __global__ __launch_bounds__(512, 1) void attn_pair_heads_kernel(
 
     typename W::Stage stage;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
-    stage.issue(smem, tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
+    stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
     for (int t = 0; t < n_tiles; ++t) {
-        uint16_t* Ks = smem + (t & 1) * T::BUF_ELEMS;
+        uint16_t* Ks = kbuf(t);
         wait_all_loads();              // this wave's part of tile t has landed
         stage.rotate(Ks, uwave, lane);  // RoPE on the K chunks this thread loaded
         __syncthreads();               // tile t complete; the other buffer is no longer read
-        const NextLoads next{t + 1 < n_tiles, smem + ((t + 1) & 1) * T::BUF_ELEMS,
+        const NextLoads next{t + 1 < n_tiles, kbuf(t + 1), vbuf(t + 1),
                              tile_rsrc<D>(kbase, vbase, table, t + 1, N), uwave, lane};
         if (t < wave_tiles) {
             if (t * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
+                st.template step<true>(Ks, vbuf(t), t * BN, qw0, n, hh, lane, scale_log2, stage,
+                                       next);
             else
-                st.template step<false>(Ks, t * BN, qw0, n, hh, lane, scale_log2, stage, next);
+                st.template step<false>(Ks, vbuf(t), t * BN, qw0, n, hh, lane, scale_log2, stage,
+                                        next);
         } else if (next.active) {
-            stage.issue(next.buf, next.rs, uwave, lane);
+            stage.issue(next.kbuf, next.vbuf, next.rs, uwave, lane);
         }
     }
     if (wave_tiles == 0) return;
@@ -667,8 +736,15 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     typedef Tile<D> T;
     typedef WaveAttn<DT, D, RM, QB> W;
     constexpr int HT = 256 / QB;  // threads per half
-    // per half: two tile buffers; after the loop the same memory holds the merge data
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * T::BUF_ELEMS];
+    // Half B runs the lagged schedule (its waves share SIMDs with half A's):
+    // it reads the previous tile's V while the next tile loads, so it keeps
+    // three V buffers. Half A: K0 K1 V0 V1; half B: K0 K1 V0 V1 V2. After the
+    // loop the same memory holds the merge data.
+    constexpr bool LAG = QB == 1;
+    constexpr int NVB_B = LAG ? 3 : 2;
+    constexpr int A_ELEMS = 2 * T::K_ELEMS + 2 * T::V_ELEMS;
+    __shared__ __attribute__((aligned(16)))
+    uint16_t smem[A_ELEMS + 2 * T::K_ELEMS + NVB_B * T::V_ELEMS];
 
     const int tid = threadIdx.x;
     // wave-uniform by construction; readfirstlane lets the compiler see it,
@@ -715,22 +791,33 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     int cur_qt = -1;   // query tile whose rows this wave holds
     int qw0 = 0, wave_tiles = 0;
 
-    uint16_t* hbuf = smem + half * 2 * T::BUF_ELEMS;
+    uint16_t* hbuf = smem + half * A_ELEMS;
+    const int nvb = half == 1 ? NVB_B : 2;
+    const bool lag = LAG && tid >= HT;  // half B (see attn_fwd_kernel on the register use)
+    auto kbuf = [&](int i) { return hbuf + (i & 1) * T::K_ELEMS; };
+    auto vbuf = [&](int i) { return hbuf + 2 * T::K_ELEMS + (i % nvb) * T::V_ELEMS; };
+    auto vprev = [&](int i) { return vbuf(i + nvb - 1); };  // step i - 1's V buffer
+    bool pending = false;  // lag: the previous step's probabilities still await their PV
     typename W::Stage stage;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
     {
         int qt;
         const int kt = job_tile(0, qt);
-        if (kt >= 0) stage.issue(hbuf, tile_rsrc<D>(kbase, vbase, table, kt, N), uwave, lane);
+        if (kt >= 0)
+            stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, kt, N), uwave, lane);
     }
     for (int i = 0; i < steps; ++i) {
         int qt;
         const int kt = job_tile(i, qt);
-        uint16_t* Ks = hbuf + (i & 1) * T::BUF_ELEMS;
+        uint16_t* Ks = kbuf(i);
         wait_all_loads();  // this wave's part of the half's tile i has landed
         if (kt >= 0) stage.rotate(Ks, uwave, lane);
         if (kt >= 0 && qt != cur_qt) {
             // half B moving from the light rows to the heavy rows: finish the light rows
+            if (pending) {
+                st.pv(0, vprev(i), lane);
+                pending = false;
+            }
             if (cur_qt >= 0 && wave_tiles > 0) {
 #pragma unroll
                 for (int b = 0; b < QB; ++b) {
@@ -747,20 +834,37 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
             st.load_q(qhead, table, qw0, N, n, hh);
             st.reset();
         }
-        __syncthreads();  // tile i complete in both halves; their other buffers are free
+        __syncthreads();  // tile i complete in both halves; the buffers of tile i+1 are free
         int qt1;
         const int kt1 = job_tile(i + 1, qt1);
-        const NextLoads next{i + 1 < steps && kt1 >= 0, hbuf + ((i + 1) & 1) * T::BUF_ELEMS,
+        const NextLoads next{i + 1 < steps && kt1 >= 0, kbuf(i + 1), vbuf(i + 1),
                              tile_rsrc<D>(kbase, vbase, table, kt1 < 0 ? 0 : kt1, N), uwave, lane};
+        const bool mask = kt * BN + BN - 1 > qw0;  // tile reaches past the wave's first row
         if (kt >= 0 && kt < wave_tiles) {
-            if (kt * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, kt * BN, qw0, n, hh, lane, scale_log2, stage, next);
-            else
-                st.template step<false>(Ks, kt * BN, qw0, n, hh, lane, scale_log2, stage, next);
-        } else if (next.active) {
-            stage.issue(next.buf, next.rs, uwave, lane);
+            if (lag) {
+                if (mask)
+                    st.template step_lag<true>(Ks, vprev(i), pending, kt * BN, qw0, n, hh, lane,
+                                               scale_log2, stage, next);
+                else
+                    st.template step_lag<false>(Ks, vprev(i), pending, kt * BN, qw0, n, hh, lane,
+                                                scale_log2, stage, next);
+                pending = true;
+            } else if (mask) {
+                st.template step<true>(Ks, vbuf(i), kt * BN, qw0, n, hh, lane, scale_log2, stage,
+                                       next);
+            } else {
+                st.template step<false>(Ks, vbuf(i), kt * BN, qw0, n, hh, lane, scale_log2,
+                                        stage, next);
+            }
+        } else {
+            if (pending) {
+                st.pv(0, vprev(i), lane);
+                pending = false;
+            }
+            if (next.active) stage.issue(next.kbuf, next.vbuf, next.rs, uwave, lane);
         }
     }
+    if (pending) st.pv(0, vprev(steps), lane);  // the last step's PV
 
     // half B: if its last rows were the light ones, they are complete now
     if (half == 1 && cur_qt == t_light && t_light != t_heavy) {

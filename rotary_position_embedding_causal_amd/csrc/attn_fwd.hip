@@ -801,10 +801,16 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     typename W::Stage stage;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
     {
+        // the first rows' Q loads go out together with the first tile's
         int qt;
         const int kt = job_tile(0, qt);
-        if (kt >= 0)
+        if (kt >= 0) {
+            cur_qt = qt;
+            qw0 = qt * BM + wave * 32 * QB;
+            wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
+            st.load_q(qhead, table, qw0, N, n, hh);
             stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, kt, N), uwave, lane);
+        }
     }
     for (int i = 0; i < steps; ++i) {
         int qt;
@@ -813,7 +819,11 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
         wait_all_loads();  // this wave's part of the half's tile i has landed
         if (kt >= 0) stage.rotate(Ks, uwave, lane);
         if (kt >= 0 && qt != cur_qt) {
-            // half B moving from the light rows to the heavy rows: finish the light rows
+            // new rows (half B moving from the light rows to the heavy rows, or
+            // a half whose first job comes late): their Q loads go out first,
+            // so that the latency overlaps the old rows' last PV and write
+            const int qw_new = qt * BM + wave * 32 * QB;
+            st.load_q(qhead, table, qw_new, N, n, hh);
             if (pending) {
                 st.pv(0, vprev(i), lane);
                 pending = false;
@@ -829,9 +839,8 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
                 }
             }
             cur_qt = qt;
-            qw0 = qt * BM + wave * 32 * QB;
+            qw0 = qw_new;
             wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
-            st.load_q(qhead, table, qw0, N, n, hh);
             st.reset();
         }
         __syncthreads();  // tile i complete in both halves; the buffers of tile i+1 are free

@@ -19,6 +19,9 @@ Also printed in the same JSON line:
   * crossover: fused vs pre-rotation (and split) times over the D=64 fp16
     MHA sweep (N = 2048 .. 32768) and the GQA shapes, with the measured
     crossover N* of fused vs pre-rotation;
+  * variants: the half-split RoPE pairing (fused and pre-rotated) and the
+    ALiBi score modification (alone and with fused RoPE), timed after the
+    step loop and not part of `value`;
   * cpu_baseline: the fp64 CPU oracle timed on this host over the full
     workload (rotation + causal attention), in the same unit.
 
@@ -313,12 +316,47 @@ def main():
         "paths": paths,
     }
 
+    result["variants"] = variants(torch, rac, w, qd, kd, vd, ev, args.steps)
     result["backward"] = backward(torch, rac, w, qd, kd, vd, out_f, lse_f, ev, args.steps)
     if not args.no_sweep:
         result["crossover"] = crossover(torch, rac, inputs, dev, ev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(inputs, w)
     print(json.dumps(result), flush=True)
+
+
+def variants(torch, rac, w, qd, kd, vd, ev, reps):
+    """The other RoPE pairing and the ALiBi score modification on the bench
+    workload, after the timed region (not part of `value`): half-split pairs
+    fused and pre-rotated, ALiBi alone and composed with fused RoPE (slopes
+    2^(-8(h+1)/Hq)). Median of `reps` warm calls each."""
+    base = w["base"]
+    Hq = w["Hq"]
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)],
+                          dtype=torch.float32, device=qd.device)
+    fns = {
+        "fused_half_pairs": lambda: rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half"),
+        "rope_prerotate_half_pairs": lambda: rac.rope_prerotate_ex(qd, kd, base, "half"),
+        "alibi": lambda: rac.attn_alibi_causal_fwd(qd, kd, vd, slopes),
+        "alibi_fused_rope": lambda: rac.attn_alibi_causal_fwd(qd, kd, vd, slopes, rope_base=base),
+    }
+    fl = attn_flops(w)
+    res = {}
+    for key, fn in fns.items():
+        warm(fn, 3, WARM_SECONDS, torch.cuda.synchronize)
+        pairs = [(ev(), ev()) for _ in range(reps)]
+        for a, b in pairs:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in pairs)
+        ms = ts[len(ts) // 2]
+        if key.startswith("rope_"):
+            pb = prerot_bytes(w)
+            res[key] = {"ms": ms, "gbs": pb / ms / 1e6, "hbm_frac": pb / ms / 1e6 / HBM_PEAK_GBS}
+        else:
+            res[key] = {"ms": ms, "tflops": fl / ms / 1e9,
+                        "mfma_frac": fl / ms / 1e9 / MFMA_PEAK_TFLOPS[w["dtype"]]}
+    return res
 
 
 def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):

@@ -188,27 +188,43 @@ struct TileStage {
     }
 
     // ROPE only: rotate the K chunks this thread loaded. Call after its loads
-    // have completed (s_waitcnt) and before the block's barrier.
+    // have completed (s_waitcnt) and before the block's barrier. All reads
+    // are issued before the first write, so their latencies overlap.
     __device__ __forceinline__ void rotate(uint16_t* buf, int wave, int lane) {
         if (ROPE == 0) return;
+        if (ROPE == 1) {
+            u32x4 x[INSTR];
 #pragma unroll
-        for (int j = 0; j < INSTR; ++j) {
-            const int blk = wave * INSTR + j;
-            u32x4* p = reinterpret_cast<u32x4*>(buf + blk * 512 + lane * 8);
-            if (ROPE == 1) {
-                *p = rope_rotate8<DT>(*p, cs[j][0], cs[j][1]);
-            } else {
-                constexpr int X = T::CH / 2;  // partner lane / chunk offset
+            for (int j = 0; j < INSTR; ++j)
+                x[j] = *reinterpret_cast<const u32x4*>(buf + (wave * INSTR + j) * 512 + lane * 8);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < INSTR; ++j)
+                *reinterpret_cast<u32x4*>(buf + (wave * INSTR + j) * 512 + lane * 8) =
+                    rope_rotate8<DT>(x[j], cs[j][0], cs[j][1]);
+        } else {
+            constexpr int X = T::CH / 2;  // partner lane / chunk offset
+            u32x2* pa[INSTR];
+            u32x2* pb[INSTR];
+            u32x2 a[INSTR], b[INSTR];
+#pragma unroll
+            for (int j = 0; j < INSTR; ++j) {
+                const int blk = wave * INSTR + j;
                 const int g = blk * 64 + lane;
                 const bool lo = ((g % T::CH) ^ kswz<D>(g / T::CH)) < X;
                 // first-half chunk's lane: pairs 0-3; partner lane: pairs 4-7
                 uint16_t* blk0 = buf + blk * 512;
-                u32x2* pa = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? 0 : X)) * 8 + (lo ? 0 : 4));
-                u32x2* pb = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? X : 0)) * 8 + (lo ? 0 : 4));
-                u32x2 a = *pa, b = *pb;
-                rope_rotate_half4<DT>(a, b, cs[j][0], cs[j][1]);
-                *pa = a;
-                *pb = b;
+                pa[j] = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? 0 : X)) * 8 + (lo ? 0 : 4));
+                pb[j] = reinterpret_cast<u32x2*>(blk0 + (lane ^ (lo ? X : 0)) * 8 + (lo ? 0 : 4));
+                a[j] = *pa[j];
+                b[j] = *pb[j];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < INSTR; ++j) {
+                rope_rotate_half4<DT>(a[j], b[j], cs[j][0], cs[j][1]);
+                *pa[j] = a[j];
+                *pb[j] = b[j];
             }
         }
     }

@@ -53,6 +53,7 @@ namespace bwd {
 
 constexpr int BR = 128;  // stationary query rows per dQ-pass workgroup (4 waves x 32)
 constexpr int BT = 64;   // rows of a streamed tile
+constexpr int NUM_CUS = 256;
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -386,9 +387,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // operands, so two waves fit on a SIMD (wave w and w + 4 share one), where a
 // wave holding both accumulators would run alone; S is computed by both
 // roles.
+// With QS > 1 the workgroup holds QS such groups of 2*RW waves on the same
+// keys: group c takes the query tiles c, c + QS, c + 2QS, ... of the walk,
+// each with its own stream buffers, and at the end the groups' partial dK
+// and dV are added in a fixed order through LDS (still one writer per
+// element and deterministic). The heaviest key tiles then finish QS times
+// sooner when there are too few workgroups to keep every CU busy.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int RM, int RW>
-__global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kernel(
+template <int DT, int D, int RM, int RW, int QS>
+__global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
@@ -399,12 +406,14 @@ __global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kerne
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 2 * RW> S;
     constexpr int TILE = BT * D;
-    // Q0 dO0 Q1 dO1, then per buffer 64 scaled L and 64 Delta values
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
-    __shared__ __attribute__((aligned(16))) float rows_lds[2][2 * BT];
+    // per query group: Q0 dO0 Q1 dO1, and per buffer 64 scaled L and 64 Delta values
+    __shared__ __attribute__((aligned(16))) uint16_t smem[QS * 4 * TILE];
+    __shared__ __attribute__((aligned(16))) float rows_lds[QS][2][2 * BT];
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qg = wave_wg / (2 * RW);   // query group
+    const int wave = wave_wg % (2 * RW);  // wave inside its group
     const bool dk_role = wave >= RW;
     const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int bg, slot;
@@ -420,17 +429,21 @@ __global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kerne
     const int t0 = (kt * KW) / BT;
     const int per_head = (N - 1) / BT + 1 - t0;
     const int steps = per_head * group;
+    const int rounds = (steps + QS - 1) / QS;  // group qg takes step s * QS + qg of round s
     auto job = [&](int i, int& qh, int& tq) {
         qh = g * group + i / per_head;
         tq = t0 + i % per_head;
     };
+    uint16_t* gbuf = smem + qg * 4 * TILE;
 
     S st;
-    auto start = [&](int i) {
+    auto start = [&](int s) {
+        const int i = s * QS + qg;
+        if (i >= steps) return;
         int qh, tq;
         job(i, qh, tq);
         const int64_t qhead = ((int64_t)b * Hq + qh) * N;
-        uint16_t* a = smem + (i & 1) * 2 * TILE;
+        uint16_t* a = gbuf + (s & 1) * 2 * TILE;
         st.issue(a, a + TILE, rows_rsrc(q + qhead * D, D, tq, N),
                  rows_rsrc(dout + qhead * D, D, tq, N),
                  rows_rsrc(table, ROPE ? D : 0, tq, N), wave, lane);
@@ -449,16 +462,19 @@ __global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kerne
 #pragma unroll
         for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
         start(0);
-        for (int i = 0; i < steps; ++i) {
-            int qh, tq;
-            job(i, qh, tq);
-            uint16_t* Qs = smem + (i & 1) * 2 * TILE;
+        for (int s = 0; s < rounds; ++s) {
+            const int i = s * QS + qg;
+            const bool live = i < steps;  // the last round may leave a group idle
+            int qh = 0, tq = 0;
+            if (live) job(i, qh, tq);
+            uint16_t* Qs = gbuf + (s & 1) * 2 * TILE;
             const uint16_t* dOs = Qs + TILE;
-            float* rl = rows_lds[i & 1];
+            float* rl = rows_lds[qg][s & 1];
             wait_all_loads();
-            st.finish(Qs, rl, true, wave, lane);
-            __syncthreads();  // step i complete; the other buffers are no longer read
-            if (i + 1 < steps) start(i + 1);
+            if (live) st.finish(Qs, rl, true, wave, lane);
+            __syncthreads();  // round s complete; the other buffers are no longer read
+            if (s + 1 < rounds) start(s + 1);
+            if (!live) continue;
             const int q0 = tq * BT;
             if (kw0 >= N) continue;           // the wave has no keys
             if (q0 + BT - 1 < kw0) continue;  // every query of the tile precedes the wave's keys
@@ -489,6 +505,25 @@ __global__ __launch_bounds__(128 * RW, RW == 2 ? 2 : 1) void attn_bwd_dkdv_kerne
                 W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
             }
         }
+        if constexpr (QS > 1) {
+            // groups 1.. hand their partial sums to group 0 through LDS, in order
+            static_assert(QS == 2, "one partner group");
+            constexpr int SLOTS = 16 * W::DBLK;
+            float* red = reinterpret_cast<float*>(smem) + (wave * SLOTS) * 64 + lane;
+            __syncthreads();  // every group is done with its stream buffers
+            if (qg == 1) {
+#pragma unroll
+                for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) red[(16 * i + j) * 64] = acc[i][j];
+            }
+            __syncthreads();
+            if (qg != 0) return;
+#pragma unroll
+            for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[i][j] += red[(16 * i + j) * 64];
+        }
         if (key < N) {
             if (DK)
                 W::write(acc, scale, dk + (kvhead + key) * D,
@@ -509,7 +544,8 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int n_qtiles = (a.N + BR - 1) / BR;
     // dK/dV pass: 128 keys per workgroup (8 waves), or 64 (4 waves) when that
-    // leaves fewer workgroups than CUs
+    // leaves fewer workgroups than CUs; and with at most two 64-key
+    // workgroups per CU, two query groups per workgroup (8 waves)
     const int64_t k_units_128 = (int64_t)((a.N + 127) / 128) * a.Hkv * a.B;
     const int rw = k_units_128 >= 256 ? 4 : 2;
     const int n_ktiles = (a.N + 32 * rw - 1) / (32 * rw);
@@ -528,11 +564,15 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (rw == 4)
-        attn_bwd_dkdv_kernel<DT, D, RM, 4><<<dim3((unsigned)k_units), 512, 0, stream>>>(
+        attn_bwd_dkdv_kernel<DT, D, RM, 4, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
+            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+    else if (k_units <= 2 * NUM_CUS)
+        attn_bwd_dkdv_kernel<DT, D, RM, 2, 2><<<dim3((unsigned)k_units), 512, 0, stream>>>(
             q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
             static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
     else
-        attn_bwd_dkdv_kernel<DT, D, RM, 2><<<dim3((unsigned)k_units), 256, 0, stream>>>(
+        attn_bwd_dkdv_kernel<DT, D, RM, 2, 1><<<dim3((unsigned)k_units), 256, 0, stream>>>(
             q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
             static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
     return hipGetLastError();

@@ -72,8 +72,11 @@
  * Launch shape: the attention kernels pick between a load-balanced launch
  * that pairs light and heavy causal query tiles in one workgroup and one
  * workgroup per query tile, by problem size. The environment variable
- * RAC_ATTN_SHAPE=pair|tile forces one of them (results are identical up to
- * floating-point summation order); any other value, or none, means automatic.
+ * RAC_ATTN_SHAPE=pair|tile|pairheads forces one of them (results are
+ * identical up to floating-point summation order); any other value, or none,
+ * means automatic. Likewise RAC_BWD_SHAPE=k128|k64|k64x2 forces the backward
+ * key-parallel pass's workgroup shape (128 keys, 64 keys, or 64 keys with two
+ * query groups).
  *
  * Library-owned memory: the cos/sin table for each (device, D, rope_base),
  * fp32 [capacity, D], grown on demand. The first call that needs a new or

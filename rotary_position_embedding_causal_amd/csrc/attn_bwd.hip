@@ -547,7 +547,9 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     // leaves fewer workgroups than CUs; and with at most two 64-key
     // workgroups per CU, two query groups per workgroup (8 waves)
     const int64_t k_units_128 = (int64_t)((a.N + 127) / 128) * a.Hkv * a.B;
-    const int rw = k_units_128 >= 256 ? 4 : 2;
+    int rw = k_units_128 >= 256 ? 4 : 2;
+    if (a.shape == BWD_SHAPE_K128) rw = 4;
+    if (a.shape == BWD_SHAPE_K64 || a.shape == BWD_SHAPE_K64X2) rw = 2;
     const int n_ktiles = (a.N + 32 * rw - 1) / (32 * rw);
     const int64_t q_units = (int64_t)n_qtiles * a.Hq * a.B;
     const int64_t k_units = (int64_t)n_ktiles * a.Hkv * a.B;
@@ -567,7 +569,7 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
         attn_bwd_dkdv_kernel<DT, D, RM, 4, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
             q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
             static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
-    else if (k_units <= 2 * NUM_CUS)
+    else if (a.shape == BWD_SHAPE_K64X2 || (a.shape != BWD_SHAPE_K64 && k_units <= 2 * NUM_CUS))
         attn_bwd_dkdv_kernel<DT, D, RM, 2, 2><<<dim3((unsigned)k_units), 512, 0, stream>>>(
             q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
             static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);

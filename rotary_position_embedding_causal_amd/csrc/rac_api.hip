@@ -179,6 +179,15 @@ int attn_shape_from_env() {
     return rac::ATTN_SHAPE_AUTO;
 }
 
+int bwd_shape_from_env() {
+    const char* e = getenv("RAC_BWD_SHAPE");
+    if (!e) return rac::BWD_SHAPE_AUTO;
+    if (!strcmp(e, "k128")) return rac::BWD_SHAPE_K128;
+    if (!strcmp(e, "k64")) return rac::BWD_SHAPE_K64;
+    if (!strcmp(e, "k64x2")) return rac::BWD_SHAPE_K64X2;
+    return rac::BWD_SHAPE_AUTO;
+}
+
 // ---- the path dispatcher ------------------------------------------------------
 //
 // All three paths give bit-identical results (they hand the same rotated
@@ -255,7 +264,8 @@ int attn_bwd_common(const void* q, const void* k, const void* v, const void* out
     if (rc != RAC_OK) return rc;
     if (rot == rac::ROT_QK && (rc = check_base(rope_base)) != RAC_OK) return rc;
     if (empty) return ok();
-    rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype};
+    rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype,
+                   bwd_shape_from_env()};
     if ((rc = check_bwd_ptrs(a)) != RAC_OK) return rc;
     if (rot == rac::ROT_QK && (rc = get_table(D, rope_base, N, &a.table)) != RAC_OK) return rc;
     return hip_status(rac::launch_attn_bwd(a, rot, static_cast<hipStream_t>(stream)), what);

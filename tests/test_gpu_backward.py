@@ -6,7 +6,8 @@ backward (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd) on small shapes
 spanning several tiles with ragged tails, GQA ratios 1-8, D = 64 and 128,
 bf16 and fp16; the inverse rotation pass on its own; determinism; and one key/
 value group of the Llama-3-8B-shaped layer at full length (N = 2048) in the
-launch configuration the bench times. Bounds: parity.assert_grad.
+launch configuration the bench times. The small cases run under every
+key-parallel workgroup shape (RAC_BWD_SHAPE). Bounds: parity.assert_grad.
 """
 import numpy as np
 import pytest
@@ -28,6 +29,13 @@ def _gpu():
     rac.lib()
     yield
     torch.cuda.synchronize()
+
+
+@pytest.fixture(params=["auto", "k128", "k64", "k64x2"])
+def bwd_shape(request, monkeypatch):
+    """Runs a test under each key-parallel workgroup shape (RAC_BWD_SHAPE)."""
+    monkeypatch.setenv("RAC_BWD_SHAPE", request.param)
+    return request.param
 
 
 SHAPES = [  # B, Hq, Hkv, N, D, dtype, base
@@ -55,9 +63,9 @@ def _case(B, Hq, Hkv, N, D, dt, base, key):
 
 @pytest.mark.parametrize("shape", SHAPES, ids=_id)
 @pytest.mark.parametrize("path", ["fused", "prerotate"])
-def test_backward_matches_oracle(shape, path):
+def test_backward_matches_oracle(shape, path, bwd_shape):
     B, Hq, Hkv, N, D, dt, base = shape
-    print("backward %s %s" % (path, _id(shape)), flush=True)
+    print("backward %s %s %s" % (path, _id(shape), bwd_shape), flush=True)
     (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (401, N, D))
     fn = rac.attn_rope_causal_bwd if path == "fused" else rac.prerotate_path_bwd
     dq, dk, dv, delta = fn(qd, kd, vd, o, lse, dod, base)
@@ -71,7 +79,7 @@ def test_backward_matches_oracle(shape, path):
 
 
 @pytest.mark.parametrize("shape", SHAPES[:4], ids=_id)
-def test_paths_agree_and_are_deterministic(shape):
+def test_paths_agree_and_are_deterministic(shape, bwd_shape):
     B, Hq, Hkv, N, D, dt, base = shape
     _, (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (402, N, D))
     f1 = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
@@ -129,7 +137,7 @@ def test_rope_prerotate_bwd_is_the_inverse_rotation(shape):
 
 @pytest.mark.parametrize("N", [2, 63, 64, 65, 127, 129])
 @pytest.mark.parametrize("ratio", [1, 4, 8])
-def test_ragged_lengths_and_gqa(N, ratio):
+def test_ragged_lengths_and_gqa(N, ratio, bwd_shape):
     B, Hkv, D, dt, base = 1, 1, 128, "bf16", 10000.0
     Hq = Hkv * ratio
     (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (405, N, ratio))

@@ -1,7 +1,9 @@
 // attn_fwd.hip -- causal MHA/GQA attention forward for gfx950, with RoPE fused
 // into the loads of both Q and K (RM = ROT_QK, or ROT_QK_HALF for the
 // half-split pairing), of Q only (RM = ROT_Q: the GQA split path, K rotated
-// beforehand) or of neither (RM = ROT_NONE).
+// beforehand) or of neither (RM = ROT_NONE); MOD_ALIBI added to the mode
+// puts the ALiBi distance penalty on the scores (it starts the score
+// accumulators, so the softmax is unchanged).
 //
 // Method: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (rainbus digest), background "FlashAttention and online softmax"
@@ -25,8 +27,9 @@
 //     B operand (the key order inside each 16-key step is permuted); the V^T
 //     operand comes from the row-major V tile through the LDS transpose read
 //     (ds_read_b64_tr_b16), gathering keys in that same permuted order.
-//   * Key tiles of BN = 64 rows, double-buffered in LDS with one barrier per
-//     tile. The next tile's K and V go straight from global memory into LDS
+//   * Key tiles of BN = 64 rows, double-buffered in LDS (V triple-buffered
+//     where a wave runs the lagged schedule) with one barrier per tile. The
+//     next tile's K and V go straight from global memory into LDS
 //     (buffer_load_dwordx4 ... lds) while the current tile is computed; with RoPE
 //     each thread also prefetches the cos/sin rows of the K chunks it loads
 //     and rotates them in place before the barrier. Tiles past a wave's last
@@ -34,6 +37,10 @@
 //   * Running-max updates are lazy: a row keeps its maximum until a tile
 //     raises it by more than 2^8, so most tiles skip the accumulator rescale;
 //     probabilities stay <= 2^8 and the final o = u / l and L are unchanged.
+//   * MFMA operands are read from LDS two MFMAs ahead of their use, and in
+//     the two-head tile launch the waves that share a SIMD run half a step
+//     apart (step() / step_lag()), so one's matrix work overlaps the other's
+//     softmax.
 //
 // Two launch shapes share that per-wave core:
 //   * attn_pair_kernel (the default): causal rows see a prefix of the keys, so
@@ -44,8 +51,9 @@
 //     take the same number of steps. The two partial softmax states of the
 //     heavy rows are merged through LDS at the end. Every workgroup then does
 //     the same work, so a grid of one workgroup per CU finishes together.
-//   * attn_fwd_kernel: one 4-wave workgroup per query tile, heaviest first;
-//     used when there are too few tile pairs to fill the chip.
+//   * attn_fwd_kernel: one workgroup per query tile (4 waves, or 8 for the
+//     same tile of two query heads of a GQA group), heaviest first; used when
+//     the grid has enough workgroups (>= 4 per CU) for that order to balance.
 //   * attn_pair_heads_kernel: an 8-wave workgroup takes the 64-row query
 //     tiles T-1-p and p of two query heads of one GQA group (heavy rows on
 //     waves 0-3, light rows on waves 4-7); all four row blocks share every key

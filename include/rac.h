@@ -216,7 +216,7 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
  * path measured fastest on MI355X for this shape -- with GQA the split path
  * at every length; with MHA pre-rotation of Q and K up to N = 6144 and the
  * split path beyond -- never the fused kernel when a workspace is given
- * (rotating every key tile in the kernel cost 16-43 % over plain attention,
+ * (rotating every key tile in the kernel cost 12-43 % over plain attention,
  * more than the streaming pass). The choice of pre-rotation versus in-kernel
  * rotation is the one the AttnFuse report, paragraphs 3 and 5, says depends
  * on the GPU and the shape.

@@ -195,7 +195,7 @@ int bwd_shape_from_env() {
 // only. Measured on MI355X (bench crossover rows, median of 15 calls after a
 // 50 ms warm-up; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) / 8192 and fp16
 // D=64 MHA at N = 2048 .. 32768): the fused kernel was never the fastest --
-// rotating every K tile in the kernel costs 16-43 % over plain attention,
+// rotating every K tile in the kernel costs 12-43 % over plain attention,
 // more than the streaming pass costs; with GQA the split path (K pre-rotated,
 // Q rotated once per row in the kernel) was fastest at every N, by 1-5 % over
 // pre-rotation of Q and K; with MHA pre-rotation was fastest up to N = 6144

@@ -1,8 +1,10 @@
 /*
  * rac.h -- RoPE + causal attention forward on AMD MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels. Five forward operations, a
- * dispatcher, and the backward of both paths:
+ * A C ABI over hand-written HIP kernels: the forward operations of the
+ * fused, pre-rotation and GQA split paths, a dispatcher, the backward of the
+ * fused and pre-rotation paths, a second RoPE pairing and the ALiBi score
+ * modification:
  *
  *   attn_rope_causal_fwd  one kernel: rotary position embedding applied to the
  *                         query and key tiles inside a causal attention
@@ -23,6 +25,11 @@
  *                         whichever of the three paths is fastest for the
  *                         shape on MI355X (the report's paragraph 5: the
  *                         choice is measured per architecture and shape).
+ *   rope_prerotate_ex, attn_rope_causal_fwd_ex
+ *                         the pass and the fused kernel with the half-split
+ *                         RoPE pairing (i, i + D/2) as an alternative.
+ *   attn_alibi_causal_fwd causal attention with the ALiBi distance penalty
+ *                         after the QK product, alone or with fused RoPE.
  *
  * The two paths and the choice between them are the subject of "AttnFuse Makes
  * RoPE a First-Class Attention Compilation Operation" (tdteach paper-news,

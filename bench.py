@@ -10,8 +10,8 @@ before timing starts; steps run back to back on torch's current stream.
 
 Also printed in the same JSON line:
   * roofline: the fused attention kernel (the dominant kernel), achieved
-    TFLOP/s from HIP events around each of its launches in the timed region,
-    against the dense bf16 MFMA peak;
+    TFLOP/s from HIP events around each of its launches in the timed region
+    (the only events recorded there), against the dense bf16 MFMA peak;
   * paths: per-path and per-kernel times (warm, and cold after a 512 MiB
     cache flush), TFLOP/s, % of MFMA peak, rope_prerotate GB/s vs 8 TB/s;
     also the GQA split path (rope_prerotate_k then attn_rope_q_causal_fwd),
@@ -229,20 +229,29 @@ def main():
     # ---- the timed region: K steps of the whole hot path ----
     # warm-up: W steps, and at least WARM_SECONDS of them
     warm(lambda: (fused(), rope(), attn()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
+    # HIP events only around the fused launches (the roofline kernel): each
+    # event record is a packet of its own on the GPU's queue, and recording
+    # around every kernel of the step added ~20 us per step
     fused_ev = [(ev(), ev()) for _ in range(args.steps)]
-    rope_ev = [(ev(), ev()) for _ in range(args.steps)]
-    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         fused_ev[i][0].record(); fused(); fused_ev[i][1].record()
-        rope_ev[i][0].record(); rope(); rope_ev[i][1].record()
-        attn_ev[i][0].record(); attn(); attn_ev[i][1].record()
+        rope()
+        attn()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
 
     def avg_ms(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    # the pre-rotation path's two kernels, timed the same way after the step loop
+    rope_ev = [(ev(), ev()) for _ in range(args.steps)]
+    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        rope_ev[i][0].record(); rope(); rope_ev[i][1].record()
+        attn_ev[i][0].record(); attn(); attn_ev[i][1].record()
+    torch.cuda.synchronize()
 
     fl = attn_flops(w)
     t_fused = avg_ms(fused_ev)

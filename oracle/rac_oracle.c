@@ -33,6 +33,12 @@
  *   then l_i = sum_j exp(s_ij - M_i), o_i = sum_j exp(s_ij - M_i) v_j / l_i,
  *   L_i = M_i + ln l_i (natural log). No tiling, no online rescaling.
  *
+ *   ALiBi. Same digest, same background section: a linear penalty on the
+ *   attention score that grows with the distance between query and key. The
+ *   reading taken: s_ij = tau * q_i . k_j - m_h * (i - j) with one slope m_h
+ *   per query head, then the same causal softmax (its own routine,
+ *   oracle_attn_alibi_rows).
+ *
  *   Storage formats. bf16 and fp16 inputs are decoded exactly to fp64, and
  *   fp64 values are rounded to bf16/fp16 once, round-to-nearest-even, by this
  *   file's own code (the "rounded rotation" variant of the oracle).

@@ -275,6 +275,38 @@ def test_large_sigma_inputs(sigma, path, launch_shape):
     assert lerr <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
 
 
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+@pytest.mark.parametrize("D,dt", [(64, "fp16"), (64, "bf16"), (128, "fp16"), (128, "bf16")])
+def test_large_sigma_attention_arithmetic(sigma, D, dt, launch_shape):
+    """Large scores with the oracle's own rounded rotation as the kernel's
+    input (attn_causal_fwd), so that any LSE difference comes from the
+    attention arithmetic alone. With RoPE in the kernel, the fp32 rotation
+    rounds a small fraction of operand elements (at most 0.1 %, as the
+    rotation tests require) to the other neighbour of the exact value than
+    the oracle's fp64 rotation does; at sigma = 4-8 one such element moves a
+    score by ~ulp(|x|) |x| / sqrt(D), which can exceed the LSE bound, so the
+    paths with RoPE are stressed at D = 128 bf16 (test_large_sigma_inputs),
+    where they stay inside it."""
+    B, Hq, Hkv, N, base = 1, 4, 2, 384, 500000.0
+    q = inputs.draw((B, Hq, N, D), dt, (109,), 0, sigma)
+    k = inputs.draw((B, Hkv, N, D), dt, (109,), 1, sigma)
+    v = inputs.draw((B, Hkv, N, D), dt, (109,), 2)
+    qr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(inputs.bits(q), dt), base), dt)
+    kr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(inputs.bits(k), dt), base), dt)
+    tdt = inputs.TORCH_DTYPES[dt]
+    qd = torch.from_numpy(qr_bits.view(np.int16)).view(tdt).to(DEV)
+    kd = torch.from_numpy(kr_bits.view(np.int16)).view(tdt).to(DEV)
+    o, l = rac.attn_causal_fwd(qd, kd, v.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+    ro, rl = oracle.attention(oracle.decode(qr_bits, dt), oracle.decode(kr_bits, dt),
+                              oracle.decode(inputs.bits(v), dt))
+    assert_o(to_f64(o), ro, "sigma=%g D=%d %s" % (sigma, D, dt))
+    lerr = float(np.max(np.abs(to_f64(l) - rl)))
+    print("sigma=%g D=%d %s: max|dLSE|=%.3e" % (sigma, D, dt, lerr))
+    assert lerr <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
+
+
 def test_deterministic(launch_shape):
     _, (qd, kd, vd) = _inputs(1, 8, 2, 777, 128, "bf16", key=(109,))
     a = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)

@@ -10,10 +10,13 @@ before timing starts; steps run back to back on torch's current stream.
 
 Also printed in the same JSON line:
   * roofline: the fused attention kernel (the dominant kernel), achieved
-    TFLOP/s from HIP events around each of its launches in the timed region
-    (the only events recorded there), against the dense bf16 MFMA peak;
-  * paths: per-path and per-kernel times (warm, and cold after a 512 MiB
-    cache flush), TFLOP/s, % of MFMA peak, rope_prerotate GB/s vs 8 TB/s;
+    TFLOP/s from a pair of HIP events that each of its launches in the timed
+    region records at the kernel's own start and end (rac.time_next_kernel,
+    hipExtLaunchKernel on the launch stream), against the dense bf16 MFMA
+    peak;
+  * paths: per-kernel times taken the same way (warm, and cold after a
+    512 MiB cache flush) and their sums per path, TFLOP/s, % of MFMA peak,
+    rope_prerotate GB/s vs 8 TB/s;
     also the GQA split path (rope_prerotate_k then attn_rope_q_causal_fwd),
     timed after the step loop and not part of `value`;
   * crossover: fused vs pre-rotation (and split) times over the D=64 fp16
@@ -226,17 +229,24 @@ def main():
         print(json.dumps({"only": args.only, "workload": name, "ms_per_call": dt * 1e3}))
         return
 
+    def made(pairs):
+        """Creates the events up front (torch creates one at its first record)."""
+        for a, b in pairs:
+            a.record(); b.record()
+        torch.cuda.synchronize()
+        return pairs
+
     # ---- the timed region: K steps of the whole hot path ----
     # warm-up: W steps, and at least WARM_SECONDS of them
     warm(lambda: (fused(), rope(), attn()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
-    # HIP events only around the fused launches (the roofline kernel): each
-    # event record is a packet of its own on the GPU's queue, and recording
-    # around every kernel of the step added ~20 us per step
-    fused_ev = [(ev(), ev()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # each fused launch (the roofline kernel) records a pair of HIP events at
+    # its own start and end (rac.time_next_kernel: hipExtLaunchKernel on the
+    # launch stream), so no event packet of its own enters the queue and the
+    # time excludes the dispatch latency
+    fused_ev = made([(ev(), ev()) for _ in range(args.steps)])
     t0 = time.perf_counter()
     for i in range(args.steps):
-        fused_ev[i][0].record(); fused(); fused_ev[i][1].record()
+        rac.time_next_kernel(*fused_ev[i]); fused()
         rope()
         attn()
     torch.cuda.synchronize()
@@ -246,11 +256,11 @@ def main():
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
     # the pre-rotation path's two kernels, timed the same way after the step loop
-    rope_ev = [(ev(), ev()) for _ in range(args.steps)]
-    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
+    rope_ev = made([(ev(), ev()) for _ in range(args.steps)])
+    attn_ev = made([(ev(), ev()) for _ in range(args.steps)])
     for i in range(args.steps):
-        rope_ev[i][0].record(); rope(); rope_ev[i][1].record()
-        attn_ev[i][0].record(); attn(); attn_ev[i][1].record()
+        rac.time_next_kernel(*rope_ev[i]); rope()
+        rac.time_next_kernel(*attn_ev[i]); attn()
     torch.cuda.synchronize()
 
     fl = attn_flops(w)
@@ -265,11 +275,11 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def cold(fn, reps=20):
+        """Median kernel time of fn's (single) kernel after a cache flush."""
         ts = []
-        for _ in range(reps):
+        for a, b in made([(ev(), ev()) for _ in range(reps)]):
             flush.zero_()
-            a, b = ev(), ev()
-            a.record(); fn(); b.record()
+            rac.time_next_kernel(a, b); fn()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
         ts.sort()
@@ -280,11 +290,11 @@ def main():
 
     # ---- the GQA split path, timed the same way after the timed region ----
     warm(lambda: (rope_k(), attn_q()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
-    rk_ev = [(ev(), ev()) for _ in range(args.steps)]
-    aq_ev = [(ev(), ev()) for _ in range(args.steps)]
+    rk_ev = made([(ev(), ev()) for _ in range(args.steps)])
+    aq_ev = made([(ev(), ev()) for _ in range(args.steps)])
     for i in range(args.steps):
-        rk_ev[i][0].record(); rope_k(); rk_ev[i][1].record()
-        aq_ev[i][0].record(); attn_q(); aq_ev[i][1].record()
+        rac.time_next_kernel(*rk_ev[i]); rope_k()
+        rac.time_next_kernel(*aq_ev[i]); attn_q()
     torch.cuda.synchronize()
     t_rk, t_aq = avg_ms(rk_ev), avg_ms(aq_ev)
     c_rk, c_aq = cold(rope_k), cold(attn_q)
@@ -338,7 +348,8 @@ def variants(torch, rac, w, qd, kd, vd, ev, reps):
     """The other RoPE pairing and the ALiBi score modification on the bench
     workload, after the timed region (not part of `value`): half-split pairs
     fused and pre-rotated, ALiBi alone and composed with fused RoPE (slopes
-    2^(-8(h+1)/Hq)). Median of `reps` warm calls each."""
+    2^(-8(h+1)/Hq)). Median of `reps` warm calls each, as the kernel's own
+    start-to-end time (rac.time_next_kernel)."""
     base = w["base"]
     Hq = w["Hq"]
     slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)],
@@ -355,7 +366,10 @@ def variants(torch, rac, w, qd, kd, vd, ev, reps):
         warm(fn, 3, WARM_SECONDS, torch.cuda.synchronize)
         pairs = [(ev(), ev()) for _ in range(reps)]
         for a, b in pairs:
-            a.record(); fn(); b.record()
+            a.record(); b.record()
+        torch.cuda.synchronize()
+        for a, b in pairs:  # each call is one kernel: its own start and end
+            rac.time_next_kernel(a, b); fn()
         torch.cuda.synchronize()
         ts = sorted(a.elapsed_time(b) for a, b in pairs)
         ms = ts[len(ts) // 2]
@@ -397,10 +411,11 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
     """Fused vs pre-rotation path time per shape; N* where their order flips.
 
     Each path is warmed up for 50 ms, then timed as the median of `reps`
-    back-to-back calls, each bracketed by HIP events on the launch stream.
-    Also per shape: the GQA split path, the dispatcher (with a workspace for
-    its preferred path), and rope_prerotate bandwidth warm and cold (after a
-    512 MiB cache flush, larger than the 256 MB MALL)."""
+    back-to-back calls, each bracketed by HIP events on the launch stream
+    (so both paths' times include their launches). Also per shape: the GQA
+    split path, the dispatcher (with a workspace for its preferred path), and
+    rope_prerotate bandwidth warm and cold (after a 512 MiB cache flush,
+    larger than the 256 MB MALL) from its kernel's own start and end."""
     rows = []
     names = ["mha_d64_fp16_n%d" % n for n in inputs.SWEEP_NS] + [
         "llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192"]
@@ -437,14 +452,21 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
             torch.cuda.synchronize()
             ts = sorted(a.elapsed_time(b) for a, b in pairs)
             t[key] = ts[len(ts) // 2]
-        cold = []
-        for _ in range(reps):
-            flush.zero_()
-            a, b = ev(), ev()
-            a.record(); fns["rope"](); b.record()
-            torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
+        # the streaming pass's bandwidth: its kernel's own start-to-end time
+        # (rac.time_next_kernel), warm and after a cache flush
+        warm_k, cold = [], []
+        for flushed, out_ in ((False, warm_k), (True, cold)):
+            for _ in range(reps):
+                a, b = ev(), ev()
+                a.record(); b.record()
+                if flushed:
+                    flush.zero_()
+                rac.time_next_kernel(a, b); fns["rope"]()
+                torch.cuda.synchronize()
+                out_.append(a.elapsed_time(b))
+        warm_k.sort()
         cold.sort()
+        t["rope"] = warm_k[len(warm_k) // 2]
         t_rope_cold = cold[len(cold) // 2]
         fl = attn_flops(w)
         pb = prerot_bytes(w)

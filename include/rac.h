@@ -223,7 +223,7 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
  * path measured fastest on MI355X for this shape -- with GQA the split path
  * at every length; with MHA pre-rotation of Q and K up to N = 6144 and the
  * split path beyond -- never the fused kernel when a workspace is given
- * (rotating every key tile in the kernel cost 12-43 % over plain attention,
+ * (rotating every key tile in the kernel cost 11-43 % over plain attention,
  * more than the streaming pass). The choice of pre-rotation versus in-kernel
  * rotation is the one the AttnFuse report, paragraphs 3 and 5, says depends
  * on the GPU and the shape.
@@ -300,6 +300,19 @@ const char* rac_last_error(void);
 /* Synchronises every device holding a table, then frees all cos/sin tables.
  * Returns RAC_OK or RAC_ERR_HIP. */
 int rac_release_tables(void);
+
+/* Kernel timing (instrumentation; defines no part of the method). Arms a
+ * pair of HIP events (hipEvent_t handles, created by the caller with timing
+ * enabled, owned by the caller) for the next forward attention or
+ * pre-rotation kernel this library launches from the calling thread: that
+ * kernel is launched with hipExtLaunchKernel, which records `start_event`
+ * and `stop_event` at the kernel's own start and end on its stream, so
+ * hipEventElapsedTime gives its execution time without the queue's dispatch
+ * latency. The events are disarmed once used; an entry point that makes
+ * several launches (the dispatcher's two-kernel paths) times the first.
+ * Backward kernels ignore the timer. Both NULL disarms.
+ * Returns RAC_OK, or RAC_ERR_ARG if exactly one event is NULL. */
+int rac_time_next_kernel(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

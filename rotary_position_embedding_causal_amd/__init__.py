@@ -37,7 +37,7 @@ EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_p
             "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
             "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
-            "rac_last_error", "rac_release_tables")
+            "rac_last_error", "rac_release_tables", "rac_time_next_kernel")
 RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
 PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
 RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.rac_last_error.restype = ctypes.c_char_p
     L.rac_release_tables.argtypes = []
     L.rac_release_tables.restype = i
+    L.rac_time_next_kernel.argtypes = [vp, vp]
+    L.rac_time_next_kernel.restype = i
     _lib = L
     return L
 
@@ -115,6 +117,22 @@ def check(rc: int, what: str) -> None:
 
 def release_tables() -> None:
     check(lib().rac_release_tables(), "rac_release_tables")
+
+
+def time_next_kernel(start, stop) -> None:
+    """Arms two torch.cuda.Event(enable_timing=True) objects to record the
+    start and end of the next forward attention or pre-rotation kernel this
+    thread launches (the kernel's own execution, without dispatch latency);
+    read it with start.elapsed_time(stop) after synchronising. None, None
+    disarms."""
+    if start is None and stop is None:
+        check(lib().rac_time_next_kernel(None, None), "rac_time_next_kernel")
+        return
+    for ev in (start, stop):
+        if ev.cuda_event == 0:  # torch creates its event at the first record
+            ev.record()
+    check(lib().rac_time_next_kernel(ctypes.c_void_p(start.cuda_event),
+                                     ctypes.c_void_p(stop.cuda_event)), "rac_time_next_kernel")
 
 
 def _ptr(t):

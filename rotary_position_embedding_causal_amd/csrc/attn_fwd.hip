@@ -51,6 +51,8 @@
 //     take the same number of steps. The two partial softmax states of the
 //     heavy rows are merged through LDS at the end. Every workgroup then does
 //     the same work, so a grid of one workgroup per CU finishes together.
+//     While half B is on the light rows, both halves work on the same key
+//     tile each step; half A alone loads (and rotates) it.
 //   * attn_fwd_kernel: one workgroup per query tile (4 waves, or 8 for the
 //     same tile of two query heads of a GQA group), heaviest first; used when
 //     the grid has enough workgroups (>= 4 per CU) for that order to balance.
@@ -805,6 +807,10 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     // per half: K0 K1 V0 V1; after the loop the same memory holds the merge
     // data. (Running half B on the lagged schedule of the tile launch was
     // measured 2.5 % slower here, so both halves run step().)
+    // At step i < len_l both halves need key tile i (half A for the heavy
+    // rows, half B for the light rows): half A alone loads (and with RoPE
+    // rotates) it and half B reads half A's copy, so those steps cost one tile
+    // load and rotation instead of two.
     constexpr int H_ELEMS = 2 * T::K_ELEMS + 2 * T::V_ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * H_ELEMS];
 
@@ -867,15 +873,19 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
             qw0 = qt * BM + wave * 32 * QB;
             wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
             st.load_q(qhead, table, qw0, N, n, hh);
-            stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, kt, N), uwave, lane);
+            if (!(half == 1 && len_l > 0))  // a shared first tile comes from half A
+                stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, kt, N), uwave,
+                            lane);
         }
     }
     for (int i = 0; i < steps; ++i) {
         int qt;
         const int kt = job_tile(i, qt);
-        uint16_t* Ks = kbuf(i);
+        const bool shared = half == 1 && i < len_l;  // key tile i from half A's buffers
+        uint16_t* Ks = shared ? smem + (i & 1) * T::K_ELEMS : kbuf(i);
+        uint16_t* Vs = shared ? smem + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS : vbuf(i);
         wait_all_loads();  // this wave's part of the half's tile i has landed
-        if (kt >= 0) stage.rotate(Ks, uwave, lane);
+        if (kt >= 0 && !shared) stage.rotate(Ks, uwave, lane);
         if (kt >= 0 && qt != cur_qt) {
             // new rows (half B moving from the light rows to the heavy rows, or
             // a half whose first job comes late): their Q loads go out first,
@@ -900,15 +910,16 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
         __syncthreads();  // tile i complete in both halves; the buffers of tile i+1 are free
         int qt1;
         const int kt1 = job_tile(i + 1, qt1);
-        const NextLoads next{i + 1 < steps && kt1 >= 0, kbuf(i + 1), vbuf(i + 1),
+        const bool next_shared = half == 1 && i + 1 < len_l;  // half A loads it
+        const NextLoads next{i + 1 < steps && kt1 >= 0 && !next_shared, kbuf(i + 1), vbuf(i + 1),
                              tile_rsrc<D>(kbase, vbase, table, kt1 < 0 ? 0 : kt1, N), uwave, lane};
         if (kt >= 0 && kt < wave_tiles) {
             if (kt * BN + BN - 1 > qw0)  // tile reaches past the wave's first row
-                st.template step<true>(Ks, vbuf(i), kt * BN, qw0, n, hh, lane, scale_log2, stage,
+                st.template step<true>(Ks, Vs, kt * BN, qw0, n, hh, lane, scale_log2, stage,
                                        next);
             else
-                st.template step<false>(Ks, vbuf(i), kt * BN, qw0, n, hh, lane, scale_log2,
-                                        stage, next);
+                st.template step<false>(Ks, Vs, kt * BN, qw0, n, hh, lane, scale_log2, stage,
+                                        next);
         } else if (next.active) {
             stage.issue(next.kbuf, next.vbuf, next.rs, uwave, lane);
         }
@@ -1000,33 +1011,29 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     if (a.shape == ATTN_SHAPE_PAIR) pair = true;
     if (a.shape == ATTN_SHAPE_TILE) pair = false, pair_heads = false;
     if (a.shape == ATTN_SHAPE_PAIR_HEADS && heads_ok) pair = false, pair_heads = true;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    uint16_t* out = static_cast<uint16_t*>(a.out);
     if (pair_heads) {
         const int n_t64 = (a.N + 63) / 64;
         const int n_pairs64 = (n_t64 + 1) / 2;
         const int64_t units = (int64_t)n_pairs64 * (a.Hq / 2) * a.B;
-        attn_pair_heads_kernel<DT, D, RM><<<dim3((unsigned)units), 512, 0, stream>>>(
-            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.slopes, a.Hq, a.Hkv, a.N, n_t64, n_pairs64, scale_log2);
-    } else if (pair) {
-        attn_pair_kernel<DT, D, RM, QB><<<dim3((unsigned)pair_units), 512 / QB, 0, stream>>>(
-            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
-    } else if ((a.Hq / a.Hkv) % 2 == 0) {
-        // GQA: two query heads of a group per workgroup share every key tile
-        attn_fwd_kernel<DT, D, RM, QB, 2><<<dim3((unsigned)(tile_units / 2)), 512 / QB, 0,
-                                             stream>>>(
-            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
-    } else {
-        attn_fwd_kernel<DT, D, RM, QB, 1><<<dim3((unsigned)tile_units), 256 / QB, 0, stream>>>(
-            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-            static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.lse, a.table,
-            a.slopes, a.Hq, a.Hkv, a.N, n_qtiles, scale_log2);
+        return launch_kernel(attn_pair_heads_kernel<DT, D, RM>, dim3((unsigned)units), dim3(512),
+                             stream, q, k, v, out, a.lse, a.table, a.slopes, a.Hq, a.Hkv, a.N,
+                             n_t64, n_pairs64, scale_log2);
     }
-    return hipGetLastError();
+    if (pair)
+        return launch_kernel(attn_pair_kernel<DT, D, RM, QB>, dim3((unsigned)pair_units),
+                             dim3(512 / QB), stream, q, k, v, out, a.lse, a.table, a.slopes, a.Hq,
+                             a.Hkv, a.N, n_qtiles, n_pairs, scale_log2);
+    if ((a.Hq / a.Hkv) % 2 == 0)  // GQA: two query heads of a group share every key tile
+        return launch_kernel(attn_fwd_kernel<DT, D, RM, QB, 2>, dim3((unsigned)(tile_units / 2)),
+                             dim3(512 / QB), stream, q, k, v, out, a.lse, a.table, a.slopes, a.Hq,
+                             a.Hkv, a.N, n_qtiles, scale_log2);
+    return launch_kernel(attn_fwd_kernel<DT, D, RM, QB, 1>, dim3((unsigned)tile_units),
+                         dim3(256 / QB), stream, q, k, v, out, a.lse, a.table, a.slopes, a.Hq,
+                         a.Hkv, a.N, n_qtiles, scale_log2);
 }
 
 template <int DT, int RM>

@@ -36,6 +36,22 @@ int ok() {
     return RAC_OK;
 }
 
+// armed by rac_time_next_kernel(), taken by the next launch_kernel() call
+thread_local hipEvent_t g_timer_start = nullptr;
+thread_local hipEvent_t g_timer_stop = nullptr;
+
+}  // namespace
+
+namespace rac {
+void take_kernel_timer(hipEvent_t* start, hipEvent_t* stop) {
+    *start = g_timer_start;
+    *stop = g_timer_stop;
+    g_timer_start = g_timer_stop = nullptr;
+}
+}  // namespace rac
+
+namespace {
+
 // ---- cos/sin tables --------------------------------------------------------
 //
 // Entry [p][2i] = cos(p * theta_i), [p][2i+1] = sin(p * theta_i), with
@@ -195,9 +211,9 @@ int bwd_shape_from_env() {
 // only. Measured on MI355X (bench crossover rows, median of 15 calls after a
 // 50 ms warm-up; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) / 8192 and fp16
 // D=64 MHA at N = 2048 .. 32768): the fused kernel was never the fastest --
-// rotating every K tile in the kernel costs 12-43 % over plain attention,
+// rotating every K tile in the kernel costs 11-43 % over plain attention,
 // more than the streaming pass costs; with GQA the split path (K pre-rotated,
-// Q rotated once per row in the kernel) was fastest at every N, by 1-5 % over
+// Q rotated once per row in the kernel) was fastest at every N, by 1-7 % over
 // pre-rotation of Q and K; with MHA pre-rotation was fastest up to N = 6144
 // and the split path from N = 8192, where the in-kernel Q rotation is
 // amortised over more key tiles.
@@ -485,6 +501,14 @@ int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out
 }
 
 const char* rac_last_error(void) { return g_last_error.c_str(); }
+
+int rac_time_next_kernel(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(RAC_ERR_ARG, "rac_time_next_kernel: pass both events or neither");
+    g_timer_start = static_cast<hipEvent_t>(start_event);
+    g_timer_stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
+}
 
 int rac_release_tables(void) {
     std::lock_guard<std::mutex> lock(g_mutex);

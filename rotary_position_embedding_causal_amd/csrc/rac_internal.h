@@ -2,10 +2,28 @@
 // kernel translation units. Arguments are already validated by the caller.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace rac {
+
+// Kernel timing: a pair of caller-created HIP events that the next kernel
+// launched through launch_kernel() on this thread records at its own start
+// and end (then the pair is cleared). Null: no timing.
+void take_kernel_timer(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches `kernel` on `stream` (no dynamic LDS), through hipExtLaunchKernel
+// so that an armed kernel timer stamps the kernel's own start and end.
+template <typename... Params, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block,
+                                hipStream_t stream, Args... args) {
+    hipEvent_t start = nullptr, stop = nullptr;
+    take_kernel_timer(&start, &stop);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0,
+                          static_cast<Params>(args)...);
+    return hipGetLastError();
+}
 
 // Launch shape of the attention kernels: chosen from the problem size, or
 // forced (tests cover both shapes on small problems; tuning).

@@ -135,10 +135,10 @@ static hipError_t launch_heads(const void* q, const void* k, void* q_rot, void* 
                                const float* table, int N, int64_t q_slabs, int64_t total,
                                unsigned gx, hipStream_t stream) {
     dim3 grid(gx, (unsigned)((total + H - 1) / H));
-    rope_prerotate_kernel<DT, D, H, INV><<<grid, PR_THREADS, 0, stream>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N, q_slabs, total);
-    return hipGetLastError();
+    return launch_kernel(rope_prerotate_kernel<DT, D, H, INV>, grid, dim3(PR_THREADS), stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N,
+                         q_slabs, total);
 }
 
 // Slabs per lane. Measured kernel times on the Llama-3-8B and D = 64 shapes
@@ -199,10 +199,10 @@ static hipError_t launch_half_heads(const void* q, const void* k, void* q_rot, v
                                     const float* table, int N, int64_t q_slabs, int64_t total,
                                     unsigned gx, hipStream_t stream) {
     dim3 grid(gx, (unsigned)((total + H - 1) / H));
-    rope_prerotate_half_kernel<DT, D, H><<<grid, PR_THREADS, 0, stream>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N, q_slabs, total);
-    return hipGetLastError();
+    return launch_kernel(rope_prerotate_half_kernel<DT, D, H>, grid, dim3(PR_THREADS), stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N,
+                         q_slabs, total);
 }
 
 // Same grid policy as the adjacent pairing, with one lane per chunk pair.

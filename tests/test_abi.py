@@ -357,3 +357,15 @@ def test_alibi_argument_rules():
     assert alibi(2, base=0.0, B=0) == rac.RAC_OK
     assert alibi(2, N=0, slopes=None, q=None) == rac.RAC_OK
     assert rac.last_error() == ""
+
+
+def test_kernel_timer_arguments():
+    """rac_time_next_kernel stores or clears an event pair (no HIP call); a
+    lone event is an argument error."""
+    L_ = rac.lib()
+    assert L_.rac_time_next_kernel(None, None) == rac.RAC_OK
+    assert L_.rac_time_next_kernel(Q, None) == rac.RAC_ERR_ARG
+    assert "both events or neither" in rac.last_error()
+    assert L_.rac_time_next_kernel(None, K) == rac.RAC_ERR_ARG
+    assert L_.rac_time_next_kernel(Q, K) == rac.RAC_OK  # armed (never launched here) ...
+    assert L_.rac_time_next_kernel(None, None) == rac.RAC_OK  # ... and disarmed

@@ -379,3 +379,23 @@ def test_full_size_sampled_rows(name):
     assert_lse(gl, rl, name + " LSE")
     mx, rel = o_errors(got, ro)
     print("%s: rows=%d max|dO|=%.3e relL2=%.3e" % (name, got.shape[0], mx, rel), flush=True)
+
+
+def test_kernel_timer_times_one_launch():
+    """rac_time_next_kernel: the armed launch records the events (a positive
+    kernel time), computes the same bits as an untimed launch, and disarms
+    the events, so a later launch leaves their reading unchanged."""
+    _, (qd, kd, vd) = _inputs(1, 8, 2, 700, 128, "bf16", key=(960,))
+    o1, l1 = rac.attn_rope_causal_fwd(qd, kd, vd, 5e5)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    rac.time_next_kernel(a, b)
+    o2, l2 = rac.attn_rope_causal_fwd(qd, kd, vd, 5e5)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b)
+    assert t > 0.0
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    rac.attn_rope_causal_fwd(qd, kd, vd, 5e5)
+    rac.rope_prerotate(qd, kd, 5e5)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == t

@@ -145,12 +145,19 @@ static hipError_t launch_heads(const void* q, const void* k, void* q_rot, void* 
 // (8 to 320 MiB per call): two slabs per lane was the fastest or within 10 %
 // of it everywhere, while eight (the most table reuse per lane) was up to
 // 15 % slower at the large sizes and 60 % slower with few slabs: the grid's
-// parallelism matters more than the table loads, which stay in cache.
+// parallelism matters more than the table loads, which stay in cache. From
+// 40 to 64 MiB per call four slabs per lane were 2-9 % faster cold and up to
+// 15 % warm (twice the loads in flight per lane; the grid, still at least
+// 1280 workgroups, fits on the chip at once), at 32 MiB with 1024 workgroups
+// 2 % slower, from 128 MiB up 0-2 % slower; a grid-stride loop over (slab,
+// row, chunk) items was 5-20 % slower than either. `bytes` = the call's
+// reads and writes (0: not counted, two slabs).
 // More slabs per lane only where the grid's y extent (<= 65535) needs it;
 // the entry points cap the slab count at 8 * 65535.
-inline int prerotate_heads(int64_t total) {
+inline int prerotate_heads(int64_t total, int64_t bytes = 0, int64_t gx = 0) {
     if (total < 2) return 1;
     int h = 2;
+    if (bytes > 0 && bytes <= (int64_t(64) << 20) && gx * ((total + 3) / 4) >= 1280) h = 4;
     while (h < 8 && (total + h - 1) / h > 65535) h *= 2;
     return h;
 }
@@ -163,7 +170,8 @@ static hipError_t launch_typed(const void* q, const void* k, void* q_rot, void* 
     const int64_t q_slabs = (int64_t)B * Hq;
     const int64_t total = q_slabs + (int64_t)B * Hkv;
     const unsigned gx = (unsigned)((lanes + PR_THREADS - 1) / PR_THREADS);
-    switch (prerotate_heads(total)) {
+    const int64_t bytes = total * N * D * 4;  // 2-byte elements, read and written
+    switch (prerotate_heads(total, bytes, gx)) {
         case 8: return launch_heads<DT, D, 8, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
         case 4: return launch_heads<DT, D, 4, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
         case 2: return launch_heads<DT, D, 2, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);

@@ -96,8 +96,11 @@ def _id(s):
 # rope_prerotate
 # ---------------------------------------------------------------------------
 
+# the last shape (42 slabs, 44 MB per call) takes the pass's four-slabs-per-lane
+# launch, with a partly filled last group of slabs
 @pytest.mark.parametrize("shape", SMALL + [(1, 16, 16, 4096, 64, "fp16", 10000.0),
-                                          (1, 4, 2, 2048, 128, "bf16", 500000.0)], ids=_id)
+                                          (1, 4, 2, 2048, 128, "bf16", 500000.0),
+                                          (1, 36, 6, 2048, 128, "bf16", 500000.0)], ids=_id)
 def test_prerotate_matches_rounded_oracle(shape):
     B, Hq, Hkv, N, D, dt, base = shape
     (q, k, _), (qd, kd, _) = _inputs(B, Hq, Hkv, N, D, dt, key=(101, N, D))

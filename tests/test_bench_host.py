@@ -1,0 +1,43 @@
+"""bench.py's host-side logic, without a GPU: the one-GPU contract, the
+counter summary's tie to the kernel sources, and the FLOP and byte counts
+the roofline and the bandwidth figures divide by."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_attention_flops_are_the_causal_half():
+    # Llama-3-8B layer at N = 2048: 2 * B * Hq * N^2 * D
+    w = dict(B=1, Hq=32, Hkv=8, N=2048, D=128)
+    assert bench.attn_flops(w) == 2 * 32 * 2048 ** 2 * 128 == 34359738368
+
+
+def test_prerotation_bytes_read_and_write_q_and_k_once():
+    w = dict(B=1, Hq=32, Hkv=8, N=2048, D=128, dtype="bf16")
+    assert bench.prerot_bytes(w) == 2 * (32 + 8) * 2048 * 128 * 2  # 40 MiB
+    assert bench.prerot_k_bytes(w) == 2 * 8 * 2048 * 128 * 2       # 8 MiB
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_measured_on(tmp_path, monkeypatch):
+    good = {"source_sha256": bench.attn_source_hash(), "read_bytes": 3.0e7, "write_bytes": 1.7e7}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(good))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic() == pytest.approx(4.7e7)
+    f.write_text(json.dumps(dict(good, source_sha256="0" * 64)))
+    assert bench.measured_traffic() is None
+

@@ -1019,11 +1019,18 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     const int64_t pair_units = (int64_t)n_pairs * a.Hq * a.B;
     const int64_t tile_units = (int64_t)n_qtiles * a.Hq * a.B;
     if (tile_units > 0x7fffffff) return hipErrorInvalidConfiguration;
-    // The pair launch fixes the causal imbalance when the grid has only a few
-    // workgroups per CU; with more, the heaviest-first tile launch balances as
-    // well and keeps more workgroups resident per CU.
-    bool pair = tile_units < 4 * NUM_CUS && pair_units >= NUM_CUS / 2 && n_qtiles >= 2;
+    // The pair launch balances the causal work inside each workgroup but runs
+    // one 8-wave workgroup per CU, so it pays while its workgroups fill at
+    // most one round of the CUs; beyond, the heaviest-first tile launch
+    // balances as well (and, with two heads per workgroup, shares each key
+    // tile among 256 query rows). Without the two-head tile launch (MHA, odd
+    // GQA groups) the pair launch also wins at exactly two full rounds.
+    // Measured on MI355X: D = 64 MHA at N = 8192 (two rounds) pair 3-9 %
+    // faster; at N = 6144 (1.5 rounds) the tile launch 12-14 % faster; from
+    // N = 16384, and for GQA from B * N = 4096, the tile launch faster.
     const bool heads_ok = (a.Hq / a.Hkv) % 2 == 0;
+    bool pair = n_qtiles >= 2 && pair_units >= NUM_CUS / 2 &&
+                (pair_units <= NUM_CUS || (!heads_ok && pair_units == 2 * NUM_CUS));
     // pair_heads (two GQA heads sharing every key tile) only when forced: with
     // K rotated in the kernel it beat the split pair by 3.5 % at N = 2048
     // (0.0616 vs 0.0638 ms), without rotation it lost (0.0512 vs 0.0448 ms),

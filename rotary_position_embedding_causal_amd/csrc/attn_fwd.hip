@@ -49,7 +49,8 @@
 //     tile over the first X key tiles, half B (waves 4-7) runs the light tile
 //     and then the heavy tile's remaining key tiles, X chosen so both halves
 //     take the same number of steps. The two partial softmax states of the
-//     heavy rows are merged through LDS at the end. Every workgroup then does
+//     heavy rows are merged through LDS at the end (each half merging and
+//     writing half of the head dimension). Every workgroup then does
 //     the same work, so a grid of one workgroup per CU finishes together.
 //     While half B is on the light rows, both halves work on the same key
 //     tile each step; half A alone loads (and rotates) it.
@@ -594,13 +595,19 @@ struct WaveAttn {
 
     // O = acc / l and LSE = ln2 * (m + log2 l) for block b's row of this
     // lane; l_tot is the full denominator (both lane halves).
+    // Output blocks i0 .. i1 - 1 only (32 head-dim columns each) with write_part.
     __device__ __forceinline__ void write(int b, uint16_t* orow, float* lse_row, float l_tot,
                                           int hh) {
+        write_part(b, orow, lse_row, l_tot, hh, 0, DBLK);
+    }
+    __device__ __forceinline__ void write_part(int b, uint16_t* orow, float* lse_row, float l_tot,
+                                               int hh, int i0, int i1) {
         const float inv = 1.f / l_tot;
 #pragma unroll
         for (int i = 0; i < DBLK; ++i)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
+                if (i < i0 || i >= i1) continue;
                 const int d0 = 32 * i + 8 * gq + 4 * hh;
                 u32x2 w;
                 w[0] = F::pack2(acc[b][i][4 * gq] * inv, acc[b][i][4 * gq + 1] * inv);
@@ -964,45 +971,50 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
     }
 
     // ---- merge the two halves' partial states of the heavy rows ----
+    // Each half merges and writes half of the output columns: half A blocks
+    // 0 .. DBLK/2 - 1, half B the rest. Each exports to LDS the blocks the
+    // other merges, with its running max and denominator; both evaluate the
+    // same expression, A's state * a_a + B's state * a_b.
     __syncthreads();  // every wave is done with the tile buffers
-    constexpr int SLOTS = 16 * W::DBLK + 2;
-    float* my = reinterpret_cast<float*>(smem) + (wave * QB * SLOTS) * 64 + lane;  // [wave][b][slot][lane]
-    float l_half[QB];
+    constexpr int HB = W::DBLK / 2;     // output blocks per half
+    constexpr int SLOTS = 16 * HB + 2;  // [half][wave][slot][lane]
+    float* xch = reinterpret_cast<float*>(smem);
+    float* mine = xch + ((half * 4 + wave) * SLOTS) * 64 + lane;
+    const float* other = xch + (((1 - half) * 4 + wave) * SLOTS) * 64 + lane;
+    const int own0 = half == 0 ? 0 : HB;  // first block this half merges
+    const float l_half = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
 #pragma unroll
-    for (int b = 0; b < QB; ++b) l_half[b] = st.l_run[b] + __shfl_xor(st.l_run[b], 32);
-    if (half == 1) {
+    for (int i = 0; i < W::DBLK; ++i) {
+        if (i >= own0 && i < own0 + HB) continue;  // kept: exported are the other's blocks
 #pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            float* mb = my + b * SLOTS * 64;
+        for (int j = 0; j < 16; ++j) mine[(16 * (i % HB) + j) * 64] = st.acc[0][i][j];
+    }
+    mine[(16 * HB) * 64] = st.m_run[0];
+    mine[(16 * HB + 1) * 64] = l_half;
+    __syncthreads();
+    const int hq = t_heavy * BM + wave * 32 + n;  // this lane's heavy row
+    if (hq >= N) return;
+    const float m_o = other[(16 * HB) * 64];
+    const float l_o = other[(16 * HB + 1) * 64];
+    const float m_a = half == 0 ? st.m_run[0] : m_o, l_a = half == 0 ? l_half : l_o;
+    const float m_b = half == 0 ? m_o : st.m_run[0], l_b = half == 0 ? l_o : l_half;
+    const float m = fmaxf(m_a, m_b);
+    const float a_a = __builtin_amdgcn_exp2f(m_a - m);
+    const float a_b = l_b > 0.f ? __builtin_amdgcn_exp2f(m_b - m) : 0.f;
 #pragma unroll
-            for (int i = 0; i < W::DBLK; ++i)
+    for (int i = 0; i < W::DBLK; ++i) {
+        if (i < own0 || i >= own0 + HB) continue;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mb[(16 * i + j) * 64] = st.acc[b][i][j];
-            mb[(16 * W::DBLK) * 64] = st.m_run[b];
-            mb[(16 * W::DBLK + 1) * 64] = l_half[b];
+        for (int j = 0; j < 16; ++j) {
+            const float x = other[(16 * (i % HB) + j) * 64];
+            st.acc[0][i][j] = half == 0 ? st.acc[0][i][j] * a_a + x * a_b
+                                        : x * a_a + st.acc[0][i][j] * a_b;
         }
     }
-    __syncthreads();
-    if (half == 1) return;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        const int hq = t_heavy * BM + wave * 32 * QB + 32 * b + n;  // this lane's heavy row
-        if (hq >= N) continue;
-        const float* mb = my + b * SLOTS * 64;
-        const float m_b = mb[(16 * W::DBLK) * 64];
-        const float l_b = mb[(16 * W::DBLK + 1) * 64];
-        const float m = fmaxf(st.m_run[b], m_b);
-        const float a_a = __builtin_amdgcn_exp2f(st.m_run[b] - m);
-        const float a_b = l_b > 0.f ? __builtin_amdgcn_exp2f(m_b - m) : 0.f;
-#pragma unroll
-        for (int i = 0; i < W::DBLK; ++i)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                st.acc[b][i][j] = st.acc[b][i][j] * a_a + mb[(16 * i + j) * 64] * a_b;
-        st.m_run[b] = m;
-        const float l_tot = l_half[b] * a_a + l_b * a_b;
-        st.write(b, out + (q_head + hq) * D, lse ? lse + q_head + hq : nullptr, l_tot, hh);
-    }
+    st.m_run[0] = m;
+    const float l_tot = l_a * a_a + l_b * a_b;
+    st.write_part(0, out + (q_head + hq) * D, half == 0 && lse ? lse + q_head + hq : nullptr,
+                  l_tot, hh, own0, own0 + HB);
 }
 
 // Rows per wave: 32 x QB. One 64-row wave per SIMD (QB = 2) uses the full

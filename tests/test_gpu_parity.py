@@ -348,8 +348,11 @@ def test_empty_inputs():
 # full-size workloads, the launch configuration the bench times
 # ---------------------------------------------------------------------------
 
+# every sweep point: the launch shape changes with the size (pair launch at
+# N = 2048, 4096 and 8192, the tile launch at 6144 and from 16384)
 FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
-        "mha_d64_fp16_n2048", "mha_d64_fp16_n8192", "mha_d64_fp16_n32768"]
+        "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
+        "mha_d64_fp16_n16384", "mha_d64_fp16_n32768"]
 
 
 @pytest.mark.parametrize("name", FULL)

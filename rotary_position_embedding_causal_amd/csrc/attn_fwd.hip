@@ -168,7 +168,8 @@ struct TileStage {
     // K into kbuf, one of V into vbuf, and (ROPE) the cos/sin entries of the K
     // block. `wave` must be wave-uniform.
     __device__ __forceinline__ void issue_part(int j, uint16_t* kbuf, uint16_t* vbuf,
-                                               const TileRsrc& rs, int wave, int lane) {
+                                               const TileRsrc& rs, int wave, int lane,
+                                               bool with_v = true) {
         const int blk = wave * INSTR + j;
         const int g = blk * 64 + lane;          // chunk index inside the tile
         const int row = g / T::CH;
@@ -178,8 +179,9 @@ struct TileStage {
         const int vel = row * D + 8 * (pc ^ vswz<D>(row));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void*)(kbuf + blk * 512), 16, kel * 2,
                                                  0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(vbuf + blk * 512), 16, vel * 2,
-                                                 0, 0, 0);
+        if (with_v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void*)(vbuf + blk * 512), 16,
+                                                     vel * 2, 0, 0, 0);
         if (ROPE) {
             // adjacent: the 8 floats of this chunk's 4 pairs; half-split: this
             // lane's half (8 floats) of the 16 of frequencies 8 (lc mod CH/2) ..
@@ -196,6 +198,12 @@ struct TileStage {
                                           int wave, int lane) {
 #pragma unroll
         for (int j = 0; j < INSTR; ++j) issue_part(j, kbuf, vbuf, rs, wave, lane);
+    }
+    // The "K" rows alone (staging query rows the same way).
+    __device__ __forceinline__ void issue_k(uint16_t* kbuf, const TileRsrc& rs, int wave,
+                                            int lane) {
+#pragma unroll
+        for (int j = 0; j < INSTR; ++j) issue_part(j, kbuf, nullptr, rs, wave, lane, false);
     }
 
     // ROPE only: rotate the K chunks this thread loaded. Call after its loads
@@ -295,6 +303,33 @@ struct WaveAttn {
     // penalty -m (i - j) on the scaled scores; raw scores are sqrt(D) larger).
     __device__ __forceinline__ void set_slope(const float* __restrict__ slopes, int64_t head) {
         if (ALIBI) slope_raw = slopes[head] * __builtin_sqrtf((float)D);
+    }
+
+    // Staged Q rows (block 0): this wave's 32 rows arrive in LDS through the
+    // key-tile path (coalesced loads, chunk swizzle, rotation of the chunks
+    // each lane loaded, with coalesced cos/sin reads), as rows 32 pw .. +31
+    // of a 64-row tile at qbuf shared with the partner wave pw ^ 1; then each
+    // lane reads its MFMA operands. Same rotation routines, same bits as
+    // load_q(); the direct reads of load_q touch 32 table rows per load
+    // instruction, which made the fused kernels' start 4-5 us slower.
+    static constexpr int ROPE_QS = ROPE_Q ? (HALF ? 2 : 1) : 0;
+    typedef TileStage<DT, D, ROPE_QS, 2> QStage;
+    __device__ __forceinline__ void stage_q_issue(QStage& qs, uint16_t* qbuf, const TileRsrc& rs,
+                                                  int pw, int lane) {
+        qs.issue_k(qbuf, rs, pw, lane);
+    }
+    // After this wave's staging loads have completed (s_waitcnt).
+    __device__ __forceinline__ void stage_q_finish(QStage& qs, uint16_t* qbuf, int pw, int lane,
+                                                   int n, int hh) {
+        qs.rotate(qbuf, pw, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const int r = 32 * pw + n;
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            const int pc = (2 * c + hh) ^ kswz<D>(r);
+            qf[0][c] = as_vec8<DT>(*reinterpret_cast<const u32x4*>(qbuf + r * D + 8 * pc));
+        }
     }
 
     // Block 0's Q operands to / from LDS (lane-major per 16-deep step, so a
@@ -897,10 +932,18 @@ __global__ __launch_bounds__(512 / QB, 1) void attn_pair_kernel(
             cur_qt = qt;
             qw0 = qt * BM + wave * 32 * QB;
             wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
-            st.load_q(qhead, table, qw0, N, n, hh);
+            // Q rows staged in the half's second K (waves 0, 1) or V (2, 3)
+            // buffer, free until the first step issues the next tile
+            uint16_t* qbuf = uwave < 2 ? hbuf + T::K_ELEMS
+                                       : hbuf + 2 * T::K_ELEMS + T::V_ELEMS;
+            typename W::QStage qs;
+            st.stage_q_issue(qs, qbuf, tile_rsrc<D>(qhead, qhead, table, (qt * BM) / BN + uwave / 2, N),
+                             uwave & 1, lane);
             if (!(half == 1 && len_l > 0))  // a shared first tile comes from half A
                 stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, kt, N), uwave,
                             lane);
+            wait_all_loads();
+            st.stage_q_finish(qs, qbuf, uwave & 1, lane, n, hh);
             if (QCOPY && half == 0) st.save_q(qcopy + uwave * W::QCH * 64, lane);
         }
     }

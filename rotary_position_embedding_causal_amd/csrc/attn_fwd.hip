@@ -697,7 +697,13 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
     // tile's V while the next tile loads, hence three V buffers.
     constexpr bool LAG = HG == 2 && QB == 1;
     constexpr int NVB = LAG ? 3 : 2;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::K_ELEMS + NVB * T::V_ELEMS];
+    // Q rows are staged through 64-row regions (one per pair of waves): the
+    // second K buffer and the V buffers the first tile does not use, plus one
+    // more region with two heads
+    constexpr int QREG = 2 * HG;                          // staging regions needed
+    constexpr int QEXTRA = QREG - 1 - (NVB - 1);          // beyond K1 and the spare V buffers
+    __shared__ __attribute__((aligned(16)))
+    uint16_t smem[2 * T::K_ELEMS + NVB * T::V_ELEMS + (QEXTRA > 0 ? QEXTRA : 0) * T::K_ELEMS];
     auto kbuf = [&](int t) { return smem + (t & 1) * T::K_ELEMS; };
     auto vbuf = [&](int t) { return smem + 2 * T::K_ELEMS + (t % NVB) * T::V_ELEMS; };
     auto vprev = [&](int t) { return vbuf(t + NVB - 1); };  // tile t - 1's V buffer
@@ -718,20 +724,34 @@ __global__ __launch_bounds__(256 * HG / QB, HG == 1 ? 2 : 1) void attn_fwd_kerne
     const uint16_t* vbase = v + kv_head * D;
 
     W st;
-    st.load_q(q + q_head * D, table, qw0, N, n, hh);
+    typename W::Stage stage;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
+    if constexpr (QB == 1) {
+        // region r: K1 (r = 0), then V1 .. V(NVB-1), then the extra ones
+        const int r = uwave / 2;
+        uint16_t* qbuf = r == 0 ? smem + T::K_ELEMS : smem + 2 * T::K_ELEMS + r * T::V_ELEMS;
+        typename W::QStage qs;
+        st.stage_q_issue(qs, qbuf,
+                         tile_rsrc<D>(q + q_head * D, q + q_head * D, table,
+                                      (qtile * BM) / BN + rwave / 2, N),
+                         uwave & 1, lane);
+        stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
+        wait_all_loads();
+        st.stage_q_finish(qs, qbuf, uwave & 1, lane, n, hh);
+    } else {
+        st.load_q(q + q_head * D, table, qw0, N, n, hh);
+        stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
+    }
     st.reset();
     st.set_slope(slopes, un.h + wave / WPH);
 
     const int n_tiles = kv_tiles_of(qtile, N);
     const int wave_tiles = qw0 < N ? (min(qw0 + 32 * QB - 1, N - 1)) / BN + 1 : 0;
 
-    typename W::Stage stage;
-    const int uwave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the LDS bases
     // (from the thread index, not the wave-uniform copy: as a divergent-looking
     // branch both schedules share one register allocation, which fits in 256
     // VGPRs; as a scalar branch the compiler allocates them apart and spills)
     const bool lag = LAG && wave >= WPH;
-    stage.issue(kbuf(0), vbuf(0), tile_rsrc<D>(kbase, vbase, table, 0, N), uwave, lane);
     for (int t = 0; t < n_tiles; ++t) {
         uint16_t* Ks = kbuf(t);
         wait_all_loads();              // this wave's part of tile t has landed

@@ -479,6 +479,7 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
                      "prerotate_tflops": fl / t["prerotate"] / 1e9,
                      "attn_only_tflops": fl / t["attn"] / 1e9,
                      "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0,
+                     "fused_vs_prerotate_gap": t["fused"] / t["prerotate"] - 1.0,
                      "rope_prerotate_ms": t["rope"], "rope_prerotate_gbs": pb / t["rope"] / 1e6,
                      "rope_prerotate_cold_ms": t_rope_cold,
                      "rope_prerotate_cold_gbs": pb / t_rope_cold / 1e6,
@@ -502,7 +503,13 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
     if n_star is None and sweep:
         winner = "fused" if all(r["fused_ms"] < r["prerotate_ms"] for r in sweep) else (
             "prerotate" if all(r["fused_ms"] > r["prerotate_ms"] for r in sweep) else "mixed")
-    return {"n_star": n_star, "bracket": bracket, "winner_if_no_crossing": winner,
+    # the relative gaps at the bracket's ends: a sign change between gaps of a
+    # few percent is within the run-to-run spread of these timings
+    gaps = None
+    if bracket:
+        gaps = [r["fused_vs_prerotate_gap"] for r in sweep if r["N"] in bracket]
+    return {"n_star": n_star, "bracket": bracket, "gaps_at_bracket": gaps,
+            "winner_if_no_crossing": winner,
             "sweep": "mha_d64_fp16 N=2048..32768 (B=1, H=16)", "rows": rows}
 
 

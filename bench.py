@@ -415,9 +415,12 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
     (so both paths' times include their launches). Also per shape: the GQA
     split path, the dispatcher (with a workspace for its preferred path), and
     rope_prerotate bandwidth warm and cold (after a 512 MiB cache flush,
-    larger than the 256 MB MALL) from its kernel's own start and end."""
+    larger than the 256 MB MALL) from its kernel's own start and end. N* is
+    located twice: over the call times, and over the kernels' own times
+    (fused kernel vs the pass plus plain attention), which leave out the
+    pre-rotation path's second launch."""
     rows = []
-    names = ["mha_d64_fp16_n%d" % n for n in inputs.SWEEP_NS] + [
+    names = ["mha_d64_fp16_n%d" % n for n in inputs.CROSSOVER_NS] + [
         "llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192"]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for name in names:
@@ -452,22 +455,24 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
             torch.cuda.synchronize()
             ts = sorted(a.elapsed_time(b) for a, b in pairs)
             t[key] = ts[len(ts) // 2]
-        # the streaming pass's bandwidth: its kernel's own start-to-end time
-        # (rac.time_next_kernel), warm and after a cache flush
-        warm_k, cold = [], []
-        for flushed, out_ in ((False, warm_k), (True, cold)):
+        # kernel-only times: each kernel's own start-to-end time
+        # (rac.time_next_kernel), warm, and for the streaming pass also after
+        # a cache flush; these leave out launches and host work
+        def kernel_ms(fn, flushed=False):
+            out_ = []
             for _ in range(reps):
                 a, b = ev(), ev()
                 a.record(); b.record()
                 if flushed:
                     flush.zero_()
-                rac.time_next_kernel(a, b); fns["rope"]()
+                rac.time_next_kernel(a, b); fn()
                 torch.cuda.synchronize()
                 out_.append(a.elapsed_time(b))
-        warm_k.sort()
-        cold.sort()
-        t["rope"] = warm_k[len(warm_k) // 2]
-        t_rope_cold = cold[len(cold) // 2]
+            out_.sort()
+            return out_[len(out_) // 2]
+        t["rope"] = kernel_ms(fns["rope"])
+        t_rope_cold = kernel_ms(fns["rope"], flushed=True)
+        tk = {key: kernel_ms(fns[key]) for key in ("fused", "attn")}
         fl = attn_flops(w)
         pb = prerot_bytes(w)
         fastest = min(("fused", "prerotate", "split"), key=lambda p: t[p])
@@ -480,6 +485,9 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
                      "attn_only_tflops": fl / t["attn"] / 1e9,
                      "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0,
                      "fused_vs_prerotate_gap": t["fused"] / t["prerotate"] - 1.0,
+                     "fused_kernel_ms": tk["fused"], "attn_kernel_ms": tk["attn"],
+                     "prerotate_kernels_ms": t["rope"] + tk["attn"],
+                     "fused_vs_prerotate_kernel_gap": tk["fused"] / (t["rope"] + tk["attn"]) - 1.0,
                      "rope_prerotate_ms": t["rope"], "rope_prerotate_gbs": pb / t["rope"] / 1e6,
                      "rope_prerotate_cold_ms": t_rope_cold,
                      "rope_prerotate_cold_gbs": pb / t_rope_cold / 1e6,
@@ -487,30 +495,37 @@ def crossover(torch, rac, inputs, dev, ev, reps=15):
         del qd, kd, vd, o, lse, qr, kr, krs, ws
         torch.cuda.empty_cache()
     sweep = [r for r in rows if r["workload"].startswith("mha_d64")]
-    n_star = None
-    bracket = None
+    calls = locate_crossover(sweep, "fused_ms", "prerotate_ms")
+    kernels = locate_crossover(sweep, "fused_kernel_ms", "prerotate_kernels_ms")
+    return {"n_star": calls["n_star"], "bracket": calls["bracket"],
+            "gaps_at_bracket": calls["gaps_at_bracket"],
+            "winner_if_no_crossing": calls["winner_if_no_crossing"],
+            "kernels": kernels,
+            "sweep": "mha_d64_fp16 N=1024..32768 (B=1, H=16)", "rows": rows}
+
+
+def locate_crossover(sweep, fused_key, pre_key):
+    """N* over the sweep rows (ascending N): the first sign change of
+    t_fused − t_prerotate, log-linearly interpolated in the relative gap;
+    with no change, which path won at every N ("mixed" if neither)."""
+    n_star = bracket = gaps = winner = None
     for a, b in zip(sweep, sweep[1:]):
-        da = a["fused_ms"] - a["prerotate_ms"]
-        db = b["fused_ms"] - b["prerotate_ms"]
+        da = a[fused_key] - a[pre_key]
+        db = b[fused_key] - b[pre_key]
         if (da < 0) != (db < 0):
-            # log-linear interpolation of the sign change of the relative gap
-            ga, gb = da / a["prerotate_ms"], db / b["prerotate_ms"]
+            ga, gb = da / a[pre_key], db / b[pre_key]
             x = ga / (ga - gb)
             n_star = math.exp(math.log(a["N"]) + x * (math.log(b["N"]) - math.log(a["N"])))
             bracket = [a["N"], b["N"]]
+            # the relative gaps at the bracket's ends: a sign change between
+            # gaps of a few percent is within the run-to-run spread
+            gaps = [r[fused_key] / r[pre_key] - 1.0 for r in (a, b)]
             break
-    winner = None
     if n_star is None and sweep:
-        winner = "fused" if all(r["fused_ms"] < r["prerotate_ms"] for r in sweep) else (
-            "prerotate" if all(r["fused_ms"] > r["prerotate_ms"] for r in sweep) else "mixed")
-    # the relative gaps at the bracket's ends: a sign change between gaps of a
-    # few percent is within the run-to-run spread of these timings
-    gaps = None
-    if bracket:
-        gaps = [r["fused_vs_prerotate_gap"] for r in sweep if r["N"] in bracket]
+        winner = "fused" if all(r[fused_key] < r[pre_key] for r in sweep) else (
+            "prerotate" if all(r[fused_key] > r[pre_key] for r in sweep) else "mixed")
     return {"n_star": n_star, "bracket": bracket, "gaps_at_bracket": gaps,
-            "winner_if_no_crossing": winner,
-            "sweep": "mha_d64_fp16 N=2048..32768 (B=1, H=16)", "rows": rows}
+            "winner_if_no_crossing": winner}
 
 
 def cpu_baseline(inputs, w, min_seconds=10.0):

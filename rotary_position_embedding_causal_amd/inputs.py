@@ -12,7 +12,8 @@ on the CPU. Layout is contiguous [B, H, N, D].
 The workloads below are the attention-layer shapes the measurements use:
 a tiny MHA case, Llama-3-8B-shaped GQA layers (32 query heads sharing 8 key/
 value heads, head dim 128, RoPE base 500000) at N = 2048, 4096 (batch 4) and
-8192, and a D = 64 fp16 MHA sweep over N for the fused/pre-rotate crossover.
+8192, and a D = 64 fp16 MHA sweep over N (1024 to 32768) for the
+fused/pre-rotate crossover.
 No trained weights or real activations are available, so N(0,1) tensors of
 these shapes stand in for them.
 """
@@ -37,6 +38,11 @@ SWEEP_NS = (2048, 4096, 6144, 8192, 16384, 32768)
 for _n in SWEEP_NS:
     WORKLOADS["mha_d64_fp16_n%d" % _n] = dict(B=1, Hq=16, Hkv=16, N=_n, D=64, dtype="fp16",
                                               base=10000.0)
+# one point below the sweep, where the fused kernel is expected to lead
+# (appended after the others so that their seed keys stay as they were)
+CROSSOVER_NS = (1024,) + SWEEP_NS
+WORKLOADS["mha_d64_fp16_n1024"] = dict(B=1, Hq=16, Hkv=16, N=1024, D=64, dtype="fp16",
+                                       base=10000.0)
 # seed keys: a workload's position in this table (stable: append only)
 SEED_KEYS = {name: (i + 1,) for i, name in enumerate(WORKLOADS)}
 

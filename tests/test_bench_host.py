@@ -41,3 +41,25 @@ def test_traffic_is_reported_only_for_the_sources_it_was_measured_on(tmp_path, m
     f.write_text(json.dumps(dict(good, source_sha256="0" * 64)))
     assert bench.measured_traffic() is None
 
+
+
+def _rows(gaps):
+    # sweep rows whose fused time is (1 + gap) times the pre-rotation time
+    return [{"N": n, "f": 100.0 * (1.0 + g), "p": 100.0} for n, g in gaps]
+
+
+def test_crossover_is_the_log_linear_zero_of_the_relative_gap():
+    r = bench.locate_crossover(_rows([(2048, -0.1), (4096, -0.1), (8192, 0.1), (16384, 0.2)]),
+                               "f", "p")
+    # the gap changes sign halfway between 4096 and 8192 on a log axis
+    assert r["n_star"] == pytest.approx((4096 * 8192) ** 0.5)
+    assert r["bracket"] == [4096, 8192]
+    assert r["gaps_at_bracket"] == pytest.approx([-0.1, 0.1])
+    assert r["winner_if_no_crossing"] is None
+
+
+def test_crossover_reports_the_winner_when_the_sign_never_changes():
+    pre = bench.locate_crossover(_rows([(2048, 0.01), (4096, 0.2)]), "f", "p")
+    assert pre["n_star"] is None and pre["winner_if_no_crossing"] == "prerotate"
+    fus = bench.locate_crossover(_rows([(2048, -0.3), (4096, -0.01)]), "f", "p")
+    assert fus["n_star"] is None and fus["winner_if_no_crossing"] == "fused"

@@ -221,18 +221,18 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
  * Dispatcher: out/lse of attn_rope_causal_fwd (bit-identical: every path hands
  * the same rotated operands to the same attention arithmetic), computed by the
  * path measured fastest on MI355X for this shape -- with GQA the split path
- * at every length; with MHA pre-rotation of Q and K up to N = 6144 and the
- * split path beyond -- never the fused kernel when a workspace is given
- * (rotating every key tile in the kernel cost 11-43 % over plain attention,
- * more than the streaming pass). The choice of pre-rotation versus in-kernel
+ * at every length; with MHA the fused kernel below N = 1536 (where the
+ * streaming pass's fixed cost and second launch outweigh the in-kernel
+ * rotation of every key tile), the split path from 1536 to 12287 and
+ * pre-rotation of Q and K from 12288. The choice of pre-rotation versus in-kernel
  * rotation is the one the AttnFuse report, paragraphs 3 and 5, says depends
  * on the GPU and the shape.
  *
  * workspace: caller-owned device memory for the rotated copies (Q' and K',
  * or K' alone), 16-byte aligned, not overlapping any tensor argument; the
- * library allocates nothing. If it is NULL or smaller than the preferred
- * path needs, the next path it holds is taken (split, then fused, which
- * needs none). rac_auto_plan tells the path and the bytes the preferred path
+ * library allocates nothing (the fused path needs none). If it is NULL or
+ * smaller than the preferred path needs, the next path it holds is taken
+ * (split, then fused). rac_auto_plan tells the path and the bytes the preferred path
  * needs. Calls that share a workspace must not run concurrently.
  */
 int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -209,14 +209,13 @@ int bwd_shape_from_env() {
 // All three paths give bit-identical results (they hand the same rotated
 // operands to the same attention arithmetic), so the choice is about time
 // only. Measured on MI355X (bench crossover rows, median of 15 calls after a
-// 50 ms warm-up; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) / 8192 and fp16
-// D=64 MHA at N = 2048 .. 32768): the fused kernel was never the fastest --
-// rotating every K tile in the kernel costs 11-43 % over plain attention,
-// more than the streaming pass costs; with GQA the split path (K pre-rotated,
-// Q rotated once per row in the kernel) was fastest at every N, by 1-7 % over
-// pre-rotation of Q and K; with MHA pre-rotation was fastest up to N = 6144
-// and the split path from N = 8192, where the in-kernel Q rotation is
-// amortised over more key tiles.
+// 50 ms warm-up, three runs; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) /
+// 8192 and fp16 D=64 MHA at N = 1024 .. 32768): with GQA the split path (K
+// pre-rotated, Q rotated once per row in the kernel) was fastest at every N,
+// 4-11 % ahead of the fused kernel; with MHA the fused kernel led at
+// N = 1024 (by 9 %, where the streaming pass's fixed cost and second launch
+// weigh most), the split path led or tied from 2048 to 8192, and
+// pre-rotation of Q and K led at 16384 (by 3 %) and tied at 32768.
 size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
     const size_t q = (size_t)B * Hq * N * D * 2, k = (size_t)B * Hkv * N * D * 2;
     const size_t q16 = (q + 255) & ~(size_t)255;  // K' starts 256-byte aligned
@@ -226,8 +225,10 @@ size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
 }
 
 int preferred_path(int Hq, int Hkv, int N) {
-    const int n_split = Hq / Hkv >= 2 ? 0 : 7168;  // MHA: between the measured crossings
-    return N >= n_split ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
+    if (Hq / Hkv >= 2) return RAC_PATH_SPLIT;
+    // MHA: thresholds between the measured points
+    if (N < 1536) return RAC_PATH_FUSED;
+    return N < 12288 ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
 }
 
 // The preferred path if the workspace holds it, else the next one it holds.

@@ -199,16 +199,22 @@ def test_auto_plan_paths():
         assert path == rac.RAC_PATH_SPLIT and need == B * Hkv * N * D * 2
         assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_FUSED
         assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
-    # MHA short sequences: Q' and K' (pre-rotation); too small for both: K' alone, then none
-    H, N = 16, 2048
+    # MHA long sequences: Q' and K' (pre-rotation); too small for both: K' alone, then none
+    H, N = 16, 16384
     path, need = rac.auto_plan(B, H, H, N, 64, rac.RAC_FP16, 1 << 40)
     q = B * H * N * 64 * 2
     assert path == rac.RAC_PATH_PREROTATE and need == ((q + 255) // 256) * 256 + q
     assert rac.auto_plan(B, H, H, N, 64, 1, need - 1)[0] == rac.RAC_PATH_SPLIT
     assert rac.auto_plan(B, H, H, N, 64, 1, q - 1)[0] == rac.RAC_PATH_FUSED
-    # MHA: pre-rotation up to 6144, the split path from 8192
-    assert rac.auto_plan(1, 16, 16, 6144, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_PREROTATE
-    assert rac.auto_plan(1, 16, 16, 8192, 64, rac.RAC_FP16, 1 << 40)[0] == rac.RAC_PATH_SPLIT
+    # MHA: the fused kernel below 1536, the split path up to 12287, then pre-rotation
+    for N, want in ((1, rac.RAC_PATH_FUSED), (1024, rac.RAC_PATH_FUSED),
+                    (1535, rac.RAC_PATH_FUSED), (1536, rac.RAC_PATH_SPLIT),
+                    (6144, rac.RAC_PATH_SPLIT), (12287, rac.RAC_PATH_SPLIT),
+                    (12288, rac.RAC_PATH_PREROTATE), (32768, rac.RAC_PATH_PREROTATE)):
+        path, need = rac.auto_plan(1, 16, 16, N, 64, rac.RAC_FP16, 1 << 40)
+        assert path == want, N
+        if want == rac.RAC_PATH_FUSED:
+            assert need == 0
     assert rac.auto_plan(0, 16, 16, 8192, 64, 1, 0) == (rac.RAC_PATH_FUSED, 0)
     with pytest.raises(NotImplementedError):
         rac.auto_plan(1, 4, 4, 64, 96, 0, 0)

@@ -203,7 +203,8 @@ def test_fused_and_prerotate_paths_agree(shape, launch_shape):
 
 
 @pytest.mark.parametrize("shape", SMALL + [(1, 8, 2, 4096, 128, "bf16", 500000.0),
-                                          (1, 4, 4, 8192, 64, "fp16", 10000.0)], ids=_id)
+                                          (1, 4, 4, 8192, 64, "fp16", 10000.0),
+                                          (1, 2, 2, 12288, 64, "fp16", 10000.0)], ids=_id)
 def test_dispatcher_matches_fused(shape):
     """attn_rope_causal_auto gives the fused kernel's result bit for bit, whichever path the
     workspace allows: the preferred one, the split path (K' only), or none (fused)."""
@@ -349,9 +350,9 @@ def test_empty_inputs():
 # ---------------------------------------------------------------------------
 
 # every sweep point: the launch shape changes with the size (pair launch at
-# N = 2048, 4096 and 8192, the tile launch at 6144 and from 16384)
+# N = 1024, 2048, 4096 and 8192, the tile launch at 6144 and from 16384)
 FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
-        "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
+        "mha_d64_fp16_n1024", "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
         "mha_d64_fp16_n16384", "mha_d64_fp16_n32768"]
 
 

@@ -27,8 +27,28 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract
 EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_bwd.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src, obj, verbose):
-    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+# The forward attention kernels compile as one object per (dtype, head dim,
+# rotation mode), in parallel, plus the dispatcher (the same source with no
+# part selected); see the end of attn_fwd.hip.
+FWD_MODES = (0, 1, 2, 3, 4, 5, 7)  # ROT_* | MOD_ALIBI combinations the dispatcher uses
+FWD_PARTS = [(dt, d, m) for dt in (0, 1) for d in (64, 128) for m in FWD_MODES]
+
+
+def _jobs(objdir):
+    """(source, object, extra flags) for every object of the library."""
+    jobs = []
+    for src in SOURCES:
+        if src == "attn_fwd.hip":
+            for dt, d, m in FWD_PARTS:
+                jobs.append((src, os.path.join(objdir, "attn_fwd_%d_%d_%d.o" % (dt, d, m)),
+                             ["-DRAC_FWD_DT=%d" % dt, "-DRAC_FWD_D=%d" % d, "-DRAC_FWD_MODE=%d" % m]))
+        jobs.append((src, os.path.join(objdir, src.replace(".hip", ".o")), []))
+    return jobs
+
+
+def _compile(src, obj, verbose, defs=()):
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + list(defs) + ["-c", os.path.join(CSRC, src),
+                                                                "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,9 +65,12 @@ def _compile(src, obj, verbose):
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build", "rac")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
+    jobs = _jobs(objdir)
+    objs = [j[1] for j in jobs]
+    # largest parts first, so the long compiles start early
+    order = sorted(jobs, key=lambda j: ("_128_" not in j[1], j[1]))
+    with ThreadPoolExecutor(max_workers=max(2, os.cpu_count() or 2)) as ex:
+        list(ex.map(lambda j: _compile(j[0], j[1], verbose, j[2]), order))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

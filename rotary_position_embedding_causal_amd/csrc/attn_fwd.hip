@@ -1141,9 +1141,23 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
                          a.Hkv, a.N, n_qtiles, scale_log2);
 }
 
+// One (dtype, head dim, mode) per object file: the build compiles this file
+// once per combination with RAC_FWD_DT / RAC_FWD_D / RAC_FWD_MODE defined
+// (the kernels are large; the parts compile in parallel), and once without
+// them for the dispatcher below, which only declares the parts.
+template <int DT, int D, int RM>
+hipError_t launch_part(const AttnArgs& a, hipStream_t stream);
+
+#ifdef RAC_FWD_MODE
+template <int DT, int D, int RM>
+hipError_t launch_part(const AttnArgs& a, hipStream_t stream) {
+    return launch_typed<DT, D, RM>(a, stream);
+}
+template hipError_t launch_part<RAC_FWD_DT, RAC_FWD_D, RAC_FWD_MODE>(const AttnArgs&, hipStream_t);
+#else
 template <int DT, int RM>
 static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
-    return a.D == 64 ? launch_typed<DT, 64, RM>(a, stream) : launch_typed<DT, 128, RM>(a, stream);
+    return a.D == 64 ? launch_part<DT, 64, RM>(a, stream) : launch_part<DT, 128, RM>(a, stream);
 }
 
 template <int DT>
@@ -1165,5 +1179,6 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int rot, hipStream_t stream) {
     return a.dtype == DT_BF16 ? launch_rot<DT_BF16>(a, rot, stream)
                               : launch_rot<DT_FP16>(a, rot, stream);
 }
+#endif
 
 }  // namespace rac

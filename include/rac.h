@@ -232,8 +232,10 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
  * or K' alone), 16-byte aligned, not overlapping any tensor argument; the
  * library allocates nothing (the fused path needs none). If it is NULL or
  * smaller than the preferred path needs, the next path it holds is taken
- * (split, then fused). rac_auto_plan tells the path and the bytes the preferred path
- * needs. Calls that share a workspace must not run concurrently.
+ * (split, then fused); so is a path whose streaming pass would exceed its
+ * grid (more than 8 * 65535 slabs). rac_auto_plan tells the path and the
+ * bytes the preferred path needs. Calls that share a workspace must not run
+ * concurrently.
  */
 int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out, float* lse,
                           int B, int Hq, int Hkv, int N, int D, double rope_base,
@@ -297,7 +299,10 @@ int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* d
 /* Text for the last non-zero return on the calling thread ("" if none). */
 const char* rac_last_error(void);
 
-/* Synchronises every device holding a table, then frees all cos/sin tables.
+/* Synchronises every device holding a table, then frees all cos/sin tables
+ * (the next call that needs one builds it again). It must not run
+ * concurrently with any other call of this library: another thread may have
+ * taken a table pointer and not yet enqueued the kernel that reads it.
  * Returns RAC_OK or RAC_ERR_HIP. */
 int rac_release_tables(void);
 
@@ -308,9 +313,11 @@ int rac_release_tables(void);
  * kernel is launched with hipExtLaunchKernel, which records `start_event`
  * and `stop_event` at the kernel's own start and end on its stream, so
  * hipEventElapsedTime gives its execution time without the queue's dispatch
- * latency. The events are disarmed once used; an entry point that makes
- * several launches (the dispatcher's two-kernel paths) times the first.
- * Backward kernels ignore the timer. Both NULL disarms.
+ * latency. The events are disarmed once used, and when the next forward or
+ * pass entry point returns without launching (an argument error, an empty
+ * problem); an entry point that makes several launches (the dispatcher's
+ * two-kernel paths) times the first. Backward kernels ignore the timer.
+ * Both NULL disarms.
  * Returns RAC_OK, or RAC_ERR_ARG if exactly one event is NULL. */
 int rac_time_next_kernel(void* start_event, void* stop_event);
 

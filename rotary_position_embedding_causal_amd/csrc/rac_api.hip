@@ -52,6 +52,18 @@ void take_kernel_timer(hipEvent_t* start, hipEvent_t* stop) {
 
 namespace {
 
+// Disarms the kernel timer when a forward or pass entry point returns, so a
+// call that launches nothing (an argument error, an empty problem) does not
+// leave it armed for an unrelated later launch, whose caller may have
+// destroyed the events by then. (A launch has already taken it.)
+struct TimerScope {
+    ~TimerScope() { g_timer_start = g_timer_stop = nullptr; }
+};
+
+}  // namespace
+
+namespace {
+
 // ---- cos/sin tables --------------------------------------------------------
 //
 // Entry [p][2i] = cos(p * theta_i), [p][2i+1] = sin(p * theta_i), with
@@ -231,13 +243,25 @@ int preferred_path(int Hq, int Hkv, int N) {
     return N < 12288 ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
 }
 
-// The preferred path if the workspace holds it, else the next one it holds.
+// Whether a path's streaming pass fits its grid (at most 8 * 65535 slabs:
+// B * (Hq + Hkv) for pre-rotation, B * Hkv for the K-only pass).
+bool pass_fits(int path, int B, int Hq, int Hkv) {
+    const int64_t slabs = path == RAC_PATH_PREROTATE ? (int64_t)B * (Hq + (int64_t)Hkv)
+                          : path == RAC_PATH_SPLIT   ? (int64_t)B * Hkv
+                                                     : 0;
+    return slabs <= 8LL * 65535;
+}
+
+// The preferred path if the workspace holds it (and its pass fits its grid),
+// else the next one that does: pre-rotation, then split, then fused.
 int plan_path(int B, int Hq, int Hkv, int N, int D, size_t workspace_bytes) {
     const int pref = preferred_path(Hq, Hkv, N);
-    if (workspace_bytes >= path_workspace(pref, B, Hq, Hkv, N, D)) return pref;
-    if (pref == RAC_PATH_PREROTATE &&
-        workspace_bytes >= path_workspace(RAC_PATH_SPLIT, B, Hq, Hkv, N, D))
-        return RAC_PATH_SPLIT;
+    auto usable = [&](int path) {
+        return pass_fits(path, B, Hq, Hkv) &&
+               workspace_bytes >= path_workspace(path, B, Hq, Hkv, N, D);
+    };
+    if (usable(pref)) return pref;
+    if (pref == RAC_PATH_PREROTATE && usable(RAC_PATH_SPLIT)) return RAC_PATH_SPLIT;
     return RAC_PATH_FUSED;
 }
 
@@ -295,6 +319,7 @@ extern "C" {
 int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                             int B, int Hq, int Hkv, int N, int D, double rope_base, int pairing,
                             int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -313,6 +338,7 @@ int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* o
 int attn_alibi_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                           int B, int Hq, int Hkv, int N, int D, const float* slopes,
                           double rope_base, int pairing, int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -348,6 +374,7 @@ int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out,
 int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void* out,
                            float* lse, int B, int Hq, int Hkv, int N, int D, double rope_base,
                            int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -363,6 +390,7 @@ int attn_rope_q_causal_fwd(const void* q, const void* k_rot, const void* v, void
 
 int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                     int Hq, int Hkv, int N, int D, int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -376,6 +404,7 @@ int attn_causal_fwd(const void* q, const void* k, const void* v, void* out, floa
 int rope_prerotate_ex(const void* q, const void* k, void* q_rot, void* k_rot, int B, int Hq,
                       int Hkv, int N, int D, double rope_base, int pairing, int dtype,
                       void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -403,6 +432,7 @@ int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B
 
 int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
                        int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -436,6 +466,7 @@ int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out
 
 int rope_prerotate_k(const void* k, void* k_rot, int B, int Hkv, int N, int D, double rope_base,
                      int dtype, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hkv, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -470,6 +501,7 @@ int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t worksp
 int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out, float* lse,
                           int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
+    const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;

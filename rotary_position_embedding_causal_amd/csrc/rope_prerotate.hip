@@ -45,11 +45,13 @@ __device__ __forceinline__ u32x4 rope_unrotate8(u32x4 y, f32x4 cs_lo, f32x4 cs_h
 
 // PR_HEADS slabs per lane: that many independent 16-byte loads in flight.
 // INV: turn by -p instead of +p (the gradient of the pass).
+// q_rot and k_rot may be q and k themselves (exact in-place use): those
+// pointers carry no __restrict__, and each lane stores only the chunks it has
+// already loaded.
 template <int DT, int D, int PR_HEADS, bool INV>
 __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* q_rot,
-    uint16_t* k_rot, const float* __restrict__ table, int N, int64_t q_slabs,
-    int64_t total_slabs) {
+    const uint16_t* q, const uint16_t* k, uint16_t* q_rot, uint16_t* k_rot,
+    const float* __restrict__ table, int N, int64_t q_slabs, int64_t total_slabs) {
     constexpr int CHUNKS = D / 8;  // 16-byte chunks per row
     const int64_t idx = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
     const int64_t row = idx / CHUNKS;
@@ -88,11 +90,11 @@ __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
 // The half-split pairing: a lane owns chunk c < D/16 of a row and its
 // partner chunk c + D/16 (elements d and d + D/2 pair), with the 16 table
 // floats of frequencies 8c .. 8c+7, for PR_HEADS slabs.
+// (in-place use as for rope_prerotate_kernel)
 template <int DT, int D, int PR_HEADS>
 __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_half_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* q_rot,
-    uint16_t* k_rot, const float* __restrict__ table, int N, int64_t q_slabs,
-    int64_t total_slabs) {
+    const uint16_t* q, const uint16_t* k, uint16_t* q_rot, uint16_t* k_rot,
+    const float* __restrict__ table, int N, int64_t q_slabs, int64_t total_slabs) {
     constexpr int HALF_CHUNKS = D / 16;  // chunk pairs per row
     const int64_t idx = (int64_t)blockIdx.x * PR_THREADS + threadIdx.x;
     const int64_t row = idx / HALF_CHUNKS;

@@ -216,6 +216,11 @@ def test_auto_plan_paths():
         if want == rac.RAC_PATH_FUSED:
             assert need == 0
     assert rac.auto_plan(0, 16, 16, 8192, 64, 1, 0) == (rac.RAC_PATH_FUSED, 0)
+    # a path whose streaming pass exceeds its grid (8 * 65535 slabs) is passed over
+    assert rac.auto_plan(65535, 32, 16, 1, 64, 0, 1 << 40)[0] == rac.RAC_PATH_FUSED  # B*Hkv
+    assert rac.auto_plan(65535, 32, 8, 1, 64, 0, 1 << 40)[0] == rac.RAC_PATH_SPLIT  # 524280
+    assert rac.auto_plan(20000, 16, 16, 16384, 64, 1, 1 << 50)[0] == rac.RAC_PATH_SPLIT
+    assert rac.auto_plan(40000, 16, 16, 16384, 64, 1, 1 << 50)[0] == rac.RAC_PATH_FUSED
     with pytest.raises(NotImplementedError):
         rac.auto_plan(1, 4, 4, 64, 96, 0, 0)
     with pytest.raises(ValueError):
@@ -375,3 +380,18 @@ def test_kernel_timer_arguments():
     assert L_.rac_time_next_kernel(None, K) == rac.RAC_ERR_ARG
     assert L_.rac_time_next_kernel(Q, K) == rac.RAC_OK  # armed (never launched here) ...
     assert L_.rac_time_next_kernel(None, None) == rac.RAC_OK  # ... and disarmed
+
+
+def test_valid_call_without_a_device_reports_hip_error():
+    """On a machine with no HIP device, calls whose arguments pass validation
+    reach the runtime and come back as RAC_ERR_HIP with a message (no crash,
+    nothing enqueued); the pointers are never dereferenced."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a HIP device is present: the runtime would accept the call")
+    assert fused() == rac.RAC_ERR_HIP and rac.last_error() != ""
+    assert plain() == rac.RAC_ERR_HIP and rac.last_error() != ""
+    assert prerot() == rac.RAC_ERR_HIP and rac.last_error() != ""
+    assert auto() == rac.RAC_ERR_HIP and rac.last_error() != ""
+    # the empty problem still succeeds without touching the runtime
+    assert fused(N=0) == rac.RAC_OK and rac.last_error() == ""

@@ -5,8 +5,8 @@ Cases: the fused backward (attn_rope_causal_bwd) and the pre-rotation path's
 backward (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd) on small shapes
 spanning several tiles with ragged tails, GQA ratios 1-8, D = 64 and 128,
 bf16 and fp16; the inverse rotation pass on its own; determinism; and one key/
-value group of the Llama-3-8B-shaped layer at full length (N = 2048) in the
-launch configuration the bench times. The small cases run under every
+value group of the Llama-3-8B-shaped layer at full length (N = 2048 and 8192)
+in the launch configuration the bench times. The small cases run under every
 key-parallel workgroup shape (RAC_BWD_SHAPE). Bounds: parity.assert_grad.
 """
 import numpy as np
@@ -149,14 +149,16 @@ def test_ragged_lengths_and_gqa(N, ratio, bwd_shape):
         assert_grad(to_f64(got), ref, "N=%d ratio=%d %s" % (N, ratio, name))
 
 
-def test_full_length_one_group():
-    """The Llama-3-8B-shaped layer at N = 2048 in the bench's launch
+@pytest.mark.parametrize("name,key", [("llama3_8b_gqa_n2048", 406), ("llama3_8b_gqa_n8192", 407)])
+def test_full_length_one_group(name, key):
+    """The Llama-3-8B-shaped layer at N = 2048 and 8192 in the bench's launch
     configuration; the oracle checks one key/value group (4 query heads and
-    their key/value head), which the other groups do not influence."""
-    w = inputs.WORKLOADS["llama3_8b_gqa_n2048"]
+    their key/value head) in full, which the other groups do not influence
+    (about 15 s of oracle time at N = 8192 on 16 cores)."""
+    w = inputs.WORKLOADS[name]
     B, Hq, Hkv, N, D, dt, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"], w["base"]
-    q, k, v = inputs.workload_qkv("llama3_8b_gqa_n2048")
-    do = inputs.draw((B, Hq, N, D), dt, (406,), 3)
+    q, k, v = inputs.workload_qkv(name)
+    do = inputs.draw((B, Hq, N, D), dt, (key,), 3)
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
     o, lse = rac.attn_rope_causal_fwd(qd, kd, vd, base)
     dq, dk, dv, _ = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
@@ -167,9 +169,9 @@ def test_full_length_one_group():
     rdq, rdk, rdv, _, _ = oracle.rope_attention_bwd(
         inputs.bits(q)[:, hs], inputs.bits(k)[:, g:g + 1], inputs.bits(v)[:, g:g + 1],
         inputs.bits(do)[:, hs], dt, base, "rounded")
-    assert_grad(to_f64(dq[:, hs]), rdq, "full-length dq")
-    assert_grad(to_f64(dk[:, g:g + 1]), rdk, "full-length dk")
-    assert_grad(to_f64(dv[:, g:g + 1]), rdv, "full-length dv")
+    assert_grad(to_f64(dq[:, hs]), rdq, "%s dq" % name)
+    assert_grad(to_f64(dk[:, g:g + 1]), rdk, "%s dk" % name)
+    assert_grad(to_f64(dv[:, g:g + 1]), rdv, "%s dv" % name)
 
 
 def test_empty_inputs():

@@ -311,6 +311,85 @@ def test_large_sigma_attention_arithmetic(sigma, D, dt, launch_shape):
     assert lerr <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
 
 
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (64, "fp16"), (128, "fp16")])
+def test_large_sigma_fused_rope(D, dt):
+    """sigma = 4 with RoPE in the kernel for the cells the stress bound does
+    not hold (D = 64, and fp16): O stays inside its bounds; the LSE excess
+    over the stress bound is measured and printed, and shown to come from the
+    fp32 rotation alone -- the same kernel arithmetic on the operands the GPU
+    rotated itself (rope_prerotate's output, bit-identical to what the fused
+    kernel feeds its matrix cores) meets the stress bound against the oracle
+    given those operands."""
+    B, Hq, Hkv, N, base, sigma = 1, 4, 2, 384, 500000.0, 4.0
+    q = inputs.draw((B, Hq, N, D), dt, (111, D), 0, sigma)
+    k = inputs.draw((B, Hkv, N, D), dt, (111, D), 1, sigma)
+    v = inputs.draw((B, Hkv, N, D), dt, (111, D), 2)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    qr, kr = rac.rope_prerotate(qd, kd, base)
+    torch.cuda.synchronize()
+    ro, rl, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt, base)
+    assert_o(to_f64(o), ro, "sigma=4 D=%d %s" % (D, dt))
+    bound = 1e-3 + 2.0 ** -16 * float(np.max(np.abs(rl)))
+    lerr = float(np.max(np.abs(to_f64(l) - rl)))
+    print("sigma=4 fused D=%d %s: max|dLSE|=%.3e, stress bound %.3e, excess %.3e" %
+          (D, dt, lerr, bound, max(0.0, lerr - bound)))
+    # the documented limit of the fp32 rotation at these scores (4-8e-3 measured)
+    assert lerr <= 1.5e-2
+    go, gl = oracle.attention(oracle.decode(bits(qr), dt), oracle.decode(bits(kr), dt),
+                              oracle.decode(inputs.bits(v), dt))
+    assert float(np.max(np.abs(to_f64(l) - gl))) <= 1e-3 + 2.0 ** -16 * float(np.max(np.abs(gl)))
+    assert_o(to_f64(o), go, "sigma=4 D=%d %s on the GPU's rotation" % (D, dt))
+
+
+def test_kernel_timer_disarmed_by_a_call_that_launches_nothing():
+    """An armed timer that meets an entry point returning without a launch
+    (an empty problem, an argument error) is dropped: the next kernel does
+    not record the caller's events. (The events are recorded back to back
+    when armed; a kernel that stamped them would stretch them to its own
+    duration, here tens of microseconds.)"""
+    _, (qd, kd, vd) = _inputs(1, 16, 16, 4096, 64, "bf16", key=(112,))
+    empty = torch.empty(1, 4, 0, 64, dtype=torch.bfloat16, device=DEV)
+    kernel_ms = None
+    for call in (None,
+                 lambda: rac.attn_rope_causal_fwd(empty, empty, empty, 10000.0),
+                 lambda: rac.lib().attn_causal_fwd(None, None, None, None, None, 1, 4, 4, 256, 64,
+                                                   0, None)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        rac.time_next_kernel(a, b)
+        if call is not None:
+            call()
+        rac.attn_causal_fwd(qd, kd, vd)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        if call is None:
+            kernel_ms = ms  # armed right before a launch: the kernel's own time
+            assert kernel_ms > 0.02
+        else:
+            assert ms < kernel_ms / 4, (ms, kernel_ms)
+
+
+def test_release_tables_and_rebuild():
+    """rac_release_tables frees the cos/sin tables; the next calls build them
+    again and give the same bits (for both paths and a second base)."""
+    _, (qd, kd, vd) = _inputs(1, 8, 2, 1000, 128, "bf16", key=(113,))
+    ref = [rac.attn_rope_causal_fwd(qd, kd, vd, b) for b in (500000.0, 10000.0)]
+    refp = rac.prerotate_path(qd, kd, vd, 500000.0)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        rac.release_tables()
+        got = [rac.attn_rope_causal_fwd(qd, kd, vd, b) for b in (500000.0, 10000.0)]
+        gotp = rac.prerotate_path(qd, kd, vd, 500000.0)
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(got + [gotp], ref + [refp]):
+            assert torch.equal(o, ro) and torch.equal(l, rl)
+    rac.release_tables()
+    rac.release_tables()  # nothing left to free
+
+
 def test_deterministic(launch_shape):
     _, (qd, kd, vd) = _inputs(1, 8, 2, 777, 128, "bf16", key=(109,))
     a = rac.attn_rope_causal_fwd(qd, kd, vd, 500000.0)
@@ -349,8 +428,9 @@ def test_empty_inputs():
 # full-size workloads, the launch configuration the bench times
 # ---------------------------------------------------------------------------
 
-# every sweep point: the launch shape changes with the size (pair launch at
-# N = 1024, 2048, 4096 and 8192, the tile launch at 6144 and from 16384)
+# every sweep point: the launch shape changes with the size (for the D = 64
+# MHA sweep the pair launch at N = 2048, 4096 and 8192, the tile launch at
+# 1024, 6144 and from 16384)
 FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
         "mha_d64_fp16_n1024", "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
         "mha_d64_fp16_n16384", "mha_d64_fp16_n32768"]

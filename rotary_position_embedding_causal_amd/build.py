@@ -80,5 +80,36 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """The same library with its host code (the C ABI: validation, the table
+    cache, the path planner) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (-Xarch_host: the device code is unchanged),
+    into _build/asan/librac.so, for the CPU tests with the ROCm clang's ASan
+    runtime preloaded (see tests/conftest.py). The kernels' objects come from
+    the regular build."""
+    objdir = os.path.join(ROOT, "_build", "rac")
+    asandir = os.path.join(ROOT, "_build", "asan")
+    os.makedirs(asandir, exist_ok=True)
+    jobs = _jobs(objdir)
+    if not all(os.path.exists(j[1]) for j in jobs):
+        build(verbose)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+           "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    api_obj = os.path.join(asandir, "rac_api.o")
+    _compile("rac_api.hip", api_obj, verbose, san)
+    objs = [api_obj if os.path.basename(j[1]) == "rac_api.o" else j[1] for j in jobs]
+    out = os.path.join(asandir, "librac.so")
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-shared-libsan",
+           "-fsanitize=address,undefined", "-o", out] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))

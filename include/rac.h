@@ -122,6 +122,28 @@ int attn_rope_causal_fwd(const void* q, const void* k, const void* v, void* out,
                          int dtype, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_rope_causal_fwd with its cos/sin table, the one buffer that call's
+ * kernel reads beyond its inputs and outputs, in a library-owned static
+ * device array of RAC_NOALLOC_MAX_N * 128 fp32 values (16 MiB, held on every
+ * GPU the library runs on until the process ends) instead of the table cache,
+ * which allocates. Each call rebuilds the N rows it needs on `stream` (one
+ * small kernel; the angles in fp64 as for the cache) and then runs the fused
+ * kernel: it calls no hipMalloc, hipFree or other allocating routine and no
+ * synchronous copy. Same arguments, results (to rounding of the table's fp64
+ * sines and cosines) and rules as attn_rope_causal_fwd, and additionally
+ * N * D <= RAC_NOALLOC_MAX_N * 128 (N <= 32768 at D = 128, 65536 at D = 64),
+ * else RAC_ERR_ARG. Every call on a GPU uses that GPU's one array: calls that
+ * overlap on one GPU (different streams, or threads) race and must not be
+ * issued; calls on one stream are ordered.
+ */
+#define RAC_NOALLOC_MAX_N 32768
+int attn_rope_causal_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, int B, int Hq, int Hkv, int N, int D,
+                                 double rope_base, int dtype, void* stream);
+
+/*
  * Pre-rotation pass: q_rot = RoPE(q), k_rot = RoPE(k), each element rounded
  * once to `dtype`. Memory-bound streaming kernel. q_rot may equal q and k_rot
  * may equal k (in place); any other overlap between the four buffers is an

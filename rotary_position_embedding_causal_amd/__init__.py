@@ -37,7 +37,9 @@ EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_p
             "attn_rope_q_causal_fwd", "attn_rope_causal_auto", "rac_auto_plan",
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
             "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
-            "rac_last_error", "rac_release_tables", "rac_time_next_kernel")
+            "rac_last_error", "rac_release_tables", "rac_time_next_kernel",
+            "attn_rope_causal_fwd_noalloc")
+RAC_NOALLOC_MAX_N = 32768
 RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
 PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
 RAC_PATH_FUSED, RAC_PATH_PREROTATE, RAC_PATH_SPLIT = 0, 1, 2
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.rac_release_tables.restype = i
     L.rac_time_next_kernel.argtypes = [vp, vp]
     L.rac_time_next_kernel.restype = i
+    L.attn_rope_causal_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, vp]
+    L.attn_rope_causal_fwd_noalloc.restype = i
     _lib = L
     return L
 
@@ -196,6 +200,21 @@ def attn_rope_causal_fwd(q, k, v, rope_base: float, out=None, lse=None, want_lse
                                         B, Hq, Hkv, N, D, float(rope_base), dt,
                                         _stream(q.device))
     check(rc, "attn_rope_causal_fwd")
+    return out, lse
+
+
+def attn_rope_causal_fwd_noalloc(q, k, v, rope_base: float, out=None, lse=None,
+                                 want_lse: bool = True):
+    """attn_rope_causal_fwd with the cos/sin table in the library's static
+    device array (the C entry point allocates nothing; pass `out` and `lse`
+    to allocate nothing here either). Returns (out, lse)."""
+    B, Hq, Hkv, N, D, dt = _check_qkv(q, k, v)
+    out, lse = _outputs(q, out, lse, want_lse)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                B, Hq, Hkv, N, D, float(rope_base), dt,
+                                                _stream(q.device))
+    check(rc, "attn_rope_causal_fwd_noalloc")
     return out, lse
 
 

@@ -85,6 +85,11 @@ uint64_t bits_of(double x) {
     return u;
 }
 
+// theta_i = base^(-2i/D), i < D/2, in fp64 (the same expression for every table)
+void table_thetas(int D, double base, double* theta) {
+    for (int i = 0; i < D / 2; ++i) theta[i] = pow(base, -(2.0 * i) / (double)D);
+}
+
 int get_table(int D, double base, int N, const float** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(RAC_ERR_HIP, "hipGetDevice failed (no HIP device?)");
@@ -98,7 +103,7 @@ int get_table(int D, double base, int N, const float** out) {
     while (cap < N) cap *= 2;
     std::vector<float> host((size_t)cap * D);
     std::vector<double> theta(D / 2);
-    for (int i = 0; i < D / 2; ++i) theta[i] = pow(base, -(2.0 * i) / (double)D);
+    table_thetas(D, base, theta.data());
     for (int64_t p = 0; p < cap; ++p)
         for (int i = 0; i < D / 2; ++i) {
             const double ang = (double)p * theta[i];
@@ -117,6 +122,54 @@ int get_table(int D, double base, int N, const float** out) {
     t.dev = d;
     t.capacity = cap;
     *out = d;
+    return RAC_OK;
+}
+
+// ---- the allocation-free entry point's table -------------------------------
+//
+// attn_rope_causal_fwd_noalloc keeps its cos/sin table in this fixed array
+// instead of the cache above: each GPU the library runs on holds one copy
+// (16 MiB) until the process ends. In host code `scratch` only stands in for
+// the device symbol; its address on each device comes from
+// hipGetSymbolAddress (kept per device in g_scratch_ptr) and only that
+// address is handed to kernels.
+constexpr int64_t SCRATCH_FLOATS = (int64_t)RAC_NOALLOC_MAX_N * 128;
+static __device__ __align__(256) float scratch[SCRATCH_FLOATS];
+constexpr int MAX_DEVICES = 64;
+float* g_scratch_ptr[MAX_DEVICES] = {};  // under g_mutex
+
+// The frequencies of one table, by value (a kernel argument).
+struct Thetas {
+    double t[64];
+};
+
+// Rows 0 .. N-1 of the table: [p][2i] = cos(p theta_i), [p][2i+1] = sin(p theta_i),
+// the angle formed in fp64 and each value rounded once to fp32, as in get_table.
+__global__ void build_table_kernel(float* tab, Thetas th, int D, int N) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = D / 2;
+    const int64_t p = idx / half;
+    const int i = (int)(idx % half);
+    if (p >= N) return;
+    const double ang = (double)p * th.t[i];
+    tab[p * D + 2 * i] = (float)cos(ang);
+    tab[p * D + 2 * i + 1] = (float)sin(ang);
+}
+
+// This device's address of `scratch` (looked up once per device, with it current).
+int scratch_table(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(RAC_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(RAC_ERR_HIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(RAC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<float*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
     return RAC_OK;
 }
 
@@ -333,6 +386,33 @@ int attn_rope_causal_fwd_ex(const void* q, const void* k, const void* v, void* o
                     pairing == RAC_PAIR_HALF};
     return hip_status(rac::launch_attn_fwd(a, rac::ROT_QK, static_cast<hipStream_t>(stream)),
                       "attn_rope_causal_fwd launch");
+}
+
+int attn_rope_causal_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, int B, int Hq, int Hkv, int N, int D,
+                                 double rope_base, int dtype, void* stream) {
+    const TimerScope timer_scope;
+    bool empty = false;
+    int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
+    if (rc != RAC_OK) return rc;
+    if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((int64_t)N * D > SCRATCH_FLOATS)
+        return fail(RAC_ERR_ARG, "N*D=%lld exceeds the static table (%lld floats: N <= %lld at D=%d)",
+                    (long long)N * D, (long long)SCRATCH_FLOATS, (long long)(SCRATCH_FLOATS / D), D);
+    if (empty) return ok();
+    if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
+    float* table = nullptr;
+    if ((rc = scratch_table(&table)) != RAC_OK) return rc;
+    // the rows this call needs, rebuilt on its stream (so a call, or a
+    // captured graph of it, never depends on another call's table)
+    Thetas th;
+    table_thetas(D, rope_base, th.t);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t items = (int64_t)N * (D / 2);
+    build_table_kernel<<<dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st>>>(table, th, D, N);
+    if ((rc = hip_status(hipGetLastError(), "table build launch")) != RAC_OK) return rc;
+    rac::AttnArgs a{q, k, v, out, lse, table, B, Hq, Hkv, N, D, dtype, attn_shape_from_env()};
+    return hip_status(rac::launch_attn_fwd(a, rac::ROT_QK, st), "attn_rope_causal_fwd_noalloc launch");
 }
 
 int attn_alibi_causal_fwd(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -13,15 +13,18 @@ Also printed in the same JSON line:
     TFLOP/s from a pair of HIP events that each of its launches in the timed
     region records at the kernel's own start and end (rac.time_next_kernel,
     hipExtLaunchKernel on the launch stream), against the dense bf16 MFMA
-    peak;
+    peak; warm (the timed steps) and cold (after a 512 MiB flush);
   * paths: per-kernel times taken the same way (warm, and cold after a
     512 MiB cache flush) and their sums per path, TFLOP/s, % of MFMA peak,
-    rope_prerotate GB/s vs 8 TB/s;
+    rope_prerotate GB/s vs 8 TB/s and vs a plain copy of the same bytes
+    with the same access pattern (rac.stream_copy), warm and cold;
     also the GQA split path (rope_prerotate_k then attn_rope_q_causal_fwd),
     timed after the step loop and not part of `value`;
-  * crossover: fused vs pre-rotation (and split) times over the D=64 fp16
-    MHA sweep (N = 2048 .. 32768) and the GQA shapes, with the measured
-    crossover N* of fused vs pre-rotation;
+  * crossover: fused vs pre-rotation (and split) times over six families
+    (D=64 fp16 MHA N = 1024 .. 32768; D=128 bf16 MHA; GQA 4:1 at D=64 bf16
+    and D=128 bf16/fp16; GQA 8:1 at D=128 bf16), three interleaved repeats,
+    the measured N* per family (kernel level, the headline; and call level),
+    and the Rotation Calculus model fitted to the same rows with its N*;
   * variants: the half-split RoPE pairing (fused and pre-rotated) and the
     ALiBi score modification (alone and with fused RoPE), timed after the
     step loop and not part of `value`;
@@ -287,6 +290,18 @@ def main():
 
     c_fused, c_rope, c_attn = cold(fused), cold(rope), cold(attn)
     pb = prerot_bytes(w)
+    # the pass's ceiling: a plain copy of as many bytes as it reads (then
+    # writes), with its access pattern, warm and cold, in this same run
+    csrc = torch.empty(int(pb // 2), dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    copy = lambda: rac.stream_copy(csrc, cdst)  # noqa: E731
+    warm(copy, args.warmup, WARM_SECONDS / 4, torch.cuda.synchronize)
+    copy_ev = made([(ev(), ev()) for _ in range(args.steps)])
+    for a, b in copy_ev:
+        rac.time_next_kernel(a, b); copy()
+    torch.cuda.synchronize()
+    t_copy, c_copy = avg_ms(copy_ev), cold(copy)
+    del csrc, cdst
 
     # ---- the GQA split path, timed the same way after the timed region ----
     warm(lambda: (rope_k(), attn_q()), args.warmup, WARM_SECONDS, torch.cuda.synchronize)
@@ -310,7 +325,11 @@ def main():
         "rope_prerotate": {"ms": t_rope, "gbs": pb / t_rope / 1e6,
                            "hbm_frac": pb / t_rope / 1e6 / HBM_PEAK_GBS, "cold_ms": c_rope,
                            "cold_gbs": pb / c_rope / 1e6,
-                           "cold_hbm_frac": pb / c_rope / 1e6 / HBM_PEAK_GBS, "bytes": pb},
+                           "cold_hbm_frac": pb / c_rope / 1e6 / HBM_PEAK_GBS, "bytes": pb,
+                           "copy_ceiling": {"ms": t_copy, "gbs": pb / t_copy / 1e6,
+                                            "cold_ms": c_copy, "cold_gbs": pb / c_copy / 1e6,
+                                            "cold_hbm_frac": pb / c_copy / 1e6 / HBM_PEAK_GBS},
+                           "frac_of_copy": t_copy / t_rope, "cold_frac_of_copy": c_copy / c_rope},
         "split": {"ms": t_rk + t_aq, "tflops": fl / (t_rk + t_aq) / 1e9,
                   "mfma_frac": fl / (t_rk + t_aq) / 1e9 / peak, "cold_ms": c_rk + c_aq},
         "attn_rope_q_causal_fwd": {"ms": t_aq, "tflops": fl / t_aq / 1e9,
@@ -331,7 +350,10 @@ def main():
                    "flops_per_path": fl},
         "roofline": {"kernel": "attn_rope_causal_fwd kernel (bf16, D=128)", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic()},
+                     "frac": achieved / peak, "traffic": measured_traffic(),
+                     "achieved_cold": fl / (c_fused * 1e-3) / 1e12,
+                     "frac_cold": fl / (c_fused * 1e-3) / 1e12 / peak,
+                     "cold": "median of 20 launches, each after a 512 MiB cache flush"},
         "paths": paths,
     }
 
@@ -407,123 +429,236 @@ def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):
     return res
 
 
-def crossover(torch, rac, inputs, dev, ev, reps=15):
-    """Fused vs pre-rotation path time per shape; N* where their order flips.
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
-    Each path is warmed up for 50 ms, then timed as the median of `reps`
-    back-to-back calls, each bracketed by HIP events on the launch stream
-    (so both paths' times include their launches). Also per shape: the GQA
-    split path, the dispatcher (with a workspace for its preferred path), and
-    rope_prerotate bandwidth warm and cold (after a 512 MiB cache flush,
-    larger than the 256 MB MALL) from its kernel's own start and end. N* is
-    located twice: over the call times, and over the kernels' own times
-    (fused kernel vs the pass plus plain attention), which leave out the
-    pre-rotation path's second launch."""
-    rows = []
-    names = ["mha_d64_fp16_n%d" % n for n in inputs.CROSSOVER_NS] + [
-        "llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192"]
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    for name in names:
-        w = inputs.WORKLOADS[name]
-        q, k, v = inputs.workload_qkv(name)
-        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        del q, k, v
-        base = w["base"]
-        o = torch.empty_like(qd)
-        lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
-        qr, kr = torch.empty_like(qd), torch.empty_like(kd)
-        krs = torch.empty_like(kd)
-        path, need = rac.auto_plan(w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], qd.dtype, 1 << 62)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        fns = {
-            "fused": lambda: rac.attn_rope_causal_fwd(qd, kd, vd, base, out=o, lse=lse),
-            "prerotate": lambda: (rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
-                                  rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse)),
-            "attn": lambda: rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse),
-            "rope": lambda: rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
-            "split": lambda: (rac.rope_prerotate_k(kd, base, k_rot=krs),
-                              rac.attn_rope_q_causal_fwd(qd, krs, vd, base, out=o, lse=lse)),
-            "auto": lambda: rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws, out=o,
-                                                      lse=lse),
-        }
-        t = {}
-        for key, fn in fns.items():
-            warm(fn, 3, 0.05, torch.cuda.synchronize)
-            pairs = [(ev(), ev()) for _ in range(reps)]
-            for a, b in pairs:
-                a.record(); fn(); b.record()
+
+def _stage_row(torch, rac, inputs, name, dev):
+    """Device tensors of one crossover row (timing-only inputs drawn on the
+    device) and the callables that time each path and kernel."""
+    w = inputs.WORKLOADS[name]
+    qd, kd, vd = inputs.device_qkv(name, dev)
+    base = w["base"]
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    krs = torch.empty_like(kd)
+    path, need = rac.auto_plan(w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], qd.dtype, 1 << 62)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    # the copy ceiling: as many bytes as the pass reads (and then writes)
+    pb = prerot_bytes(w)
+    csrc = torch.empty(int(pb // 2), dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    fns = {
+        "fused": lambda: rac.attn_rope_causal_fwd(qd, kd, vd, base, out=o, lse=lse),
+        "rope": lambda: rac.rope_prerotate(qd, kd, base, q_rot=qr, k_rot=kr),
+        "attn": lambda: rac.attn_causal_fwd(qr, kr, vd, out=o, lse=lse),
+        "rope_k": lambda: rac.rope_prerotate_k(kd, base, k_rot=krs),
+        "attn_q": lambda: rac.attn_rope_q_causal_fwd(qd, krs, vd, base, out=o, lse=lse),
+        "copy": lambda: rac.stream_copy(csrc, cdst),
+        "auto": lambda: rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws, out=o,
+                                                  lse=lse),
+    }
+    fns["prerotate"] = lambda: (fns["rope"](), fns["attn"]())  # noqa: E731
+    fns["split"] = lambda: (fns["rope_k"](), fns["attn_q"]())
+    return {"w": w, "fns": fns, "auto_path": rac.PATH_NAMES[path],
+            "keep": (qd, kd, vd, o, lse, qr, kr, krs, ws, csrc, cdst)}
+
+
+def _events(torch, n):
+    """n pairs of timing events, created up front (torch creates the HIP
+    event at its first record)."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for a, b in pairs:
+        a.record(); b.record()
+    torch.cuda.synchronize()
+    return pairs
+
+
+def _time_row(torch, rac, st, flush, reps, warm_s):
+    """One repeat of one row. Each path is warmed up, then called `reps`
+    times back to back (steady clocks, as in a model's step) with events
+    around each call, then `reps` times more with each of its kernels timed
+    by the events it records at its own start and end (rac.time_next_kernel;
+    those records lengthen the calls, so the two are kept apart); medians.
+    The pass and the copy are also timed cold, one launch at a time after a
+    512 MiB flush written (zero_) or only read (max)."""
+    fns = st["fns"]
+    t = {}
+    plans = (("fused", ("fused",)), ("prerotate", ("rope", "attn")),
+             ("split", ("rope_k", "attn_q")), ("auto", ()), ("copy", ("copy",)))
+    for path, kernels in plans:
+        warm(fns[path], 3, warm_s, torch.cuda.synchronize)
+        if path != "copy":
+            # calls alone: the kernel timer's events are not recorded here
+            calls = _events(torch, reps)
+            for a, b in calls:
+                a.record(); fns[path](); b.record()
             torch.cuda.synchronize()
-            ts = sorted(a.elapsed_time(b) for a, b in pairs)
-            t[key] = ts[len(ts) // 2]
-        # kernel-only times: each kernel's own start-to-end time
-        # (rac.time_next_kernel), warm, and for the streaming pass also after
-        # a cache flush; these leave out launches and host work
-        def kernel_ms(fn, flushed=False):
-            out_ = []
-            for _ in range(reps):
-                a, b = ev(), ev()
-                a.record(); b.record()
-                if flushed:
-                    flush.zero_()
-                rac.time_next_kernel(a, b); fn()
-                torch.cuda.synchronize()
-                out_.append(a.elapsed_time(b))
-            out_.sort()
-            return out_[len(out_) // 2]
-        t["rope"] = kernel_ms(fns["rope"])
-        t_rope_cold = kernel_ms(fns["rope"], flushed=True)
-        tk = {key: kernel_ms(fns[key]) for key in ("fused", "attn")}
-        fl = attn_flops(w)
-        pb = prerot_bytes(w)
-        fastest = min(("fused", "prerotate", "split"), key=lambda p: t[p])
-        rows.append({"workload": name, "N": w["N"], "fused_ms": t["fused"],
-                     "prerotate_ms": t["prerotate"], "attn_only_ms": t["attn"],
-                     "split_ms": t["split"], "auto_ms": t["auto"],
-                     "auto_path": rac.PATH_NAMES[path], "fastest_path": fastest,
-                     "fused_tflops": fl / t["fused"] / 1e9,
-                     "prerotate_tflops": fl / t["prerotate"] / 1e9,
-                     "attn_only_tflops": fl / t["attn"] / 1e9,
-                     "fused_overhead_vs_plain": t["fused"] / t["attn"] - 1.0,
-                     "fused_vs_prerotate_gap": t["fused"] / t["prerotate"] - 1.0,
-                     "fused_kernel_ms": tk["fused"], "attn_kernel_ms": tk["attn"],
-                     "prerotate_kernels_ms": t["rope"] + tk["attn"],
-                     "fused_vs_prerotate_kernel_gap": tk["fused"] / (t["rope"] + tk["attn"]) - 1.0,
-                     "rope_prerotate_ms": t["rope"], "rope_prerotate_gbs": pb / t["rope"] / 1e6,
-                     "rope_prerotate_cold_ms": t_rope_cold,
-                     "rope_prerotate_cold_gbs": pb / t_rope_cold / 1e6,
-                     "rope_prerotate_cold_hbm_frac": pb / t_rope_cold / 1e6 / HBM_PEAK_GBS})
-        del qd, kd, vd, o, lse, qr, kr, krs, ws
-        torch.cuda.empty_cache()
-    sweep = [r for r in rows if r["workload"].startswith("mha_d64")]
-    calls = locate_crossover(sweep, "fused_ms", "prerotate_ms")
-    kernels = locate_crossover(sweep, "fused_kernel_ms", "prerotate_kernels_ms")
-    return {"n_star": calls["n_star"], "bracket": calls["bracket"],
-            "gaps_at_bracket": calls["gaps_at_bracket"],
-            "winner_if_no_crossing": calls["winner_if_no_crossing"],
-            "kernels": kernels,
+            t["c_" + path] = _median([a.elapsed_time(b) for a, b in calls]) * 1e3
+        kev = {k: _events(torch, reps) for k in kernels}
+        for i in range(reps):
+            for k in kernels:
+                rac.time_next_kernel(*kev[k][i]); fns[k]()
+        torch.cuda.synchronize()
+        for k in kernels:
+            t["k_" + k] = _median([a.elapsed_time(b) for a, b in kev[k]]) * 1e3
+
+    def cold_us(fn, how):
+        out_ = []
+        for a, b in _events(torch, reps):
+            if how == "write":
+                flush.zero_()
+            else:
+                flush.max()
+            rac.time_next_kernel(a, b); fn()
+            torch.cuda.synchronize()
+            out_.append(a.elapsed_time(b))
+        return _median(out_) * 1e3
+
+    for key in ("rope", "copy"):
+        t["k_%s_cold" % key] = cold_us(fns[key], "write")
+        t["k_%s_cold_read" % key] = cold_us(fns[key], "read")
+    return t
+
+
+def crossover(torch, rac, inputs, dev, ev, repeats=3, reps=11):
+    """Fused vs pre-rotation (and GQA split) over the crossover families,
+    each row timed `repeats` times (interleaved: one pass over every row,
+    then the next), and the Rotation Calculus model fitted to the same rows.
+
+    Per row and time: the median over repeats (each repeat's own figure is
+    the median of `reps` calls), and the min/median/max of the fused vs
+    pre-rotation gap over repeats. N* per family is located twice: over the
+    kernels' own times (the fused kernel vs the pass plus plain attention;
+    the headline) and over call times (which add the pre-rotation path's
+    second launch). The model (rotary_position_embedding_causal_amd.
+    dispatch_fit) is fitted to the median kernel times of all rows, and its
+    N* per family set beside the measured one; the dispatcher's own constants
+    (csrc/dispatch_model.h) are checked against the call times: auto_ms vs
+    the fastest path per row."""
+    from rotary_position_embedding_causal_amd import dispatch_fit
+    fams = inputs.CROSSOVER_FAMILIES
+    names = [n for _, rows in fams.values() for n in rows] + list(inputs.CROSSOVER_EXTRA)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    staged = {name: _stage_row(torch, rac, inputs, name, dev) for name in names}
+    samples = {name: [] for name in names}
+    for r in range(repeats):
+        for name in names:
+            samples[name].append(_time_row(torch, rac, staged[name], flush, reps,
+                                           0.05 if r == 0 else 0.02))
+        print("crossover repeat %d/%d done" % (r + 1, repeats), file=sys.stderr, flush=True)
+    rows = []
+    for name in names:
+        st, ts = staged[name], samples[name]
+        w = st["w"]
+        med = {key: _median([t[key] for t in ts]) for key in ts[0]}
+        fl, pb, kb = attn_flops(w), prerot_bytes(w), prerot_k_bytes(w)
+        gk = sorted(t["k_fused"] / (t["k_rope"] + t["k_attn"]) - 1.0 for t in ts)
+        gc = sorted(t["c_fused"] / t["c_prerotate"] - 1.0 for t in ts)
+        calls = {p: med["c_" + p] for p in ("fused", "prerotate", "split")}
+        fastest = min(calls, key=calls.get)
+        row = {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "N": w["N"],
+               "D": w["D"], "dtype": w["dtype"]}
+        row.update({k_: v_ for k_, v_ in med.items()})
+        row.update({
+            "auto_path": st["auto_path"], "fastest_path": fastest,
+            "auto_vs_fastest": med["c_auto"] / calls[fastest] - 1.0,
+            "gap_kernels": {"min": gk[0], "median": _median(gk), "max": gk[-1]},
+            "gap_calls": {"min": gc[0], "median": _median(gc), "max": gc[-1]},
+            "fused_tflops": fl / med["k_fused"] / 1e6,
+            "attn_tflops": fl / med["k_attn"] / 1e6,
+            "attn_q_tflops": fl / med["k_attn_q"] / 1e6,
+            "fused_mfma_frac": fl / med["k_fused"] / 1e6 / MFMA_PEAK_TFLOPS[w["dtype"]],
+            "attn_mfma_frac": fl / med["k_attn"] / 1e6 / MFMA_PEAK_TFLOPS[w["dtype"]],
+            "rope_gbs": pb / med["k_rope"] / 1e3,
+            "rope_cold_gbs": pb / med["k_rope_cold"] / 1e3,
+            "rope_cold_hbm_frac": pb / med["k_rope_cold"] / 1e3 / HBM_PEAK_GBS,
+            "rope_cold_read_hbm_frac": pb / med["k_rope_cold_read"] / 1e3 / HBM_PEAK_GBS,
+            "copy_gbs": pb / med["k_copy"] / 1e3,
+            "copy_cold_hbm_frac": pb / med["k_copy_cold"] / 1e3 / HBM_PEAK_GBS,
+            "copy_cold_read_hbm_frac": pb / med["k_copy_cold_read"] / 1e3 / HBM_PEAK_GBS,
+            "rope_k_gbs": kb / med["k_rope_k"] / 1e3,
+            "samples": ts})
+        rows.append(row)
+    del staged
+    torch.cuda.empty_cache()
+
+    # the model, fitted to this run's rows
+    fit = dispatch_fit.fit(rows)
+    header = dispatch_fit.load_params()
+    byname = {r["workload"]: r for r in rows}
+    families = {}
+    for fam, (desc, fam_rows) in fams.items():
+        sweep = [byname[n] for n in fam_rows]
+        w0 = sweep[0]
+        cls = dispatch_fit.class_key(w0["D"], w0["Hq"], w0["Hkv"])
+        kern = locate_crossover(sweep, "k_fused", None, pre_fn=lambda r: r["k_rope"] + r["k_attn"])
+        per_rep = []
+        for i in range(repeats):
+            reps_i = [dict(N=r["N"], f=r["samples"][i]["k_fused"],
+                           p=r["samples"][i]["k_rope"] + r["samples"][i]["k_attn"]) for r in sweep]
+            per_rep.append(locate_crossover(reps_i, "f", "p")["n_star"])
+        callx = locate_crossover(sweep, "c_fused", "c_prerotate")
+        full = dict(fit)
+        full.update({c: fit[cls] for c in dispatch_fit.CLASSES})
+        n_model = dispatch_fit.n_star_model(full, 1, w0["Hq"], w0["Hkv"], w0["D"])
+        n_closed = dispatch_fit.n_star_closed(fit[cls], fit, w0["Hq"], w0["Hkv"])
+        measured = kern["n_star"]
+        worst = max(r["auto_vs_fastest"] for r in sweep)
+        families[fam] = {
+            "desc": desc, "class": cls, "N": [r["N"] for r in sweep],
+            "n_star_kernels": kern, "n_star_kernels_per_repeat": per_rep,
+            "n_star_calls": callx,
+            "n_star_model": n_model, "n_star_closed_form": n_closed,
+            "model_vs_measured": (n_model / measured - 1.0) if (n_model and measured) else None,
+            "auto_worst_vs_fastest": worst, "auto_within_2pct": worst <= 0.02}
+    for r in rows:
+        del r["samples"]  # per-repeat figures: summarised above
+    head = families["mha_d64_fp16"]
+    c64 = fit["d64_mha"]
+    model = {"alpha": c64["alpha_qk"], "eta_mfma": c64["eta_attn"], "eta_bw": fit["eta_bw"],
+             "n_star_model": head["n_star_model"], "n_star_closed_form": head["n_star_closed_form"],
+             "alpha_underfilled": c64["alpha_qk_underfilled"], "t0_us": fit["t0_us"],
+             "t_gap_us": fit["t_gap_us"], "fit": fit,
+             "dispatcher_constants": header,
+             "form": "T_k = max(F/(eta_k P), t_tile_k N/128) per kernel; alpha = eta_attn/eta_fused"
+                     " - 1; pre = t0 + 4B(Hq+Hkv)ND/(eta_bw BW) + T_attn; N* where T_fused = pre"}
+    return {"n_star": head["n_star_kernels"]["n_star"],
+            "level": "kernels (the fused kernel vs the pass plus plain attention)",
+            "bracket": head["n_star_kernels"]["bracket"],
+            "gaps_at_bracket": head["n_star_kernels"]["gaps_at_bracket"],
+            "n_star_per_repeat": head["n_star_kernels_per_repeat"],
+            "n_star_calls": head["n_star_calls"]["n_star"],
+            "winner_if_no_crossing": head["n_star_kernels"]["winner_if_no_crossing"],
+            "model": model, "families": families, "repeats": repeats,
             "sweep": "mha_d64_fp16 N=1024..32768 (B=1, H=16)", "rows": rows}
 
 
-def locate_crossover(sweep, fused_key, pre_key):
+def locate_crossover(sweep, fused_key, pre_key, pre_fn=None):
     """N* over the sweep rows (ascending N): the first sign change of
-    t_fused − t_prerotate, log-linearly interpolated in the relative gap;
+    t_fused - t_prerotate, log-linearly interpolated in the relative gap;
     with no change, which path won at every N ("mixed" if neither)."""
+    pre = pre_fn or (lambda r: r[pre_key])
     n_star = bracket = gaps = winner = None
     for a, b in zip(sweep, sweep[1:]):
-        da = a[fused_key] - a[pre_key]
-        db = b[fused_key] - b[pre_key]
+        da = a[fused_key] - pre(a)
+        db = b[fused_key] - pre(b)
         if (da < 0) != (db < 0):
-            ga, gb = da / a[pre_key], db / b[pre_key]
+            ga, gb = da / pre(a), db / pre(b)
             x = ga / (ga - gb)
             n_star = math.exp(math.log(a["N"]) + x * (math.log(b["N"]) - math.log(a["N"])))
             bracket = [a["N"], b["N"]]
             # the relative gaps at the bracket's ends: a sign change between
             # gaps of a few percent is within the run-to-run spread
-            gaps = [r[fused_key] / r[pre_key] - 1.0 for r in (a, b)]
+            gaps = [r[fused_key] / pre(r) - 1.0 for r in (a, b)]
             break
     if n_star is None and sweep:
-        winner = "fused" if all(r[fused_key] < r[pre_key] for r in sweep) else (
-            "prerotate" if all(r[fused_key] > r[pre_key] for r in sweep) else "mixed")
+        winner = "fused" if all(r[fused_key] < pre(r) for r in sweep) else (
+            "prerotate" if all(r[fused_key] > pre(r) for r in sweep) else "mixed")
     return {"n_star": n_star, "bracket": bracket, "gaps_at_bracket": gaps,
             "winner_if_no_crossing": winner}
 

@@ -242,17 +242,23 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
 /*
  * Dispatcher: out/lse of attn_rope_causal_fwd (bit-identical: every path hands
  * the same rotated operands to the same attention arithmetic), computed by the
- * path measured fastest on MI355X for this shape -- with GQA the split path
- * at every length; with MHA the fused kernel below N = 1536 (where the
- * streaming pass's fixed cost and second launch outweigh the in-kernel
- * rotation of every key tile), the split path from 1536 to 12287 and
- * pre-rotation of Q and K from 12288. The choice of pre-rotation versus in-kernel
- * rotation is the one the AttnFuse report, paragraphs 3 and 5, says depends
- * on the GPU and the shape.
+ * path with the least modelled time on MI355X for this shape. The model costs
+ * the streaming pass by its bytes (4 B H N D for H rotated heads) at a fitted
+ * fraction of 8 TB/s plus a fixed cost and a second launch, the attention
+ * kernel by its work at a fitted fraction of the MFMA peak (or, when the grid
+ * is too small to fill the chip, by one workgroup's N / 128 key tiles), and
+ * in-kernel rotation as a fitted fraction of the attention time; the
+ * constants are fitted per head dim (64, 128) and MHA/GQA to kernel times
+ * measured over D = 64 and 128, bf16 and fp16, MHA, GQA 4:1 and 8:1,
+ * N = 1024 .. 32768. It weighs the whole problem: more batch or heads at the
+ * same N moves the choice as the work moves it. The choice of pre-rotation
+ * versus in-kernel rotation is the one the AttnFuse report, paragraphs 3 and
+ * 5, says depends on the GPU and the shape.
  *
  * workspace: caller-owned device memory for the rotated copies (Q' and K',
- * or K' alone), 16-byte aligned, not overlapping any tensor argument; the
- * library allocates nothing (the fused path needs none). If it is NULL or
+ * or K' alone), 16-byte aligned; its whole workspace_bytes must not overlap
+ * any tensor argument (checked whichever path is taken); the library
+ * allocates nothing (the fused path needs none). If it is NULL or
  * smaller than the preferred path needs, the next path it holds is taken
  * (split, then fused); so is a path whose streaming pass would exceed its
  * grid (more than 8 * 65535 slabs). rac_auto_plan tells the path and the
@@ -327,6 +333,15 @@ const char* rac_last_error(void);
  * taken a table pointer and not yet enqueued the kernel that reads it.
  * Returns RAC_OK or RAC_ERR_HIP. */
 int rac_release_tables(void);
+
+/* Bandwidth ceiling (instrumentation; defines no part of the method). A
+ * plain device-to-device copy of `bytes` bytes from `src` to `dst` (device
+ * pointers, 16-byte aligned, not overlapping; `bytes` a multiple of 16) with
+ * the pre-rotation pass's memory access pattern (16-byte non-temporal loads
+ * and stores, 256-lane workgroups): the rate the pass could reach if rotating
+ * cost nothing. Enqueued on `stream`; the kernel timer times it like a pass.
+ * bytes == 0 is a no-op. Returns RAC_OK, RAC_ERR_ARG or RAC_ERR_ALIGN. */
+int rac_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Kernel timing (instrumentation; defines no part of the method). Arms a
  * pair of HIP events (hipEvent_t handles, created by the caller with timing

@@ -38,7 +38,7 @@ EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_p
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
             "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
             "rac_last_error", "rac_release_tables", "rac_time_next_kernel",
-            "attn_rope_causal_fwd_noalloc")
+            "attn_rope_causal_fwd_noalloc", "rac_stream_copy")
 RAC_NOALLOC_MAX_N = 32768
 RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
 PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.rac_release_tables.restype = i
     L.rac_time_next_kernel.argtypes = [vp, vp]
     L.rac_time_next_kernel.restype = i
+    L.rac_stream_copy.argtypes = [vp, vp, sz, vp]
+    L.rac_stream_copy.restype = i
     L.attn_rope_causal_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, vp]
     L.attn_rope_causal_fwd_noalloc.restype = i
     _lib = L
@@ -315,6 +317,19 @@ def rope_prerotate_k(k, rope_base: float, k_rot=None):
                                     _stream(k.device))
     check(rc, "rope_prerotate_k")
     return k_rot
+
+
+def stream_copy(src, dst) -> None:
+    """A plain device copy of src into dst (contiguous, same byte size) with
+    the pre-rotation pass's access pattern: its bandwidth ceiling."""
+    if not (src.is_contiguous() and dst.is_contiguous()) or src.device != dst.device:
+        raise ValueError("src and dst must be contiguous tensors on one device")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    with torch.cuda.device(src.device):
+        rc = lib().rac_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device))
+    check(rc, "rac_stream_copy")
 
 
 def attn_rope_q_causal_fwd(q, k_rot, v, rope_base: float, out=None, lse=None,

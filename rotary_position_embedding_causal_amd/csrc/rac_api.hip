@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/rac.h"
+#include "dispatch_model.h"
 #include "rac_internal.h"
 
 namespace {
@@ -273,14 +274,13 @@ int bwd_shape_from_env() {
 //
 // All three paths give bit-identical results (they hand the same rotated
 // operands to the same attention arithmetic), so the choice is about time
-// only. Measured on MI355X (bench crossover rows, median of 15 calls after a
-// 50 ms warm-up, three runs; bf16 D=128 GQA 4:1 at N = 2048 / 4096 (B=4) /
-// 8192 and fp16 D=64 MHA at N = 1024 .. 32768): with GQA the split path (K
-// pre-rotated, Q rotated once per row in the kernel) was fastest at every N,
-// 4-11 % ahead of the fused kernel; with MHA the fused kernel led at
-// N = 1024 (by 9 %, where the streaming pass's fixed cost and second launch
-// weigh most), the split path led or tied from 2048 to 8192, and
-// pre-rotation of Q and K led at 16384 (by 3 %) and tied at 32768.
+// only: the path with the least modelled time (dispatch_model.h: a cost model
+// of the attention kernel, the in-kernel rotation and the streaming pass,
+// fitted per head dim and MHA/GQA class to kernel times measured on MI355X).
+// The model weighs the whole problem (B, heads, N, D), not N alone: the pass
+// costs bytes, the rotation a share of the attention's time, and an
+// under-filled grid (few heads, short N) keeps the attention time from
+// shrinking with the work.
 size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
     const size_t q = (size_t)B * Hq * N * D * 2, k = (size_t)B * Hkv * N * D * 2;
     const size_t q16 = (q + 255) & ~(size_t)255;  // K' starts 256-byte aligned
@@ -289,11 +289,14 @@ size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
     return 0;
 }
 
-int preferred_path(int Hq, int Hkv, int N) {
-    if (Hq / Hkv >= 2) return RAC_PATH_SPLIT;
-    // MHA: thresholds between the measured points
-    if (N < 1536) return RAC_PATH_FUSED;
-    return N < 12288 ? RAC_PATH_SPLIT : RAC_PATH_PREROTATE;
+int preferred_path(int B, int Hq, int Hkv, int N, int D) {
+    double fused = 0, prerot = 0, split = 0;
+    rac_model::path_times(B, Hq, Hkv, N, D, &fused, &prerot, &split);
+    int best = RAC_PATH_FUSED;
+    double t = fused;
+    if (prerot < t) best = RAC_PATH_PREROTATE, t = prerot;
+    if (split < t) best = RAC_PATH_SPLIT;
+    return best;
 }
 
 // Whether a path's streaming pass fits its grid (at most 8 * 65535 slabs:
@@ -308,7 +311,7 @@ bool pass_fits(int path, int B, int Hq, int Hkv) {
 // The preferred path if the workspace holds it (and its pass fits its grid),
 // else the next one that does: pre-rotation, then split, then fused.
 int plan_path(int B, int Hq, int Hkv, int N, int D, size_t workspace_bytes) {
-    const int pref = preferred_path(Hq, Hkv, N);
+    const int pref = preferred_path(B, Hq, Hkv, N, D);
     auto usable = [&](int path) {
         return pass_fits(path, B, Hq, Hkv) &&
                workspace_bytes >= path_workspace(path, B, Hq, Hkv, N, D);
@@ -572,7 +575,7 @@ int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t worksp
     bool empty = false;
     const int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
-    const int pref = preferred_path(Hq, Hkv, N);
+    const int pref = preferred_path(B, Hq, Hkv, N, D);
     if (path) *path = empty ? RAC_PATH_FUSED : plan_path(B, Hq, Hkv, N, D, workspace_bytes);
     if (preferred_bytes) *preferred_bytes = empty ? 0 : path_workspace(pref, B, Hq, Hkv, N, D);
     return ok();
@@ -589,17 +592,21 @@ int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out
     if (empty) return ok();
     if ((rc = check_attn_ptrs(q, k, v, out, lse, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     if (!workspace) workspace_bytes = 0;
+    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
+    const int64_t kvbytes = (int64_t)B * Hkv * N * D * 2;
+    if (workspace_bytes > 0) {
+        // the whole workspace given, whichever path is taken
+        if (!aligned16(workspace)) return fail(RAC_ERR_ALIGN, "workspace must be 16-byte aligned");
+        const int64_t wbytes = workspace_bytes > ((size_t)1 << 62) ? (int64_t)1 << 62
+                                                                   : (int64_t)workspace_bytes;
+        if (overlap(workspace, wbytes, q, qbytes) || overlap(workspace, wbytes, k, kvbytes) ||
+            overlap(workspace, wbytes, v, kvbytes) || overlap(workspace, wbytes, out, qbytes) ||
+            (lse && overlap(workspace, wbytes, lse, (int64_t)B * Hq * N * 4)))
+            return fail(RAC_ERR_ARG, "workspace must not overlap q, k, v, out or lse");
+    }
     const int path = plan_path(B, Hq, Hkv, N, D, workspace_bytes);
     if (path == RAC_PATH_FUSED)
         return attn_rope_causal_fwd(q, k, v, out, lse, B, Hq, Hkv, N, D, rope_base, dtype, stream);
-    if (!aligned16(workspace)) return fail(RAC_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
-    const int64_t kvbytes = (int64_t)B * Hkv * N * D * 2;
-    const int64_t wbytes = (int64_t)path_workspace(path, B, Hq, Hkv, N, D);
-    if (overlap(workspace, wbytes, q, qbytes) || overlap(workspace, wbytes, k, kvbytes) ||
-        overlap(workspace, wbytes, v, kvbytes) || overlap(workspace, wbytes, out, qbytes) ||
-        (lse && overlap(workspace, wbytes, lse, (int64_t)B * Hq * N * 4)))
-        return fail(RAC_ERR_ARG, "workspace must not overlap q, k, v, out or lse");
     char* ws = static_cast<char*>(workspace);
     if (path == RAC_PATH_SPLIT) {
         if ((rc = rope_prerotate_k(k, ws, B, Hkv, N, D, rope_base, dtype, stream)) != RAC_OK)
@@ -614,6 +621,21 @@ int attn_rope_causal_auto(const void* q, const void* k, const void* v, void* out
 }
 
 const char* rac_last_error(void) { return g_last_error.c_str(); }
+
+int rac_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    const TimerScope timer_scope;
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(RAC_ERR_ARG, "src and dst must be non-null");
+    if (bytes % 16 != 0) return fail(RAC_ERR_ARG, "bytes must be a multiple of 16");
+    if (bytes > (size_t)1 << 46) return fail(RAC_ERR_ARG, "bytes must be <= 2^46");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(RAC_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    if (overlap(dst, (int64_t)bytes, src, (int64_t)bytes))
+        return fail(RAC_ERR_ARG, "src and dst must not overlap");
+    return hip_status(rac::launch_stream_copy(src, dst, (int64_t)bytes,
+                                              static_cast<hipStream_t>(stream)),
+                      "rac_stream_copy launch");
+}
 
 int rac_time_next_kernel(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr))

@@ -78,6 +78,9 @@ enum { BWD_SHAPE_AUTO = 0, BWD_SHAPE_K128 = 1, BWD_SHAPE_K64 = 2, BWD_SHAPE_K64X
 hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream);
 
 // q_rot = RoPE(q), k_rot = RoPE(k).
+// A plain streaming device copy of `bytes` (a multiple of 16) bytes.
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
                                  const float* table, int B, int Hq, int Hkv, int N, int D,
                                  int dtype, hipStream_t stream);

@@ -192,6 +192,39 @@ static hipError_t launch_any(const void* q, const void* k, void* q_rot, void* k_
                    : launch_typed<DT_FP16, 128, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
 }
 
+// A plain device copy with the pass's access pattern: 16-byte non-temporal
+// loads and stores, 256-lane workgroups, COPY_CHUNKS chunks per lane in
+// flight (a workgroup moves COPY_CHUNKS * 4 KiB; chunk j of lane t sits at
+// (j * 256 + t) * 16 bytes into the workgroup's span, so each load and store
+// instruction of a wave covers 1 KiB of consecutive bytes). It computes
+// nothing: it is the bandwidth ceiling the pass is measured against.
+constexpr int COPY_CHUNKS = 4;
+
+__global__ __launch_bounds__(PR_THREADS) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                                 u32x4* __restrict__ dst,
+                                                                 int64_t chunks) {
+    const int64_t first = (int64_t)blockIdx.x * (COPY_CHUNKS * PR_THREADS) + threadIdx.x;
+    u32x4 x[COPY_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < COPY_CHUNKS; ++j) {
+        const int64_t c = first + (int64_t)j * PR_THREADS;
+        if (c < chunks) x[j] = __builtin_nontemporal_load(src + c);
+    }
+#pragma unroll
+    for (int j = 0; j < COPY_CHUNKS; ++j) {
+        const int64_t c = first + (int64_t)j * PR_THREADS;
+        if (c < chunks) __builtin_nontemporal_store(x[j], dst + c);
+    }
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    const int64_t chunks = bytes / 16;
+    const int64_t per_block = (int64_t)COPY_CHUNKS * PR_THREADS;
+    const unsigned grid = (unsigned)((chunks + per_block - 1) / per_block);
+    return launch_kernel(stream_copy_kernel, dim3(grid), dim3(PR_THREADS), stream,
+                         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks);
+}
+
 hipError_t launch_rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot,
                                  const float* table, int B, int Hq, int Hkv, int N, int D,
                                  int dtype, hipStream_t stream) {

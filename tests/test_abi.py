@@ -7,6 +7,7 @@ import re
 import pytest
 
 import rotary_position_embedding_causal_amd as rac
+from rotary_position_embedding_causal_amd import dispatch_fit
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rac.h")
@@ -133,6 +134,19 @@ def test_prerotate_k_argument_rules():
     assert prerot_k(N=0, k=None, kr=None) == rac.RAC_OK
 
 
+def test_stream_copy_argument_rules():
+    cp = rac.lib().rac_stream_copy
+    assert cp(Q, ctypes.c_void_p(P + 16), 4096, None) == rac.RAC_ERR_ARG  # overlap
+    assert cp(Q, K, P + 16, None) == rac.RAC_ERR_ARG                     # overlap
+    assert cp(Q, K, 24, None) == rac.RAC_ERR_ARG                       # not a multiple of 16
+    assert cp(None, K, 16, None) == rac.RAC_ERR_ARG
+    assert cp(Q, None, 16, None) == rac.RAC_ERR_ARG
+    assert cp(ctypes.c_void_p(P + 8), K, 16, None) == rac.RAC_ERR_ALIGN
+    assert cp(Q, ctypes.c_void_p(2 * P + 4), 16, None) == rac.RAC_ERR_ALIGN
+    assert cp(None, None, 0, None) == rac.RAC_OK
+    assert rac.last_error() == ""
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, q=None, k=None, v=None,
                                                            out=None, lse=None)])
 def test_empty_problem_is_a_noop(kw):
@@ -191,36 +205,77 @@ def test_dispatcher_workspace_rules():
     assert auto(B=0) == rac.RAC_OK
 
 
-def test_auto_plan_paths():
-    B, Hq, Hkv, D = 1, 32, 8, 128
-    # GQA: the split path (K' only) at every length, else the fused kernel
-    for N in (1, 512, 2048, 4096, 8192):
-        path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 40)
-        assert path == rac.RAC_PATH_SPLIT and need == B * Hkv * N * D * 2
-        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, need - 1)[0] == rac.RAC_PATH_FUSED
-        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
-    # MHA long sequences: Q' and K' (pre-rotation); too small for both: K' alone, then none
-    H, N = 16, 16384
-    path, need = rac.auto_plan(B, H, H, N, 64, rac.RAC_FP16, 1 << 40)
-    q = B * H * N * 64 * 2
-    assert path == rac.RAC_PATH_PREROTATE and need == ((q + 255) // 256) * 256 + q
-    assert rac.auto_plan(B, H, H, N, 64, 1, need - 1)[0] == rac.RAC_PATH_SPLIT
-    assert rac.auto_plan(B, H, H, N, 64, 1, q - 1)[0] == rac.RAC_PATH_FUSED
-    # MHA: the fused kernel below 1536, the split path up to 12287, then pre-rotation
-    for N, want in ((1, rac.RAC_PATH_FUSED), (1024, rac.RAC_PATH_FUSED),
-                    (1535, rac.RAC_PATH_FUSED), (1536, rac.RAC_PATH_SPLIT),
-                    (6144, rac.RAC_PATH_SPLIT), (12287, rac.RAC_PATH_SPLIT),
-                    (12288, rac.RAC_PATH_PREROTATE), (32768, rac.RAC_PATH_PREROTATE)):
-        path, need = rac.auto_plan(1, 16, 16, N, 64, rac.RAC_FP16, 1 << 40)
-        assert path == want, N
-        if want == rac.RAC_PATH_FUSED:
+PATH_CODES = {"fused": rac.RAC_PATH_FUSED, "prerotate": rac.RAC_PATH_PREROTATE,
+              "split": rac.RAC_PATH_SPLIT}
+
+
+def _model_choice(B, Hq, Hkv, N, D):
+    """The path-cost model's choice, or None within 1e-9 of a tie."""
+    p = dispatch_fit.load_params()
+    t = dispatch_fit.model_us(p, B, Hq, Hkv, N, D)
+    order = sorted(t.values())
+    if order[1] - order[0] <= 1e-9 * order[0]:
+        return None
+    return dispatch_fit.choose(p, B, Hq, Hkv, N, D)
+
+
+def test_auto_plan_follows_the_cost_model():
+    """With room for any workspace, rac_auto_plan takes the path the fitted
+    model (dispatch_model.h, evaluated here from the same constants) costs
+    least -- over batch, heads, GQA ratio, length and head dim."""
+    seen = set()
+    for D in (64, 128):
+        for Hq, Hkv in ((4, 4), (16, 16), (32, 32), (32, 8), (64, 8), (8, 1)):
+            for B in (1, 2, 8, 64):
+                for N in (1, 64, 300, 1024, 1500, 2048, 3000, 4096, 6144, 8192, 16384, 32768,
+                          65536):
+                    want = _model_choice(B, Hq, Hkv, N, D)
+                    if want is None:
+                        continue
+                    path, need = rac.auto_plan(B, Hq, Hkv, N, D, rac.RAC_BF16, 1 << 62)
+                    assert path == PATH_CODES[want], (B, Hq, Hkv, N, D, want)
+                    seen.add(want)
+    assert seen == set(PATH_CODES)  # the grid reaches every path
+
+
+def test_auto_plan_workspace_fallbacks():
+    """The preferred path's bytes, and the fallbacks when the workspace is short."""
+    for B, H, Hkv, N, D in ((1, 16, 16, 16384, 64), (1, 32, 8, 8192, 128), (1, 16, 16, 512, 64),
+                            (8, 32, 32, 4096, 128)):
+        want = dispatch_fit.choose(dispatch_fit.load_params(), B, H, Hkv, N, D)
+        path, need = rac.auto_plan(B, H, Hkv, N, D, rac.RAC_FP16, 1 << 40)
+        assert path == PATH_CODES[want]
+        q, k = B * H * N * D * 2, B * Hkv * N * D * 2
+        if want == "prerotate":
+            assert need == ((q + 255) // 256) * 256 + k
+            assert rac.auto_plan(B, H, Hkv, N, D, 1, need - 1)[0] == rac.RAC_PATH_SPLIT
+            assert rac.auto_plan(B, H, Hkv, N, D, 1, k - 1)[0] == rac.RAC_PATH_FUSED
+        elif want == "split":
+            assert need == k
+            assert rac.auto_plan(B, H, Hkv, N, D, 1, need - 1)[0] == rac.RAC_PATH_FUSED
+        else:
             assert need == 0
+        assert rac.auto_plan(B, H, Hkv, N, D, 0, 0)[0] == rac.RAC_PATH_FUSED
+
+
+def test_auto_plan_empty_and_grid_limits():
     assert rac.auto_plan(0, 16, 16, 8192, 64, 1, 0) == (rac.RAC_PATH_FUSED, 0)
-    # a path whose streaming pass exceeds its grid (8 * 65535 slabs) is passed over
-    assert rac.auto_plan(65535, 32, 16, 1, 64, 0, 1 << 40)[0] == rac.RAC_PATH_FUSED  # B*Hkv
-    assert rac.auto_plan(65535, 32, 8, 1, 64, 0, 1 << 40)[0] == rac.RAC_PATH_SPLIT  # 524280
-    assert rac.auto_plan(20000, 16, 16, 16384, 64, 1, 1 << 50)[0] == rac.RAC_PATH_SPLIT
-    assert rac.auto_plan(40000, 16, 16, 16384, 64, 1, 1 << 50)[0] == rac.RAC_PATH_FUSED
+    # a path whose streaming pass exceeds its grid (8 * 65535 slabs) is passed over:
+    # pre-rotation falls back to split, split to fused
+    fell_back = set()
+    for B, Hq, Hkv, N, D in ((65535, 32, 16, 4096, 64), (65535, 32, 8, 4096, 64),
+                             (20000, 16, 16, 16384, 64), (40000, 16, 16, 16384, 64),
+                             (20000, 16, 16, 32768, 128), (40000, 16, 16, 32768, 128),
+                             (4000, 128, 8, 8192, 128)):
+        pref = dispatch_fit.choose(dispatch_fit.load_params(), B, Hq, Hkv, N, D)
+        assert pref != "fused", (B, Hq, Hkv, N, D)
+        fits = {"prerotate": B * (Hq + Hkv) <= 8 * 65535, "split": B * Hkv <= 8 * 65535}
+        want = pref
+        if not fits[want]:
+            want = "split" if want == "prerotate" and fits["split"] else "fused"
+            fell_back.add((pref, want))
+        assert rac.auto_plan(B, Hq, Hkv, N, D, 0, 1 << 60)[0] == PATH_CODES[want], (B, Hq, N)
+    assert ("prerotate", "split") in fell_back and any(w == "fused" for _, w in fell_back)
     with pytest.raises(NotImplementedError):
         rac.auto_plan(1, 4, 4, 64, 96, 0, 0)
     with pytest.raises(ValueError):

@@ -486,3 +486,16 @@ def test_kernel_timer_times_one_launch():
     rac.rope_prerotate(qd, kd, 5e5)
     torch.cuda.synchronize()
     assert a.elapsed_time(b) == t
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16384, 16400, (3 << 20) + 48])
+def test_stream_copy_is_exact(nbytes):
+    """The bandwidth-ceiling copy: every byte lands, nothing past the end is
+    written (sizes below, at and across a workgroup's 16 KiB span)."""
+    g = torch.Generator(device=DEV).manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV, generator=g)
+    dst = torch.full((nbytes + 4096,), 7, dtype=torch.uint8, device=DEV)
+    rac.stream_copy(src, dst[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 7).all())

@@ -266,6 +266,21 @@ struct Wave {
                 *reinterpret_cast<u32x2*>(orow + d0) = w;
             }
     }
+
+    // Writes C^T unscaled in fp32 as row `row` of a [N][D] fp32 tensor (the
+    // same elements per lane as write()).
+    __device__ __forceinline__ static void write_f32(const f32x16 (&acc)[DBLK], float* orow,
+                                                     int hh) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = 32 * i + 8 * gq + 4 * hh;
+                const f32x4 y = {acc[i][4 * gq], acc[i][4 * gq + 1], acc[i][4 * gq + 2],
+                                 acc[i][4 * gq + 3]};
+                *reinterpret_cast<f32x4*>(orow + d0) = y;
+            }
+    }
 };
 
 // 1-D work-unit index, XCD-aware order (the hardware deals workgroup ids
@@ -393,14 +408,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // and dV are added in a fixed order through LDS (still one writer per
 // element and deterministic). The heaviest key tiles then finish QS times
 // sooner when there are too few workgroups to keep every CU busy.
+// With HS = 2 (GQA, an even group) two workgroups share each key tile, one
+// per half of the group's query heads, so the heaviest tiles carry half the
+// steps and the heaviest-first order balances the CUs; each writes its
+// unscaled fp32 sums to `part` ([half][dK, dV][B*Hkv*N][D]) and
+// kv_reduce_kernel adds the two halves (a + b: the same value whichever
+// finished first) and finishes dK and dV as the single-writer epilogue does.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int RM, int RW, int QS>
+template <int DT, int D, int RM, int RW, int QS, int HS>
 __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, const float* __restrict__ table, int Hq, int Hkv, int N,
-    int n_ktiles, float scale_log2, float scale) {
+    uint16_t* __restrict__ dv, float* __restrict__ part, const float* __restrict__ table, int Hq,
+    int Hkv, int N, int n_ktiles, float scale_log2, float scale) {
     constexpr bool ROPE = RM == ROT_QK;
     constexpr int KW = 32 * RW;  // keys per workgroup
     typedef Wave<DT, D> W;
@@ -417,10 +438,11 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     const bool dk_role = wave >= RW;
     const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int bg, slot;
-    decode(n_ktiles, bg, slot);
-    const int kt = slot;  // heaviest first: key tile 0 sees every query
+    decode(n_ktiles * HS, bg, slot);
+    const int kt = slot / HS;  // heaviest first: key tile 0 sees every query
+    const int hs = slot % HS;  // which half of the group's query heads (HS = 2)
     const int b = bg / Hkv, g = bg % Hkv;
-    const int group = Hq / Hkv;
+    const int group = Hq / Hkv / HS;  // query heads this workgroup walks
     const int kw0 = kt * KW + 32 * (wave % RW);
     const int key = kw0 + n;
     const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
@@ -431,7 +453,7 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     const int steps = per_head * group;
     const int rounds = (steps + QS - 1) / QS;  // group qg takes step s * QS + qg of round s
     auto job = [&](int i, int& qh, int& tq) {
-        qh = g * group + i / per_head;
+        qh = (g * HS + hs) * group + i / per_head;
         tq = t0 + i % per_head;
     };
     uint16_t* gbuf = smem + qg * 4 * TILE;
@@ -525,17 +547,70 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
                 for (int j = 0; j < 16; ++j) acc[i][j] += red[(16 * i + j) * 64];
         }
         if (key < N) {
-            if (DK)
+            if constexpr (HS > 1) {
+                const int64_t kv_rows = (int64_t)gridDim.x / (n_ktiles * HS) * N;
+                W::write_f32(acc, part + ((2 * hs + (DK ? 0 : 1)) * kv_rows + kvhead + key) * D,
+                             hh);
+            } else if (DK) {
                 W::write(acc, scale, dk + (kvhead + key) * D,
                          ROPE ? table + (int64_t)key * D : nullptr, hh);
-            else
+            } else {
                 W::write(acc, 1.f, dv + (kvhead + key) * D, nullptr, hh);
+            }
         }
     };
     if (dk_role)
         run(std::integral_constant<bool, true>());
     else
         run(std::integral_constant<bool, false>());
+}
+
+// The two halves' sums of a head-split dK/dV pass: dV = a + b, and dK the
+// same sum scaled by tau and (RoPE) turned back by R(-p), exactly as
+// Wave::write finishes a single workgroup's sums. One thread per 4 elements
+// (two pairs) of a row of dK and of dV.
+template <int DT, bool ROPE>
+__global__ __launch_bounds__(256) void kv_reduce_kernel(const float* __restrict__ part,
+                                                        uint16_t* __restrict__ dk,
+                                                        uint16_t* __restrict__ dv,
+                                                        const float* __restrict__ table,
+                                                        int64_t kv_rows, int N, int D,
+                                                        float scale) {
+    typedef Fmt<DT> F;
+    const int64_t quads = kv_rows * D / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= quads) return;
+    const int64_t e = 4 * i;  // element offset in [kv_rows][D]
+    const int64_t span = kv_rows * D;
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(part + e);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(part + span + e);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(part + 2 * span + e);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(part + 3 * span + e);
+    float y[4], x[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        y[t] = (k0[t] + k1[t]) * scale;
+        x[t] = (v0[t] + v1[t]) * 1.f;
+    }
+    if (ROPE) {
+        const int64_t row = e / D;
+        const int d0 = (int)(e % D);
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(table + (row % N) * D + d0);
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const float c = cs[2 * pr], s = cs[2 * pr + 1];
+            const float y0 = y[2 * pr], y1 = y[2 * pr + 1];
+            y[2 * pr] = __builtin_fmaf(y0, c, y1 * s);
+            y[2 * pr + 1] = __builtin_fmaf(y1, c, -(y0 * s));
+        }
+    }
+    u32x2 wk, wv;
+    wk[0] = F::pack2(y[0], y[1]);
+    wk[1] = F::pack2(y[2], y[3]);
+    wv[0] = F::pack2(x[0], x[1]);
+    wv[1] = F::pack2(x[2], x[3]);
+    *reinterpret_cast<u32x2*>(dk + e) = wk;
+    *reinterpret_cast<u32x2*>(dv + e) = wv;
 }
 
 template <int DT, int D, int RM>
@@ -549,7 +624,8 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     const int64_t k_units_128 = (int64_t)((a.N + 127) / 128) * a.Hkv * a.B;
     int rw = k_units_128 >= 256 ? 4 : 2;
     if (a.shape == BWD_SHAPE_K128) rw = 4;
-    if (a.shape == BWD_SHAPE_K64 || a.shape == BWD_SHAPE_K64X2) rw = 2;
+    if (a.shape == BWD_SHAPE_K64 || a.shape == BWD_SHAPE_K64X2 || a.shape == BWD_SHAPE_K64X2H)
+        rw = 2;
     const int n_ktiles = (a.N + 32 * rw - 1) / (32 * rw);
     const int64_t q_units = (int64_t)n_qtiles * a.Hq * a.B;
     const int64_t k_units = (int64_t)n_ktiles * a.Hkv * a.B;
@@ -565,18 +641,50 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
         a.N, n_qtiles, scale_log2, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    uint16_t* dk = static_cast<uint16_t*>(a.dk);
+    uint16_t* dv = static_cast<uint16_t*>(a.dv);
+    const int group = a.Hq / a.Hkv;
+    // two workgroups per 64-key tile, one per half of the query heads, where
+    // one workgroup per tile would leave the CUs unbalanced (at most two
+    // rounds of them, so the heaviest tile sets the time)
+    const bool split = rw == 2 && group % 2 == 0 &&
+                       (a.shape == BWD_SHAPE_K64X2H ||
+                        (a.shape == BWD_SHAPE_AUTO && k_units <= 2 * NUM_CUS));
+    if (split) {
+        const int64_t kv_rows = (int64_t)a.B * a.Hkv * a.N;
+        const int64_t quads = kv_rows * a.D / 4;
+        if (2 * k_units > 0x7fffffff || (quads + 255) / 256 > 0x7fffffff)
+            return hipErrorInvalidConfiguration;
+        float* part = nullptr;
+        e = hipMallocAsync(reinterpret_cast<void**>(&part), 4 * kv_rows * a.D * sizeof(float),
+                           stream);
+        if (e != hipSuccess) return e;
+        attn_bwd_dkdv_kernel<DT, D, RM, 2, 2, 2><<<dim3((unsigned)(2 * k_units)), 512, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, dk, dv, part, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            scale_log2, scale);
+        e = hipGetLastError();
+        if (e == hipSuccess) {
+            kv_reduce_kernel<DT, RM == ROT_QK><<<dim3((unsigned)((quads + 255) / 256)), 256, 0,
+                                                 stream>>>(part, dk, dv, a.table, kv_rows, a.N,
+                                                           a.D, scale);
+            e = hipGetLastError();
+        }
+        const hipError_t f = hipFreeAsync(part, stream);
+        return e != hipSuccess ? e : f;
+    }
     if (rw == 4)
-        attn_bwd_dkdv_kernel<DT, D, RM, 4, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
-            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
-    else if (a.shape == BWD_SHAPE_K64X2 || (a.shape != BWD_SHAPE_K64 && k_units <= 2 * NUM_CUS))
-        attn_bwd_dkdv_kernel<DT, D, RM, 2, 2><<<dim3((unsigned)k_units), 512, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
-            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+        attn_bwd_dkdv_kernel<DT, D, RM, 4, 1, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            scale_log2, scale);
+    else if (a.shape == BWD_SHAPE_K64X2 || a.shape == BWD_SHAPE_K64X2H ||
+             (a.shape != BWD_SHAPE_K64 && k_units <= 2 * NUM_CUS))
+        attn_bwd_dkdv_kernel<DT, D, RM, 2, 2, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            scale_log2, scale);
     else
-        attn_bwd_dkdv_kernel<DT, D, RM, 2, 1><<<dim3((unsigned)k_units), 256, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, static_cast<uint16_t*>(a.dk),
-            static_cast<uint16_t*>(a.dv), a.table, a.Hq, a.Hkv, a.N, n_ktiles, scale_log2, scale);
+        attn_bwd_dkdv_kernel<DT, D, RM, 2, 1, 1><<<dim3((unsigned)k_units), 256, 0, stream>>>(
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            scale_log2, scale);
     return hipGetLastError();
 }
 

@@ -267,6 +267,7 @@ int bwd_shape_from_env() {
     if (!strcmp(e, "k128")) return rac::BWD_SHAPE_K128;
     if (!strcmp(e, "k64")) return rac::BWD_SHAPE_K64;
     if (!strcmp(e, "k64x2")) return rac::BWD_SHAPE_K64X2;
+    if (!strcmp(e, "k64x2h")) return rac::BWD_SHAPE_K64X2H;
     return rac::BWD_SHAPE_AUTO;
 }
 

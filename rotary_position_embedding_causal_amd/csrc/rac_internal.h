@@ -71,7 +71,8 @@ struct BwdArgs {
 
 // dK/dV pass workgroup shapes: automatic, 128 keys (8 waves), 64 keys (4
 // waves), or 64 keys with two query groups (8 waves).
-enum { BWD_SHAPE_AUTO = 0, BWD_SHAPE_K128 = 1, BWD_SHAPE_K64 = 2, BWD_SHAPE_K64X2 = 3 };
+enum { BWD_SHAPE_AUTO = 0, BWD_SHAPE_K128 = 1, BWD_SHAPE_K64 = 2, BWD_SHAPE_K64X2 = 3,
+       BWD_SHAPE_K64X2H = 4 };
 
 // Causal attention backward (ROT_QK: RoPE fused, gradients with respect to
 // the unrotated q and k; ROT_NONE: inputs already rotated).

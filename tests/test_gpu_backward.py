@@ -31,7 +31,7 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["auto", "k128", "k64", "k64x2"])
+@pytest.fixture(params=["auto", "k128", "k64", "k64x2", "k64x2h"])
 def bwd_shape(request, monkeypatch):
     """Runs a test under each key-parallel workgroup shape (RAC_BWD_SHAPE)."""
     monkeypatch.setenv("RAC_BWD_SHAPE", request.param)

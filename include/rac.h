@@ -285,7 +285,11 @@ int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t worksp
  * (rainbus digest), method section, Algorithm 2: a query-parallel pass
  * computes dq, a key-parallel pass dk and dv, each element with one writer
  * (no atomics; deterministic). RoPE's gradient, the inverse turn R(-p), is
- * applied to dq and dk in fp32 inside the kernels. The training step of
+ * applied to dq and dk in fp32 inside the kernels' epilogues. Both passes
+ * read every query and key tile many times, so q and k are rotated once by
+ * the streaming pass into 2 * B * (Hq + Hkv) * N * D bytes of stream-ordered
+ * scratch (hipMallocAsync / hipFreeAsync on `stream`) rather than at each
+ * tile visit; the results are bit for bit those of rotating in the kernels. The training step of
  * "AttnFuse Makes RoPE a First-Class Attention Compilation Operation",
  * paragraph 3, needs this backward.
  *
@@ -298,7 +302,12 @@ int rac_auto_plan(int B, int Hq, int Hkv, int N, int D, int dtype, size_t worksp
  *   dk, dv:   summed over the Hq/Hkv query heads of each group.
  * Every pointer is a caller-owned device pointer, 16-byte aligned; lse is
  * required. Outputs must not overlap inputs or each other. Two kernels are
- * enqueued on `stream` (the dq pass first: it writes delta).
+ * enqueued on `stream` (the dq pass first: it writes delta). For GQA shapes
+ * whose key/value pass would leave the CUs unbalanced (at most two rounds
+ * of its workgroups) two workgroups share each key tile: their fp32 sums
+ * go to 16 * B * Hkv * N * D bytes of scratch taken with hipMallocAsync on
+ * `stream` and released there with hipFreeAsync after a third kernel adds
+ * them (RAC_ERR_HIP if that allocation fails).
  */
 int attn_rope_causal_bwd(const void* q, const void* k, const void* v, const void* out,
                          const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -283,6 +283,52 @@ struct Wave {
     }
 };
 
+// dS^T = P * (dP - Delta) for one 32 x 32 score block of the dQ pass (lane
+// column = query row `row`, element j = key key0 + 8(j/4) + 4hh + j%4), with
+// P = 2^(s * scale_log2 - l2) rebuilt from the forward's log-sum-exp. MASK:
+// keys after the row get P = 0 (only blocks on the diagonal need it; keys
+// past the sequence end are after every row).
+template <bool MASK>
+__device__ __forceinline__ f32x16 ds_block(const f32x16& s, const f32x16& dp, float scale_log2,
+                                           float l2, float dl, int key0, int hh, int row) {
+    f32x16 ds;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -l2));
+        if (MASK && key0 + 8 * (j >> 2) + 4 * hh + (j & 3) > row) p = 0.f;
+        ds[j] = p * (dp[j] - dl);
+    }
+    return ds;
+}
+
+// P, or (DK) dS = P * (dP - Delta), in place for one 32 x 32 score block of
+// the dK/dV pass (lane column = key `key`, element j = query row
+// r0 + 8(j/4) + 4hh + j%4 of the tile, whose base-2 L and Delta sit in
+// rl[row] and rl[BT + row]); P = 2^(s * scale_log2 - L). MASK: query rows
+// before the key, or past the sequence end (q_first + row >= N), get P = 0.
+template <bool MASK, bool DK>
+__device__ __forceinline__ void kv_p_block(f32x16& x, const f32x16& dp, const float* rl,
+                                           int q_first, int r0, int hh, int key, int N,
+                                           float scale_log2) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+        const int r = r0 + 8 * gq + 4 * hh;  // the lane's 4 query rows in the tile
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(rl + r);
+        f32x4 dq4;
+        if (DK) dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * gq + jj;
+            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, -lq[jj]));
+            if (MASK) {
+                const int qrow = q_first + 8 * gq + 4 * hh + jj;
+                if (qrow < key || qrow >= N) pj = 0.f;
+            }
+            x[j] = DK ? pj * (dp[j] - dq4[jj]) : pj;  // dS or P
+        }
+    }
+}
+
 // 1-D work-unit index, XCD-aware order (the hardware deals workgroup ids
 // round-robin over 8 XCDs; consecutive units on one XCD share a head), then
 // (outer, tile) with the heaviest tile first.
@@ -305,7 +351,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     float* __restrict__ delta, const float* __restrict__ table, int Hq, int Hkv, int N,
     int n_qtiles, float scale_log2, float scale) {
-    constexpr bool ROPE = RM == ROT_QK;
+    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 4> S;
     constexpr int TILE = BT * D;
@@ -375,21 +422,178 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
             // S^T and dP^T for keys k0 + 32kb .. +31 (lane column = query row)
             f32x16 s = W::score(Ks, 32 * kb, qf, n, hh);
             const f32x16 dp = W::score(Vs, 32 * kb, dof, n, hh);
-            f32x16 ds;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = k0 + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -l2));
-                if (diag && key > row) p = 0.f;
-                ds[j] = p * (dp[j] - dl);
-            }
+            // only tiles on the diagonal mask (a wave-uniform branch)
+            const f32x16 ds = diag ? ds_block<true>(s, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row)
+                                   : ds_block<false>(s, dp, scale_log2, l2, dl, 0, 0, 0);
             u32x4 y[2];
             W::pack(ds, y);
             W::pv(acc, Ks, 32 * kb, y, lane);
         }
     }
     if (row < N)
-        W::write(acc, scale, dq + (qhead + row) * D, ROPE ? table + (int64_t)row * D : nullptr, hh);
+        W::write(acc, scale, dq + (qhead + row) * D, ROPE_OUT ? table + (int64_t)row * D : nullptr,
+                 hh);
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass, balanced: one 8-wave workgroup per (b, query head, pair p of
+// 128-row query tiles), used where one workgroup per tile would be resident
+// on the chip all at once, so that its heaviest tile would set the time. The
+// heavy tile T-1-p needs nh key tiles and the light tile p needs nl (an odd
+// T's middle tile has no partner: nl = 0). Half A (waves 0-3) takes the
+// heavy rows over key tiles [0, X), X = ceil((nh + nl) / 2); half B (waves
+// 4-7) the light rows over [0, nl), then the heavy rows over [X, nh), so
+// neither half takes more than X steps. Each half streams its own key tiles
+// through its own LDS buffers. At the end half B hands its fp32 sums of the
+// heavy rows to half A through LDS; A adds them to its own (A + B, a fixed
+// order: deterministic) and writes those rows, B writes the light rows.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int RM>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
+    float* __restrict__ delta, const float* __restrict__ table, int Hq, int Hkv, int N,
+    int n_qtiles, float scale_log2, float scale) {
+    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
+    typedef Wave<DT, D> W;
+    typedef Streamer<DT, D, ROPE, 4> S;
+    constexpr int TILE = BT * D;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[8 * TILE];  // per half: K0 V0 K1 V1
+
+    const int tid = threadIdx.x;
+    const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave_wg >> 2;  // 0: A, 1: B
+    const int wave = wave_wg & 3;   // wave inside its half
+    const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    int bh, slot;
+    decode((n_qtiles + 1) / 2, bh, slot);
+    const int hv = n_qtiles - 1 - slot;     // the heavy tile
+    const int lt = slot < hv ? slot : -1;   // the light tile, if any
+    const int b = bh / Hq, h = bh % Hq;
+    const int g = h / (Hq / Hkv);
+    const int64_t qhead = ((int64_t)b * Hq + h) * N;
+    const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
+    const uint16_t* kbase = k + kvhead * D;
+    const uint16_t* vbase = v + kvhead * D;
+    const int nh = (min(hv * BR + BR, N) - 1) / BT + 1;
+    const int nl = lt >= 0 ? (min(lt * BR + BR, N) - 1) / BT + 1 : 0;
+    const int X = (nh + nl + 1) / 2;
+    const bool b_heavy = nh > X;  // half B also takes heavy key tiles
+    uint16_t* hbuf = smem + half * 4 * TILE;
+
+    // the key tile this half reads at step s, or -1 for none
+    auto tile_at = [&](int s) -> int {
+        if (half == 0 || s < nl) return s;
+        const int t = X + (s - nl);
+        return t < nh ? t : -1;
+    };
+
+    // the wave's stationary rows, their Delta and L, and its dQ sums
+    typename W::vec8 qf[W::QCH], dof[W::QCH];
+    float dl = 0.f, l2 = 0.f;
+    int qw0 = 0, row = 0, wave_tiles = 0;
+    f32x16 acc[W::DBLK];
+    auto setup = [&](int qt, bool write_delta) {
+        qw0 = qt * BR + 32 * wave;
+        row = qw0 + n;
+        wave_tiles = qw0 < N ? min(qw0 + 31, N - 1) / BT + 1 : 0;
+        W::load_rows(qf, q + qhead * D, ROPE ? table : nullptr, qw0, N, n, hh);
+        W::load_rows(dof, dout + qhead * D, nullptr, qw0, N, n, hh);
+        dl = 0.f;
+        l2 = 0.f;
+        if (row < N) {
+            const uint16_t* orow = out + (qhead + row) * D;
+#pragma unroll
+            for (int c = 0; c < W::QCH; ++c) {
+                const u32x4 o = *reinterpret_cast<const u32x4*>(orow + 16 * c + 8 * hh);
+                const u32x4 d = __builtin_bit_cast(u32x4, dof[c]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    dl += W::F::lo(o[t]) * W::F::lo(d[t]) + W::F::hi(o[t]) * W::F::hi(d[t]);
+            }
+            l2 = lse[qhead + row] * LOG2E;
+        }
+        dl += __shfl_xor(dl, 32);
+        if (write_delta && row < N && hh == 0) delta[qhead + row] = dl;
+#pragma unroll
+        for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
+    };
+    // B starts on the light rows, or with no light tile on the heavy rows
+    // (whose Delta A writes)
+    setup(half == 1 && nl > 0 ? lt : hv, half == 0 || nl > 0);
+
+    S st;
+    auto rt = [&](int t) { return rows_rsrc(table, ROPE ? D : 0, t, N); };
+    {
+        const int t0 = tile_at(0);
+        if (t0 >= 0)
+            st.issue(hbuf, hbuf + TILE, rows_rsrc(kbase, D, t0, N), rows_rsrc(vbase, D, t0, N),
+                     rt(t0), wave, lane);
+    }
+    for (int s = 0; s < X; ++s) {
+        const int t = tile_at(s);
+        uint16_t* Ks = hbuf + (s & 1) * 2 * TILE;
+        const uint16_t* Vs = Ks + TILE;
+        wait_all_loads();
+        if (t >= 0) st.finish(Ks, nullptr, false, wave, lane);
+        __syncthreads();  // step s's tiles complete; the other buffers are no longer read
+        const int tn = s + 1 < X ? tile_at(s + 1) : -1;
+        if (tn >= 0) {
+            uint16_t* nk = hbuf + ((s + 1) & 1) * 2 * TILE;
+            st.issue(nk, nk + TILE, rows_rsrc(kbase, D, tn, N), rows_rsrc(vbase, D, tn, N),
+                     rt(tn), wave, lane);
+        }
+        if (half == 1 && s == nl && nl > 0 && b_heavy) {
+            // the light rows are complete: write them, then take the heavy rows
+            if (row < N)
+                W::write(acc, scale, dq + (qhead + row) * D,
+                         ROPE_OUT ? table + (int64_t)row * D : nullptr, hh);
+            setup(hv, false);
+        }
+        if (t < 0 || t >= wave_tiles) continue;
+        const int k0 = t * BT;
+        const bool diag = k0 + BT - 1 > qw0;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // S^T and dP^T for keys k0 + 32kb .. +31 (lane column = query row)
+            const f32x16 sc = W::score(Ks, 32 * kb, qf, n, hh);
+            const f32x16 dp = W::score(Vs, 32 * kb, dof, n, hh);
+            // only tiles on the diagonal mask (a wave-uniform branch)
+            const f32x16 ds = diag
+                ? ds_block<true>(sc, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row)
+                : ds_block<false>(sc, dp, scale_log2, l2, dl, 0, 0, 0);
+            u32x4 y[2];
+            W::pack(ds, y);
+            W::pv(acc, Ks, 32 * kb, y, lane);
+        }
+    }
+    __syncthreads();  // every wave is done with the stream buffers
+    constexpr int SLOTS = 16 * W::DBLK;
+    float* red = reinterpret_cast<float*>(smem) + (wave * SLOTS) * 64 + lane;
+    if (b_heavy && half == 1) {
+#pragma unroll
+        for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) red[(16 * i + j) * 64] = acc[i][j];
+    }
+    __syncthreads();
+    if (half == 0) {
+        if (b_heavy) {
+#pragma unroll
+            for (int i = 0; i < W::DBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[i][j] += red[(16 * i + j) * 64];
+        }
+        if (row < N)
+            W::write(acc, scale, dq + (qhead + row) * D,
+                     ROPE_OUT ? table + (int64_t)row * D : nullptr, hh);
+    } else if (!b_heavy && nl > 0 && row < N) {
+        // half B stayed on the light rows
+        W::write(acc, scale, dq + (qhead + row) * D, ROPE_OUT ? table + (int64_t)row * D : nullptr,
+                 hh);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +626,8 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, float* __restrict__ part, const float* __restrict__ table, int Hq,
     int Hkv, int N, int n_ktiles, float scale_log2, float scale) {
-    constexpr bool ROPE = RM == ROT_QK;
+    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
     constexpr int KW = 32 * RW;  // keys per workgroup
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 2 * RW> S;
@@ -500,28 +705,19 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
             const int q0 = tq * BT;
             if (kw0 >= N) continue;           // the wave has no keys
             if (q0 + BT - 1 < kw0) continue;  // every query of the tile precedes the wave's keys
-            const bool diag = q0 < kw0 + 31;
+            // masking only where the tile crosses the wave's keys or the
+            // sequence end (a wave-uniform branch)
+            const bool mask = q0 < kw0 + 31 || q0 + BT > N;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 // S (and for dK, dP) for queries q0 + 32qb .. +31 (lane column = key)
                 f32x16 x = W::score(Qs, 32 * qb, kf, n, hh);
                 f32x16 dp;
                 if (DK) dp = W::score(dOs, 32 * qb, vf, n, hh);
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int r = 32 * qb + 8 * gq + 4 * hh;  // the lane's 4 query rows in the tile
-                    const f32x4 lq = *reinterpret_cast<const f32x4*>(rl + r);
-                    f32x4 dq4;
-                    if (DK) dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int j = 4 * gq + jj;
-                        const int qrow = q0 + r + jj;
-                        float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, -lq[jj]));
-                        if ((diag && qrow < key) || qrow >= N) pj = 0.f;
-                        x[j] = DK ? pj * (dp[j] - dq4[jj]) : pj;  // dS or P
-                    }
-                }
+                if (mask)
+                    kv_p_block<true, DK>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N, scale_log2);
+                else
+                    kv_p_block<false, DK>(x, dp, rl, 0, 32 * qb, hh, 0, 0, scale_log2);
                 u32x4 y[2];
                 W::pack(x, y);
                 W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
@@ -553,7 +749,7 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
                              hh);
             } else if (DK) {
                 W::write(acc, scale, dk + (kvhead + key) * D,
-                         ROPE ? table + (int64_t)key * D : nullptr, hh);
+                         ROPE_OUT ? table + (int64_t)key * D : nullptr, hh);
             } else {
                 W::write(acc, 1.f, dv + (kvhead + key) * D, nullptr, hh);
             }
@@ -635,10 +831,19 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     const uint16_t* out = static_cast<const uint16_t*>(a.out);
     const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-    // the dQ pass writes Delta, which the dK/dV pass reads: same stream, in order
-    attn_bwd_dq_kernel<DT, D, RM><<<dim3((unsigned)q_units), 256, 0, stream>>>(
-        q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq, a.Hkv,
-        a.N, n_qtiles, scale_log2, scale);
+    // the dQ pass writes Delta, which the dK/dV pass reads: same stream, in order.
+    // Where one workgroup per query tile (two per CU) would all be resident at
+    // once, the heaviest tile would set the time: pair heavy and light tiles.
+    if (n_qtiles >= 2 && a.dq_shape != BWD_DQ_TILE &&
+        (a.dq_shape == BWD_DQ_PAIR || q_units <= 2 * NUM_CUS))
+        attn_bwd_dq_pair_kernel<DT, D, RM>
+            <<<dim3((unsigned)((n_qtiles + 1) / 2 * (int64_t)a.Hq * a.B)), 512, 0, stream>>>(
+                q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq,
+                a.Hkv, a.N, n_qtiles, scale_log2, scale);
+    else
+        attn_bwd_dq_kernel<DT, D, RM><<<dim3((unsigned)q_units), 256, 0, stream>>>(
+            q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq,
+            a.Hkv, a.N, n_qtiles, scale_log2, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* dk = static_cast<uint16_t*>(a.dk);
@@ -664,7 +869,7 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
             scale_log2, scale);
         e = hipGetLastError();
         if (e == hipSuccess) {
-            kv_reduce_kernel<DT, RM == ROT_QK><<<dim3((unsigned)((quads + 255) / 256)), 256, 0,
+            kv_reduce_kernel<DT, RM == ROT_QK || RM == ROT_QK_OUT><<<dim3((unsigned)((quads + 255) / 256)), 256, 0,
                                                  stream>>>(part, dk, dv, a.table, kv_rows, a.N,
                                                            a.D, scale);
             e = hipGetLastError();
@@ -697,10 +902,12 @@ static hipError_t launch_dt(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream) {
     if (a.dtype == DT_BF16)
-        return rot == ROT_QK ? bwd::launch_dt<DT_BF16, ROT_QK>(a, stream)
-                             : bwd::launch_dt<DT_BF16, ROT_NONE>(a, stream);
-    return rot == ROT_QK ? bwd::launch_dt<DT_FP16, ROT_QK>(a, stream)
-                         : bwd::launch_dt<DT_FP16, ROT_NONE>(a, stream);
+        return rot == ROT_QK       ? bwd::launch_dt<DT_BF16, ROT_QK>(a, stream)
+               : rot == ROT_QK_OUT ? bwd::launch_dt<DT_BF16, ROT_QK_OUT>(a, stream)
+                                   : bwd::launch_dt<DT_BF16, ROT_NONE>(a, stream);
+    return rot == ROT_QK       ? bwd::launch_dt<DT_FP16, ROT_QK>(a, stream)
+           : rot == ROT_QK_OUT ? bwd::launch_dt<DT_FP16, ROT_QK_OUT>(a, stream)
+                               : bwd::launch_dt<DT_FP16, ROT_NONE>(a, stream);
 }
 
 }  // namespace rac

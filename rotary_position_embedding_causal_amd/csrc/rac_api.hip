@@ -271,6 +271,22 @@ int bwd_shape_from_env() {
     return rac::BWD_SHAPE_AUTO;
 }
 
+// RAC_BWD_ROT=kernel makes the fused backward rotate q and k inside its
+// kernels instead of once through the streaming pass (tests, timing).
+bool bwd_rotation_in_kernel() {
+    const char* e = getenv("RAC_BWD_ROT");
+    return e && !strcmp(e, "kernel");
+}
+
+// RAC_BWD_DQ=tile|pair forces the dQ pass's launch shape (default: by size).
+int bwd_dq_from_env() {
+    const char* e = getenv("RAC_BWD_DQ");
+    if (!e) return rac::BWD_DQ_AUTO;
+    if (!strcmp(e, "tile")) return rac::BWD_DQ_TILE;
+    if (!strcmp(e, "pair")) return rac::BWD_DQ_PAIR;
+    return rac::BWD_DQ_AUTO;
+}
+
 // ---- the path dispatcher ------------------------------------------------------
 //
 // All three paths give bit-identical results (they hand the same rotated
@@ -363,10 +379,39 @@ int attn_bwd_common(const void* q, const void* k, const void* v, const void* out
     if (rot == rac::ROT_QK && (rc = check_base(rope_base)) != RAC_OK) return rc;
     if (empty) return ok();
     rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype,
-                   bwd_shape_from_env()};
+                   bwd_shape_from_env(), bwd_dq_from_env()};
     if ((rc = check_bwd_ptrs(a)) != RAC_OK) return rc;
     if (rot == rac::ROT_QK && (rc = get_table(D, rope_base, N, &a.table)) != RAC_OK) return rc;
-    return hip_status(rac::launch_attn_bwd(a, rot, static_cast<hipStream_t>(stream)), what);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (rot != rac::ROT_QK || bwd_rotation_in_kernel())
+        return hip_status(rac::launch_attn_bwd(a, rot, st), what);
+    // Both passes read every query and key tile many times (each key tile once
+    // per query tile that sees it, and the reverse), so the rotated operands
+    // are formed once by the streaming pass into stream-ordered scratch; the
+    // kernels then read them as they are and turn dq and dk back by R(-p) in
+    // their epilogues, exactly as when rotating in the kernel (the same
+    // operands, the same arithmetic).
+    const size_t qbytes = (size_t)B * Hq * N * D * 2, kbytes = (size_t)B * Hkv * N * D * 2;
+    const size_t q16 = (qbytes + 255) & ~(size_t)255;
+    char* scratch = nullptr;
+    if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)  // the pass's grid: rotate in the kernel
+        return hip_status(rac::launch_attn_bwd(a, rot, st), what);
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), q16 + kbytes, st);
+    if (e != hipSuccess) return hip_status(e, "attn_rope_causal_bwd scratch allocation");
+    // backward launches leave the kernel timer armed for the next forward or pass call
+    const hipEvent_t timer_start = g_timer_start, timer_stop = g_timer_stop;
+    g_timer_start = g_timer_stop = nullptr;
+    e = rac::launch_rope_prerotate(q, k, scratch, scratch + q16, a.table, B, Hq, Hkv, N, D, dtype,
+                                   st);
+    g_timer_start = timer_start;
+    g_timer_stop = timer_stop;
+    if (e == hipSuccess) {
+        a.q = scratch;
+        a.k = scratch + q16;
+        e = rac::launch_attn_bwd(a, rac::ROT_QK_OUT, st);
+    }
+    const hipError_t f = hipFreeAsync(scratch, st);
+    return hip_status(e != hipSuccess ? e : f, what);
 }
 
 }  // namespace

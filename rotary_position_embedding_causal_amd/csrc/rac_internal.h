@@ -46,6 +46,9 @@ struct AttnArgs {
 // Rotation applied inside the attention kernel: none (inputs already
 // rotated), Q and K (the fused path), or Q only (K rotated beforehand).
 enum { ROT_NONE = 0, ROT_QK = 1, ROT_Q = 2, ROT_QK_HALF = 3 };
+// Backward only: q and k arrive already rotated; dq and dk are turned back
+// by R(-p) in the epilogues (the gradients with respect to the unrotated q, k).
+enum { ROT_QK_OUT = 8 };
 // Added to a rotation mode: the ALiBi distance penalty on the scores.
 enum { MOD_ALIBI = 4 };
 
@@ -66,16 +69,20 @@ struct BwdArgs {
     const float* table;  // cos/sin table (ROT_QK only)
     int B, Hq, Hkv, N, D;
     int dtype;
-    int shape = 0;       // BWD_SHAPE_*
+    int shape = 0;       // BWD_SHAPE_* (the dK/dV pass)
+    int dq_shape = 0;    // BWD_DQ_* (the dQ pass)
 };
 
 // dK/dV pass workgroup shapes: automatic, 128 keys (8 waves), 64 keys (4
 // waves), or 64 keys with two query groups (8 waves).
 enum { BWD_SHAPE_AUTO = 0, BWD_SHAPE_K128 = 1, BWD_SHAPE_K64 = 2, BWD_SHAPE_K64X2 = 3,
        BWD_SHAPE_K64X2H = 4 };
+enum { BWD_DQ_AUTO = 0, BWD_DQ_TILE = 1, BWD_DQ_PAIR = 2 };
 
 // Causal attention backward (ROT_QK: RoPE fused, gradients with respect to
-// the unrotated q and k; ROT_NONE: inputs already rotated).
+// the unrotated q and k; ROT_QK_OUT: q and k already rotated, gradients with
+// respect to the unrotated ones; ROT_NONE: inputs already rotated, gradients
+// with respect to them).
 hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream);
 
 // q_rot = RoPE(q), k_rot = RoPE(k).

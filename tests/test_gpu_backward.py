@@ -31,10 +31,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["auto", "k128", "k64", "k64x2", "k64x2h"])
+@pytest.fixture(params=["auto", "k128", "k64", "k64x2", "k64x2h", "dqtile"])
 def bwd_shape(request, monkeypatch):
-    """Runs a test under each key-parallel workgroup shape (RAC_BWD_SHAPE)."""
-    monkeypatch.setenv("RAC_BWD_SHAPE", request.param)
+    """Runs a test under each key-parallel workgroup shape (RAC_BWD_SHAPE),
+    and once with the dQ pass's one-tile-per-workgroup launch (RAC_BWD_DQ;
+    small problems otherwise take its paired launch)."""
+    if request.param == "dqtile":
+        monkeypatch.setenv("RAC_BWD_DQ", "tile")
+    else:
+        monkeypatch.setenv("RAC_BWD_SHAPE", request.param)
     return request.param
 
 
@@ -76,6 +81,22 @@ def test_backward_matches_oracle(shape, path, bwd_shape):
         for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
             assert_grad(to_f64(got), ref, "%s %s vs %s oracle" % (path, name, variant))
         assert_grad(delta.cpu().double().numpy(), rdelta, "%s delta" % path)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+def test_fused_backward_rotation_once_or_per_tile_agree(shape, bwd_shape, monkeypatch):
+    """The fused backward rotates q and k once through the streaming pass
+    (default) or inside its kernels at every tile visit (RAC_BWD_ROT=kernel):
+    the same rotated operands reach the same arithmetic, so every output is
+    bit for bit the same."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    _, (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (403, N, D))
+    once = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    monkeypatch.setenv("RAC_BWD_ROT", "kernel")
+    per_tile = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    for a, b, name in zip(once, per_tile, ("dq", "dk", "dv", "delta")):
+        assert torch.equal(a, b), name
 
 
 @pytest.mark.parametrize("shape", SHAPES[:4], ids=_id)

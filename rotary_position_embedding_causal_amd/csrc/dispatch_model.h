@@ -34,37 +34,37 @@ namespace rac_model {
 constexpr double MFMA_PEAK = 2516.6e12;  // FLOP/s, dense bf16/fp16
 constexpr double HBM_BW = 8.0e12;        // B/s
 
-constexpr double D64_MHA_ETA_ATTN = 0.317331;
-constexpr double D64_MHA_TILE_US_ATTN = 1.83696;
-constexpr double D64_MHA_ETA_FUSED = 0.259388;
-constexpr double D64_MHA_TILE_US_FUSED = 2.16267;
-constexpr double D64_MHA_ETA_Q = 0.314605;
-constexpr double D64_MHA_TILE_US_Q = 1.8855;
+constexpr double D64_MHA_ETA_ATTN = 0.31683;
+constexpr double D64_MHA_TILE_US_ATTN = 1.83122;
+constexpr double D64_MHA_ETA_FUSED = 0.257395;
+constexpr double D64_MHA_TILE_US_FUSED = 2.15604;
+constexpr double D64_MHA_ETA_Q = 0.313765;
+constexpr double D64_MHA_TILE_US_Q = 1.87799;
 
-constexpr double D128_MHA_ETA_ATTN = 0.358194;
-constexpr double D128_MHA_TILE_US_ATTN = 2.96008;
-constexpr double D128_MHA_ETA_FUSED = 0.269982;
-constexpr double D128_MHA_TILE_US_FUSED = 3.68891;
-constexpr double D128_MHA_ETA_Q = 0.350423;
-constexpr double D128_MHA_TILE_US_Q = 3.02404;
+constexpr double D128_MHA_ETA_ATTN = 0.359034;
+constexpr double D128_MHA_TILE_US_ATTN = 2.93947;
+constexpr double D128_MHA_ETA_FUSED = 0.268154;
+constexpr double D128_MHA_TILE_US_FUSED = 3.69692;
+constexpr double D128_MHA_ETA_Q = 0.35094;
+constexpr double D128_MHA_TILE_US_Q = 3.00882;
 
-constexpr double D64_GQA_ETA_ATTN = 0.336585;
-constexpr double D64_GQA_TILE_US_ATTN = 2.08379;
-constexpr double D64_GQA_ETA_FUSED = 0.291205;
-constexpr double D64_GQA_TILE_US_FUSED = 2.3847;
-constexpr double D64_GQA_ETA_Q = 0.332287;
-constexpr double D64_GQA_TILE_US_Q = 2.12463;
+constexpr double D64_GQA_ETA_ATTN = 0.337758;
+constexpr double D64_GQA_TILE_US_ATTN = 2.06035;
+constexpr double D64_GQA_ETA_FUSED = 0.288994;
+constexpr double D64_GQA_TILE_US_FUSED = 2.36427;
+constexpr double D64_GQA_ETA_Q = 0.334648;
+constexpr double D64_GQA_TILE_US_Q = 2.088;
 
-constexpr double D128_GQA_ETA_ATTN = 0.419617;
-constexpr double D128_GQA_TILE_US_ATTN = 3.05084;
-constexpr double D128_GQA_ETA_FUSED = 0.345648;
-constexpr double D128_GQA_TILE_US_FUSED = 3.7151;
-constexpr double D128_GQA_ETA_Q = 0.412102;
-constexpr double D128_GQA_TILE_US_Q = 3.09343;
+constexpr double D128_GQA_ETA_ATTN = 0.419355;
+constexpr double D128_GQA_TILE_US_ATTN = 3.03572;
+constexpr double D128_GQA_ETA_FUSED = 0.343728;
+constexpr double D128_GQA_TILE_US_FUSED = 3.71924;
+constexpr double D128_GQA_ETA_Q = 0.413199;
+constexpr double D128_GQA_TILE_US_Q = 3.06474;
 
-constexpr double ETA_BW = 0.839421;
-constexpr double T0_US = 3.30451;
-constexpr double T_GAP_US = 0;
+constexpr double ETA_BW = 0.839185;
+constexpr double T0_US = 3.35922;
+constexpr double T_GAP_US = 0.120002;
 
 struct Kernel {
     double eta, tile_us;

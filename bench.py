@@ -625,8 +625,9 @@ def crossover(torch, rac, inputs, dev, ev, repeats=3, reps=11):
              "alpha_underfilled": c64["alpha_qk_underfilled"], "t0_us": fit["t0_us"],
              "t_gap_us": fit["t_gap_us"], "fit": fit,
              "dispatcher_constants": header,
-             "form": "T_k = max(F/(eta_k P), t_tile_k N/128) per kernel; alpha = eta_attn/eta_fused"
-                     " - 1; pre = t0 + 4B(Hq+Hkv)ND/(eta_bw BW) + T_attn; N* where T_fused = pre"}
+             "form": "T_k = max(F/(eta_k P), t_pro_k + t_tile_k N/128) per kernel; alpha = "
+                     "eta_attn/eta_fused - 1; pre = t0 + 4B(Hq+Hkv)ND/(eta_bw BW) + T_attn; N* "
+                     "where T_fused = pre"}
     return {"n_star": head["n_star_kernels"]["n_star"],
             "level": "kernels (the fused kernel vs the pass plus plain attention)",
             "bracket": head["n_star_kernels"]["bracket"],

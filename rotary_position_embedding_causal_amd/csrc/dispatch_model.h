@@ -10,15 +10,15 @@
 // memory-bandwidth cost, in-kernel rotation a compute-and-tiling cost; per
 // paragraph 5 the choice is measured per architecture and shape. In
 // microseconds, with F = 2 B Hq N^2 D, P = 2516.6 TFLOP/s, BW = 8 TB/s:
-//   T_k     = max(F / (ETA_k P), TILE_US_k N / 128)  for the plain attention
-//             kernel (k = ATTN), the one rotating Q and K tiles (FUSED) and
-//             the one rotating Q rows (Q); the second term is an under-filled
-//             chip, where one workgroup's N / 128 key tiles set the time
+//   T_k     = max(F / (ETA_k P), TPRO_US_k + TILE_US_k N / 128)  for the plain
+//             attention kernel (k = ATTN), the one rotating Q and K tiles
+//             (FUSED) and the one rotating Q rows (Q); the second term is an
+//             under-filled chip: one workgroup's prologue and N / 128 key tiles
 //   fused   = T_FUSED
 //   prerot  = T0_US + 4 B (Hq + Hkv) N D / (ETA_BW BW) + T_ATTN + T_GAP_US
 //   split   = T0_US + 4 B Hkv N D / (ETA_BW BW) + T_Q + T_GAP_US
 // Per class of shape (head dim 64 or 128; MHA, or GQA when Hq / Hkv >= 2) the
-// six kernel constants, and the three pass/launch constants shared by all,
+// nine kernel constants, and the three pass/launch constants shared by all,
 // are least-squares fits to kernel times measured on MI355X back to back
 // (steady clocks) over the crossover families:
 //   MHA D=64 fp16, B=1 H=16, N = 1024, 2048, 4096, 6144, 8192, 16384, 32768
@@ -34,48 +34,63 @@ namespace rac_model {
 constexpr double MFMA_PEAK = 2516.6e12;  // FLOP/s, dense bf16/fp16
 constexpr double HBM_BW = 8.0e12;        // B/s
 
-constexpr double D64_MHA_ETA_ATTN = 0.31683;
-constexpr double D64_MHA_TILE_US_ATTN = 1.83122;
-constexpr double D64_MHA_ETA_FUSED = 0.257395;
-constexpr double D64_MHA_TILE_US_FUSED = 2.15604;
-constexpr double D64_MHA_ETA_Q = 0.313765;
-constexpr double D64_MHA_TILE_US_Q = 1.87799;
+constexpr double D64_MHA_ETA_ATTN = 0.327305;
+constexpr double D64_MHA_TPRO_US_ATTN = 8.75;
+constexpr double D64_MHA_TILE_US_ATTN = 1.21982;
+constexpr double D64_MHA_ETA_FUSED = 0.261231;
+constexpr double D64_MHA_TPRO_US_FUSED = 7.65;
+constexpr double D64_MHA_TILE_US_FUSED = 1.61918;
+constexpr double D64_MHA_ETA_Q = 0.321517;
+constexpr double D64_MHA_TPRO_US_Q = 8.4;
+constexpr double D64_MHA_TILE_US_Q = 1.28665;
 
-constexpr double D128_MHA_ETA_ATTN = 0.359034;
-constexpr double D128_MHA_TILE_US_ATTN = 2.93947;
-constexpr double D128_MHA_ETA_FUSED = 0.268154;
-constexpr double D128_MHA_TILE_US_FUSED = 3.69692;
-constexpr double D128_MHA_ETA_Q = 0.35094;
-constexpr double D128_MHA_TILE_US_Q = 3.00882;
+constexpr double D128_MHA_ETA_ATTN = 0.366479;
+constexpr double D128_MHA_TPRO_US_ATTN = 7.25;
+constexpr double D128_MHA_TILE_US_ATTN = 2.23296;
+constexpr double D128_MHA_ETA_FUSED = 0.273001;
+constexpr double D128_MHA_TPRO_US_FUSED = 5.5;
+constexpr double D128_MHA_TILE_US_FUSED = 3.15368;
+constexpr double D128_MHA_ETA_Q = 0.356813;
+constexpr double D128_MHA_TPRO_US_Q = 9.6;
+constexpr double D128_MHA_TILE_US_Q = 2.09965;
 
-constexpr double D64_GQA_ETA_ATTN = 0.337758;
-constexpr double D64_GQA_TILE_US_ATTN = 2.06035;
-constexpr double D64_GQA_ETA_FUSED = 0.288994;
-constexpr double D64_GQA_TILE_US_FUSED = 2.36427;
-constexpr double D64_GQA_ETA_Q = 0.334648;
-constexpr double D64_GQA_TILE_US_Q = 2.088;
+constexpr double D64_GQA_ETA_ATTN = 0.340929;
+constexpr double D64_GQA_TPRO_US_ATTN = 8.3;
+constexpr double D64_GQA_TILE_US_ATTN = 1.2929;
+constexpr double D64_GQA_ETA_FUSED = 0.29406;
+constexpr double D64_GQA_TPRO_US_FUSED = 8.25;
+constexpr double D64_GQA_TILE_US_FUSED = 1.61937;
+constexpr double D64_GQA_ETA_Q = 0.335883;
+constexpr double D64_GQA_TPRO_US_Q = 8.85;
+constexpr double D64_GQA_TILE_US_Q = 1.27393;
 
-constexpr double D128_GQA_ETA_ATTN = 0.419355;
-constexpr double D128_GQA_TILE_US_ATTN = 3.03572;
-constexpr double D128_GQA_ETA_FUSED = 0.343728;
-constexpr double D128_GQA_TILE_US_FUSED = 3.71924;
-constexpr double D128_GQA_ETA_Q = 0.413199;
-constexpr double D128_GQA_TILE_US_Q = 3.06474;
+constexpr double D128_GQA_ETA_ATTN = 0.430263;
+constexpr double D128_GQA_TPRO_US_ATTN = 9.55;
+constexpr double D128_GQA_TILE_US_ATTN = 2.07093;
+constexpr double D128_GQA_ETA_FUSED = 0.349817;
+constexpr double D128_GQA_TPRO_US_FUSED = 8.5;
+constexpr double D128_GQA_TILE_US_FUSED = 2.85299;
+constexpr double D128_GQA_ETA_Q = 0.424949;
+constexpr double D128_GQA_TPRO_US_Q = 9.7;
+constexpr double D128_GQA_TILE_US_Q = 2.08077;
 
-constexpr double ETA_BW = 0.839185;
-constexpr double T0_US = 3.35922;
-constexpr double T_GAP_US = 0.120002;
+constexpr double ETA_BW = 0.839877;
+constexpr double T0_US = 3.32335;
+constexpr double T_GAP_US = 0;
 
 struct Kernel {
-    double eta, tile_us;
+    double eta, tpro_us, tile_us;
 };
 struct Class {
     Kernel attn, fused, q;
 };
 
-#define RAC_MODEL_CLASS(P) \
-    Class { {P##_ETA_ATTN, P##_TILE_US_ATTN}, {P##_ETA_FUSED, P##_TILE_US_FUSED}, \
-            {P##_ETA_Q, P##_TILE_US_Q} }
+#define RAC_MODEL_CLASS(P)                                                          \
+    Class {                                                                         \
+        {P##_ETA_ATTN, P##_TPRO_US_ATTN, P##_TILE_US_ATTN},                         \
+            {P##_ETA_FUSED, P##_TPRO_US_FUSED, P##_TILE_US_FUSED},                  \
+            {P##_ETA_Q, P##_TPRO_US_Q, P##_TILE_US_Q}                               \
+    }
 
 inline Class shape_class(int D, int Hq, int Hkv) {
     const bool gqa = Hq / Hkv >= 2;
@@ -87,7 +102,7 @@ inline Class shape_class(int D, int Hq, int Hkv) {
 
 inline double kernel_us(const Kernel& k, double flops, double n) {
     const double thr = flops / (k.eta * MFMA_PEAK) * 1e6;
-    const double lat = k.tile_us * n / 128.0;
+    const double lat = k.tpro_us + k.tile_us * n / 128.0;
     return thr > lat ? thr : lat;
 }
 

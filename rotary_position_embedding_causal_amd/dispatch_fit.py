@@ -9,15 +9,16 @@ be measured per architecture and shape. The AttnFuse abstract (arxivdaily
 2609.13612) says a crossover derived that way matches measurement. The pages
 print no formula; the reading written out here is the plain one:
 
-  kernel      T = max(F / (eta * P),  t_tile * N / 128)
-              F = 2 B Hq N^2 D (causal), P = the dense MFMA peak; the second
-              term is the under-filled regime, where too few workgroups run
-              to fill the chip and time grows with one workgroup's N / 128
-              key tiles instead of with the total work. Each attention
-              kernel has its own (eta, t_tile): plain (T_attn), rotating Q
-              and K tiles (T_fused), rotating Q rows only (T_q); the
-              rotation's cost is alpha = eta_attn / eta_fused - 1 when the
-              chip is full and t_tile_fused / t_tile_attn - 1 when it is not
+  kernel      T = max(F / (eta * P),  t_pro + t_tile * N / 128)
+              F = 2 B Hq N^2 D (causal), P = the dense MFMA peak. The first
+              term is a full chip; the second an under-filled one, where too
+              few workgroups run to fill it and time is one workgroup's
+              prologue (Q rows, first tiles) plus its N / 128 key tiles.
+              Each attention kernel has its own (eta, t_pro, t_tile): plain
+              (T_attn), rotating Q and K tiles (T_fused), rotating Q rows
+              only (T_q); the rotation's cost is alpha = eta_attn /
+              eta_fused - 1 on a full chip and t_tile_fused / t_tile_attn
+              - 1 per key tile on an under-filled one
   pass        T_pass  = t0 + bytes / (eta_bw * BW)    (BW = 8 TB/s HBM peak)
               bytes = 2 x (the rotated heads) x B N D x 2 bytes, read + write
   fused       T_fused
@@ -46,7 +47,7 @@ MFMA_PEAK = 2516.6e12   # MI355X dense bf16/fp16, FLOP/s (published)
 HBM_BW = 8.0e12         # MI355X HBM3E, B/s (published)
 CLASSES = ("d64_mha", "d128_mha", "d64_gqa", "d128_gqa")
 KERNELS = ("attn", "fused", "q")
-CLASS_PARAMS = tuple("%s_%s" % (a, k) for k in KERNELS for a in ("eta", "tile_us"))
+CLASS_PARAMS = tuple("%s_%s" % (a, k) for k in KERNELS for a in ("eta", "tpro_us", "tile_us"))
 GLOBAL_PARAMS = ("eta_bw", "t0_us", "t_gap_us")
 HEADER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "dispatch_model.h")
 
@@ -77,7 +78,8 @@ def pass_bytes(B, heads, N, D) -> float:
 def kernel_us(c: dict, kernel: str, B, Hq, N, D) -> float:
     """Modelled time of one attention kernel ("attn", "fused" or "q")."""
     thr = flops(B, Hq, N, D) / (c["eta_" + kernel] * MFMA_PEAK) * 1e6
-    return max(thr, c["tile_us_" + kernel] * N / 128.0)
+    lat = c["tpro_us_" + kernel] + c["tile_us_" + kernel] * N / 128.0
+    return max(thr, lat)
 
 
 def pass_us(p: dict, nbytes: float) -> float:
@@ -144,28 +146,30 @@ def _median(xs):
 
 
 def fit_kernel(rows, key):
-    """(eta, t_tile_us) minimising the squared log error of
-    max(F / (eta P), t_tile N / 128) against the kernel times r[key]: a grid
-    over both in log steps of 10^(1/120), then one of 10^(1/2400) around the
+    """(eta, t_pro_us, t_tile_us) minimising the squared log error of
+    max(F / (eta P), t_pro + t_tile N / 128) against the kernel times r[key]:
+    a grid over t_pro in 0.25 us steps and over 1 / eta and t_tile in log
+    steps of 10^(1/120), then a finer one (0.05 us, 10^(1/2400)) around the
     best point."""
-    def err(a, b):
-        e = 0.0
-        for r in rows:
-            m = max(a * flops(r["B"], r["Hq"], r["N"], r["D"]) * 1e6, b * r["N"] / 128.0)
-            e += math.log(r[key] / m) ** 2
-        return e
+    import numpy as np
+    F = np.array([flops(r["B"], r["Hq"], r["N"], r["D"]) for r in rows]) * 1e6
+    n = np.array([r["N"] / 128.0 for r in rows])
+    t = np.array([float(r[key]) for r in rows])
 
-    # each term alone can only under-predict a row: start at the smallest
-    a0 = min(r[key] * 1e-6 / flops(r["B"], r["Hq"], r["N"], r["D"]) for r in rows)
-    b0 = min(r[key] / (r["N"] / 128.0) for r in rows)
-    best = min((err(a0 * 10 ** (i / 120.0), b0 * 10 ** (j / 120.0) if j else 0.0), i, j)
-               for i in range(121) for j in range(121))
-    _, i, j = best
-    a1, b1 = a0 * 10 ** (i / 120.0), b0 * 10 ** (j / 120.0) if j else 0.0
-    fine = min((err(a1 * 10 ** (u / 2400.0), b1 * 10 ** (v / 2400.0)), u, v)
-               for u in range(-20, 21) for v in range(-20, 21))
-    _, u, v = fine
-    return 1.0 / (a1 * 10 ** (u / 2400.0) * MFMA_PEAK), b1 * 10 ** (v / 2400.0)
+    def best(tp, a, b):
+        m = np.maximum(a[None, :, None, None] * F, tp[:, None, None, None] + b[None, None, :, None] * n)
+        e = (np.log(t / m) ** 2).sum(-1)
+        i = np.unravel_index(e.argmin(), e.shape)
+        return tp[i[0]], a[i[1]], b[i[2]]
+
+    a0 = (t / F).min()  # seconds per flop that the fastest row reaches
+    b0 = (t / n).min()
+    tp, a, b = best(np.arange(0.0, 20.001, 0.25), a0 * 10 ** (np.arange(-30, 91) / 120.0),
+                    np.concatenate([[0.0], b0 * 10 ** (np.arange(-90, 31) / 120.0)]))
+    tp, a, b = best(np.maximum(tp + np.arange(-5, 6) * 0.05, 0.0),
+                    a * 10 ** (np.arange(-20, 21) / 2400.0),
+                    b * 10 ** (np.arange(-20, 21) / 2400.0) if b > 0 else np.array([0.0]))
+    return 1.0 / (float(a) * MFMA_PEAK), float(tp), float(b)
 
 
 def fit_pass(rows):
@@ -199,7 +203,7 @@ def fit(rows) -> dict:
             continue
         c = {}
         for kern in KERNELS:
-            c["eta_" + kern], c["tile_us_" + kern] = fit_kernel(rs, keys[kern])
+            c["eta_" + kern], c["tpro_us_" + kern], c["tile_us_" + kern] = fit_kernel(rs, keys[kern])
         c.update(alphas(c))
         c["rows"] = len(rs)
         p[cls] = c
@@ -224,15 +228,15 @@ _HEADER_HEAD = """\
 // memory-bandwidth cost, in-kernel rotation a compute-and-tiling cost; per
 // paragraph 5 the choice is measured per architecture and shape. In
 // microseconds, with F = 2 B Hq N^2 D, P = 2516.6 TFLOP/s, BW = 8 TB/s:
-//   T_k     = max(F / (ETA_k P), TILE_US_k N / 128)  for the plain attention
-//             kernel (k = ATTN), the one rotating Q and K tiles (FUSED) and
-//             the one rotating Q rows (Q); the second term is an under-filled
-//             chip, where one workgroup's N / 128 key tiles set the time
+//   T_k     = max(F / (ETA_k P), TPRO_US_k + TILE_US_k N / 128)  for the plain
+//             attention kernel (k = ATTN), the one rotating Q and K tiles
+//             (FUSED) and the one rotating Q rows (Q); the second term is an
+//             under-filled chip: one workgroup's prologue and N / 128 key tiles
 //   fused   = T_FUSED
 //   prerot  = T0_US + 4 B (Hq + Hkv) N D / (ETA_BW BW) + T_ATTN + T_GAP_US
 //   split   = T0_US + 4 B Hkv N D / (ETA_BW BW) + T_Q + T_GAP_US
 // Per class of shape (head dim 64 or 128; MHA, or GQA when Hq / Hkv >= 2) the
-// six kernel constants, and the three pass/launch constants shared by all,
+// nine kernel constants, and the three pass/launch constants shared by all,
 // are least-squares fits to kernel times measured on MI355X back to back
 // (steady clocks) over the crossover families:%s
 #pragma once
@@ -246,15 +250,18 @@ constexpr double HBM_BW = 8.0e12;        // B/s
 
 _HEADER_TAIL = """
 struct Kernel {
-    double eta, tile_us;
+    double eta, tpro_us, tile_us;
 };
 struct Class {
     Kernel attn, fused, q;
 };
 
-#define RAC_MODEL_CLASS(P) \\
-    Class { {P##_ETA_ATTN, P##_TILE_US_ATTN}, {P##_ETA_FUSED, P##_TILE_US_FUSED}, \\
-            {P##_ETA_Q, P##_TILE_US_Q} }
+#define RAC_MODEL_CLASS(P)                                                          \\
+    Class {                                                                         \\
+        {P##_ETA_ATTN, P##_TPRO_US_ATTN, P##_TILE_US_ATTN},                         \\
+            {P##_ETA_FUSED, P##_TPRO_US_FUSED, P##_TILE_US_FUSED},                  \\
+            {P##_ETA_Q, P##_TPRO_US_Q, P##_TILE_US_Q}                               \\
+    }
 
 inline Class shape_class(int D, int Hq, int Hkv) {
     const bool gqa = Hq / Hkv >= 2;
@@ -266,7 +273,7 @@ inline Class shape_class(int D, int Hq, int Hkv) {
 
 inline double kernel_us(const Kernel& k, double flops, double n) {
     const double thr = flops / (k.eta * MFMA_PEAK) * 1e6;
-    const double lat = k.tile_us * n / 128.0;
+    const double lat = k.tpro_us + k.tile_us * n / 128.0;
     return thr > lat ? thr : lat;
 }
 
@@ -331,6 +338,9 @@ if __name__ == "__main__":
 
     line = json.loads(open(sys.argv[1]).read().strip().splitlines()[-1])
     cx = line["crossover"]
+    # the constants are this module's fit of the run's rows (the same fit the
+    # bench reports, redone here so that header and summary always agree)
+    cx["model"]["fit"] = fit(cx["rows"])
     fams = "".join("\n//   " + v["desc"] + ", N = " + ", ".join(str(n) for n in v["N"])
                    for v in cx["families"].values())
     with open(HEADER, "w") as f:

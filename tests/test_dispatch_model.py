@@ -50,19 +50,33 @@ def _synthetic_rows(p):
 def _params():
     p = {"eta_bw": 0.8, "t0_us": 3.0, "t_gap_us": 1.5}
     for i, cls in enumerate(M.CLASSES):
-        p[cls] = {"eta_attn": 0.30 + 0.02 * i, "tile_us_attn": 1.8 + 0.3 * i,
-                  "eta_fused": 0.25 + 0.01 * i, "tile_us_fused": 2.2 + 0.3 * i,
-                  "eta_q": 0.29 + 0.02 * i, "tile_us_q": 1.9 + 0.3 * i}
+        p[cls] = {"eta_attn": 0.30 + 0.02 * i, "tpro_us_attn": 8.0 + 0.5 * i,
+                  "tile_us_attn": 1.2 + 0.3 * i,
+                  "eta_fused": 0.25 + 0.01 * i, "tpro_us_fused": 7.5 + 0.5 * i,
+                  "tile_us_fused": 1.6 + 0.3 * i,
+                  "eta_q": 0.29 + 0.02 * i, "tpro_us_q": 8.25 + 0.5 * i,
+                  "tile_us_q": 1.3 + 0.3 * i}
     return p
 
 
 def test_fit_recovers_the_parameters_that_made_the_times():
+    """Every class's fit reproduces the times it was given; where a class
+    has several rows in each regime (D = 64: three under-filled, four full)
+    its parameters are the ones that made them. (With one under-filled row,
+    prologue and per-tile cost are not separable, and only the times are.)"""
     p = _params()
-    got = M.fit(_synthetic_rows(p))
-    for cls in M.CLASSES:
+    rows = _synthetic_rows(p)
+    got = M.fit(rows)
+    for r in rows:
+        c = got[M.class_key(r["D"], r["Hq"], r["Hkv"])]
+        for k, key in (("attn", "k_attn"), ("fused", "k_fused"), ("q", "k_attn_q")):
+            assert M.kernel_us(c, k, r["B"], r["Hq"], r["N"], r["D"]) == pytest.approx(
+                r[key], rel=5e-3), (r, k)
+    for cls in ("d64_mha", "d64_gqa"):
         for name in M.CLASS_PARAMS:
-            # the grid's last step is 10^(1/2400): 0.1 %
-            assert got[cls][name] == pytest.approx(p[cls][name], rel=2e-3), (cls, name)
+            # the grids' last steps: 10^(1/2400) (0.1 %) and 0.05 us
+            tol = dict(abs=0.051) if name.startswith("tpro") else dict(rel=3e-3)
+            assert got[cls][name] == pytest.approx(p[cls][name], **tol), (cls, name)
     assert got["eta_bw"] == pytest.approx(0.8, rel=1e-9)
     assert got["t0_us"] == pytest.approx(3.0, rel=1e-9)
     assert got["t_gap_us"] == pytest.approx(1.5, rel=1e-9)
@@ -72,7 +86,7 @@ def test_fit_alphas_are_the_rotation_cost():
     p = _params()
     a = M.alphas(p["d64_mha"])
     assert a["alpha_qk"] == pytest.approx(0.30 / 0.25 - 1.0)
-    assert a["alpha_qk_underfilled"] == pytest.approx(2.2 / 1.8 - 1.0)
+    assert a["alpha_qk_underfilled"] == pytest.approx(1.6 / 1.2 - 1.0)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(16, 16), (32, 8), (64, 8)])
@@ -84,7 +98,7 @@ def test_closed_form_is_the_model_crossover_when_the_chip_is_full(Hq, Hkv):
     p["t0_us"] = p["t_gap_us"] = 0.0
     for cls in M.CLASSES:
         for k in M.KERNELS:
-            p[cls]["tile_us_" + k] = 0.0
+            p[cls]["tile_us_" + k] = p[cls]["tpro_us_" + k] = 0.0
     c = p[M.class_key(128, Hq, Hkv)]
     n_closed = M.n_star_closed(c, p, Hq, Hkv)
     t = M.model_us(p, 1, Hq, Hkv, n_closed, 128, gap=False)

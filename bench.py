@@ -603,10 +603,7 @@ def crossover(torch, rac, inputs, dev, ev, repeats=3, reps=11):
                            p=r["samples"][i]["k_rope"] + r["samples"][i]["k_attn"]) for r in sweep]
             per_rep.append(locate_crossover(reps_i, "f", "p")["n_star"])
         callx = locate_crossover(sweep, "c_fused", "c_prerotate")
-        full = dict(fit)
-        full.update({c: fit[cls] for c in dispatch_fit.CLASSES})
-        n_model = dispatch_fit.n_star_model(full, 1, w0["Hq"], w0["Hkv"], w0["D"])
-        n_closed = dispatch_fit.n_star_closed(fit[cls], fit, w0["Hq"], w0["Hkv"])
+        n_model, n_closed = dispatch_fit.family_n_star(fit, w0["Hq"], w0["Hkv"], w0["D"])
         measured = kern["n_star"]
         worst = max(r["auto_vs_fastest"] for r in sweep)
         families[fam] = {

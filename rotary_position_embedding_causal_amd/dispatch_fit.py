@@ -139,6 +139,15 @@ def n_star_closed(c: dict, p: dict, Hq, Hkv) -> float:
         / alphas(c)["alpha_qk"]
 
 
+def family_n_star(p: dict, Hq, Hkv, D):
+    """A family's modelled N* (B = 1, kernel level: no second-launch cost)
+    and the closed form, from fitted parameters p."""
+    cls = class_key(D, Hq, Hkv)
+    full = dict(p)
+    full.update({c: p[cls] for c in CLASSES})
+    return n_star_model(full, 1, Hq, Hkv, D), n_star_closed(p[cls], p, Hq, Hkv)
+
+
 def _median(xs):
     xs = sorted(xs)
     n = len(xs)
@@ -340,7 +349,21 @@ if __name__ == "__main__":
     cx = line["crossover"]
     # the constants are this module's fit of the run's rows (the same fit the
     # bench reports, redone here so that header and summary always agree)
-    cx["model"]["fit"] = fit(cx["rows"])
+    fitted = fit(cx["rows"])
+    cx["model"]["fit"] = fitted
+    byname = {r["workload"]: r for r in cx["rows"]}
+    from rotary_position_embedding_causal_amd import inputs
+    for fam, v in cx["families"].items():
+        r0 = byname[inputs.CROSSOVER_FAMILIES[fam][1][0]]
+        n_model, n_closed = family_n_star(fitted, r0["Hq"], r0["Hkv"], r0["D"])
+        measured = v["n_star_kernels"]["n_star"]
+        v.update(n_star_model=n_model, n_star_closed_form=n_closed,
+                 model_vs_measured=(n_model / measured - 1.0) if (n_model and measured) else None)
+    head, c64 = cx["families"]["mha_d64_fp16"], fitted["d64_mha"]
+    cx["model"].update(alpha=c64["alpha_qk"], eta_mfma=c64["eta_attn"], eta_bw=fitted["eta_bw"],
+                       alpha_underfilled=c64["alpha_qk_underfilled"], t0_us=fitted["t0_us"],
+                       t_gap_us=fitted["t_gap_us"], n_star_model=head["n_star_model"],
+                       n_star_closed_form=head["n_star_closed_form"])
     fams = "".join("\n//   " + v["desc"] + ", N = " + ", ".join(str(n) for n in v["N"])
                    for v in cx["families"].values())
     with open(HEADER, "w") as f:

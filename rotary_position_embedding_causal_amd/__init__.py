@@ -363,7 +363,7 @@ def auto_plan(B: int, Hq: int, Hkv: int, N: int, D: int, dtype, workspace_bytes:
 
 def attn_rope_causal_auto(q, k, v, rope_base: float, workspace=None, out=None, lse=None,
                           want_lse: bool = True):
-    """RoPE + causal attention through the path measured fastest for the shape.
+    """RoPE + causal attention through the path the fitted cost model rates fastest.
 
     `workspace` is a caller-owned device tensor (any dtype, contiguous) for the rotated
     copies; None or too small falls back to a path that fits (the fused kernel needs

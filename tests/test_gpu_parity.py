@@ -5,9 +5,10 @@ Cases: the tiny MHA workload in full; small ragged shapes that span several
 tiles and end in partial tiles (N in {1, 2, 3, 17, 63, 64, 65, 127, 129,
 300}); GQA ratios 1, 2, 4, 8; D = 64 and 128; bf16 and fp16; large-sigma
 inputs that force many running-max rescales; and the full-size workloads
-(Llama-3-8B-shaped GQA layers, the D = 64 fp16 sweep) in the launch
-configuration the bench times, checked on sampled rows the oracle computes
-one by one.
+(Llama-3-8B-shaped GQA layers, the D = 64 fp16 sweep, the largest shape of
+each other crossover family) in the launch configuration the bench times,
+checked on sampled rows the oracle computes one by one, with the three paths
+and the dispatcher bit-identical.
 """
 import numpy as np
 import pytest
@@ -433,7 +434,10 @@ def test_empty_inputs():
 # 1024, 6144 and from 16384)
 FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
         "mha_d64_fp16_n1024", "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
-        "mha_d64_fp16_n16384", "mha_d64_fp16_n32768"]
+        "mha_d64_fp16_n16384", "mha_d64_fp16_n32768",
+        # the largest shape of each other crossover family, and its batched rows
+        "mha_d128_bf16_n16384", "mha_d128_bf16_b8_n1024", "gqa4_d64_bf16_n16384",
+        "llama3_8b_gqa_n16384", "gqa4_d128_fp16_n8192", "gqa8_d128_bf16_n8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -446,9 +450,14 @@ def test_full_size_sampled_rows(name):
     of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
     op, lp = rac.prerotate_path(qd, kd, vd, base)
     osp, lsp = rac.split_path(qd, kd, vd, base)
+    need = rac.auto_plan(B, Hq, Hkv, N, D, qd.dtype, 1 << 62)[1]
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    oa, la = rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(of, op) and torch.equal(lf, lp)
     assert torch.equal(of, osp) and torch.equal(lf, lsp)
+    assert torch.equal(of, oa) and torch.equal(lf, la)  # whichever path the model picks
+    del op, lp, osp, lsp, oa, la, ws
     rng = np.random.default_rng(len(name))
     rows = sampled_rows(B, Hq, N, rng)
     qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)

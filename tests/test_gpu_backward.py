@@ -170,12 +170,15 @@ def test_ragged_lengths_and_gqa(N, ratio, bwd_shape):
         assert_grad(to_f64(got), ref, "N=%d ratio=%d %s" % (N, ratio, name))
 
 
-@pytest.mark.parametrize("name,key", [("llama3_8b_gqa_n2048", 406), ("llama3_8b_gqa_n8192", 407)])
+@pytest.mark.parametrize("name,key", [("llama3_8b_gqa_n2048", 406), ("llama3_8b_gqa_n8192", 407),
+                                      ("gqa8_d128_bf16_n2048", 408), ("mha_d64_fp16_n8192", 409)])
 def test_full_length_one_group(name, key):
     """The Llama-3-8B-shaped layer at N = 2048 and 8192 in the bench's launch
-    configuration; the oracle checks one key/value group (4 query heads and
-    their key/value head) in full, which the other groups do not influence
-    (about 15 s of oracle time at N = 8192 on 16 cores)."""
+    configuration, a GQA 8:1 layer (two workgroups per key tile, paired dQ
+    launch) and a D = 64 fp16 MHA layer at N = 8192; the oracle checks one
+    key/value group (its query heads and their key/value head) in full,
+    which the other groups do not influence (about 15 s of oracle time at
+    N = 8192 on 16 cores)."""
     w = inputs.WORKLOADS[name]
     B, Hq, Hkv, N, D, dt, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"], w["base"]
     q, k, v = inputs.workload_qkv(name)

@@ -712,7 +712,7 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
             for (int qb = 0; qb < 2; ++qb) {
                 // S (and for dK, dP) for queries q0 + 32qb .. +31 (lane column = key)
                 f32x16 x = W::score(Qs, 32 * qb, kf, n, hh);
-                f32x16 dp;
+                f32x16 dp{};  // read only with DK
                 if (DK) dp = W::score(dOs, 32 * qb, vf, n, hh);
                 if (mask)
                     kv_p_block<true, DK>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N, scale_log2);

@@ -1103,9 +1103,25 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     // Measured on MI355X: D = 64 MHA at N = 8192 (two rounds) pair 3-9 %
     // faster; at N = 6144 (1.5 rounds) the tile launch 12-14 % faster; from
     // N = 16384, and for GQA from B * N = 4096, the tile launch faster.
+    // Below half a round the pair launch still wins once a head has enough
+    // query tiles for its shorter critical path (n_qtiles + 1 steps against
+    // the heaviest tile's 2 n_qtiles) to outweigh its merge: from 4 tiles
+    // against the two-head tile launch, from 12 against one head per 4-wave
+    // workgroup (MHA). With one head per tile workgroup the pair launch
+    // also wins at 1.5-2 rounds at D = 128. Measured on MI355X (fused,
+    // plain and Q-rotating kernels alike): GQA 8/2 D = 128 N = 1024-2048
+    // pair 17-28 % faster, GQA 32/8 N = 512-768 3-15 %, MHA 16/16 D = 64
+    // N = 1536-1792 1-10 % but N = 768-1024 0-12 % slower, MHA 32/32
+    // D = 128 N = 3072-3840 2-17 % faster, while at D = 64 N = 5120-7168
+    // (1.25-1.75 rounds) the tile launch stays 3-22 % faster.
     const bool heads_ok = (a.Hq / a.Hkv) % 2 == 0;
-    bool pair = n_qtiles >= 2 && pair_units >= NUM_CUS / 2 &&
-                (pair_units <= NUM_CUS || (!heads_ok && pair_units == 2 * NUM_CUS));
+    const int min_tiles = heads_ok ? 4 : 12;
+    bool pair = n_qtiles >= 2 && pair_units <= NUM_CUS &&
+                (pair_units >= NUM_CUS / 2 || n_qtiles >= min_tiles);
+    if (!heads_ok && n_qtiles >= 2 &&
+        (pair_units == 2 * NUM_CUS ||
+         (D == 128 && pair_units >= 3 * NUM_CUS / 2 && pair_units <= 2 * NUM_CUS)))
+        pair = true;
     // pair_heads (two GQA heads sharing every key tile) only when forced: with
     // K rotated in the kernel it beat the split pair by 3.5 % at N = 2048
     // (0.0616 vs 0.0638 ms), without rotation it lost (0.0512 vs 0.0448 ms),

@@ -603,28 +603,19 @@ def crossover(torch, rac, inputs, dev, ev, repeats=3, reps=11):
                            p=r["samples"][i]["k_rope"] + r["samples"][i]["k_attn"]) for r in sweep]
             per_rep.append(locate_crossover(reps_i, "f", "p")["n_star"])
         callx = locate_crossover(sweep, "c_fused", "c_prerotate")
-        n_model, n_closed = dispatch_fit.family_n_star(fit, w0["Hq"], w0["Hkv"], w0["D"])
-        measured = kern["n_star"]
         worst = max(r["auto_vs_fastest"] for r in sweep)
         families[fam] = {
             "desc": desc, "class": cls, "N": [r["N"] for r in sweep],
             "n_star_kernels": kern, "n_star_kernels_per_repeat": per_rep,
             "n_star_calls": callx,
-            "n_star_model": n_model, "n_star_closed_form": n_closed,
-            "model_vs_measured": (n_model / measured - 1.0) if (n_model and measured) else None,
             "auto_worst_vs_fastest": worst, "auto_within_2pct": worst <= 0.02}
+    dispatch_fit.family_models(fit, families, byname)
     for r in rows:
         del r["samples"]  # per-repeat figures: summarised above
     head = families["mha_d64_fp16"]
-    c64 = fit["d64_mha"]
-    model = {"alpha": c64["alpha_qk"], "eta_mfma": c64["eta_attn"], "eta_bw": fit["eta_bw"],
-             "n_star_model": head["n_star_model"], "n_star_closed_form": head["n_star_closed_form"],
-             "alpha_underfilled": c64["alpha_qk_underfilled"], "t0_us": fit["t0_us"],
-             "t_gap_us": fit["t_gap_us"], "fit": fit,
-             "dispatcher_constants": header,
-             "form": "T_k = max(F/(eta_k P), t_pro_k + t_tile_k N/128) per kernel; alpha = "
-                     "eta_attn/eta_fused - 1; pre = t0 + 4B(Hq+Hkv)ND/(eta_bw BW) + T_attn; N* "
-                     "where T_fused = pre"}
+    model = dict(dispatch_fit.headline_model(fit, families), fit=fit,
+                 fit_errors=dispatch_fit.fit_errors(fit, rows),
+                 dispatcher_constants=header, form=dispatch_fit.FORM)
     return {"n_star": head["n_star_kernels"]["n_star"],
             "level": "kernels (the fused kernel vs the pass plus plain attention)",
             "bracket": head["n_star_kernels"]["bracket"],

@@ -66,21 +66,40 @@ for _n in (1024, 4096, 16384):
     WORKLOADS["llama3_8b_gqa_n%d" % _n] = dict(B=1, Hq=32, Hkv=8, N=_n, D=128, dtype="bf16",
                                                base=500000.0)
 
+# midpoints around the crossovers (1.5K, 3K) for every family
+for _n in (1536, 3072):
+    WORKLOADS["mha_d64_fp16_n%d" % _n] = dict(B=1, Hq=16, Hkv=16, N=_n, D=64, dtype="fp16",
+                                              base=10000.0)
+    WORKLOADS["mha_d128_bf16_n%d" % _n] = dict(B=1, Hq=32, Hkv=32, N=_n, D=128, dtype="bf16",
+                                               base=10000.0)
+    WORKLOADS["gqa4_d64_bf16_n%d" % _n] = dict(B=1, Hq=32, Hkv=8, N=_n, D=64, dtype="bf16",
+                                               base=10000.0)
+    WORKLOADS["llama3_8b_gqa_n%d" % _n] = dict(B=1, Hq=32, Hkv=8, N=_n, D=128, dtype="bf16",
+                                               base=500000.0)
+    WORKLOADS["gqa4_d128_fp16_n%d" % _n] = dict(B=1, Hq=32, Hkv=8, N=_n, D=128, dtype="fp16",
+                                                base=500000.0)
+    WORKLOADS["gqa8_d128_bf16_n%d" % _n] = dict(B=1, Hq=64, Hkv=8, N=_n, D=128, dtype="bf16",
+                                                base=500000.0)
+
 # crossover families: (description, row names in ascending N); one family
 # shares D, dtype and Hq/Hkv, and within it only N changes (B = 1)
 CROSSOVER_FAMILIES = {
     "mha_d64_fp16": ("MHA D=64 fp16, B=1 H=16",
-                     ["mha_d64_fp16_n%d" % n for n in CROSSOVER_NS]),
+                     ["mha_d64_fp16_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 6144, 8192,
+                                                       16384, 32768)]),
     "mha_d128_bf16": ("MHA D=128 bf16, B=1 H=32",
-                      ["mha_d128_bf16_n%d" % n for n in (1024, 2048, 4096, 8192, 16384)]),
+                      ["mha_d128_bf16_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 8192,
+                                                         16384)]),
     "gqa4_d64_bf16": ("GQA 4:1 D=64 bf16, B=1 Hq=32 Hkv=8",
-                      ["gqa4_d64_bf16_n%d" % n for n in (1024, 2048, 4096, 8192, 16384)]),
+                      ["gqa4_d64_bf16_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 8192,
+                                                         16384)]),
     "gqa4_d128_bf16": ("GQA 4:1 D=128 bf16 (Llama-3-8B layer), B=1 Hq=32 Hkv=8",
-                       ["llama3_8b_gqa_n%d" % n for n in (1024, 2048, 4096, 8192, 16384)]),
+                       ["llama3_8b_gqa_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 8192,
+                                                          16384)]),
     "gqa4_d128_fp16": ("GQA 4:1 D=128 fp16, B=1 Hq=32 Hkv=8",
-                       ["gqa4_d128_fp16_n%d" % n for n in (1024, 2048, 4096, 8192)]),
+                       ["gqa4_d128_fp16_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 8192)]),
     "gqa8_d128_bf16": ("GQA 8:1 D=128 bf16, B=1 Hq=64 Hkv=8",
-                       ["gqa8_d128_bf16_n%d" % n for n in (1024, 2048, 4096, 8192)]),
+                       ["gqa8_d128_bf16_n%d" % n for n in (1024, 1536, 2048, 3072, 4096, 8192)]),
 }
 # rows outside the families: other batch sizes of a family's layer
 CROSSOVER_EXTRA = ["mha_d128_bf16_b8_n1024", "llama3_8b_gqa_b4_n4096"]

@@ -244,13 +244,14 @@ enum { RAC_PATH_FUSED = 0, RAC_PATH_PREROTATE = 1, RAC_PATH_SPLIT = 2 };
  * the same rotated operands to the same attention arithmetic), computed by the
  * path with the least modelled time on MI355X for this shape. The model costs
  * the streaming pass by its bytes (4 B H N D for H rotated heads) at a fitted
- * fraction of 8 TB/s plus a fixed cost and a second launch, the attention
- * kernel by its work at a fitted fraction of the MFMA peak (or, when the grid
- * is too small to fill the chip, by one workgroup's N / 128 key tiles), and
- * in-kernel rotation as a fitted fraction of the attention time; the
- * constants are fitted per head dim (64, 128) and MHA/GQA to kernel times
- * measured over D = 64 and 128, bf16 and fp16, MHA, GQA 4:1 and 8:1,
- * N = 1024 .. 32768. It weighs the whole problem: more batch or heads at the
+ * fraction of 8 TB/s plus a fixed cost and a second launch, and each
+ * attention kernel (plain, rotating Q and K, rotating Q only) by a fitted
+ * time per workgroup step over one 64-key tile times the makespan of its
+ * launch: every workgroup's key tiles plus a fitted fixed part, scheduled on
+ * the CUs of each XCD in launch order; the constants are fitted per head dim
+ * (64, 128) and MHA/GQA to kernel times measured over D = 64 and 128, bf16
+ * and fp16, MHA, GQA 4:1 and 8:1, N = 1024 .. 32768. It weighs the whole
+ * problem: more batch or heads at the
  * same N moves the choice as the work moves it. The choice of pre-rotation
  * versus in-kernel rotation is the one the AttnFuse report, paragraphs 3 and
  * 5, says depends on the GPU and the shape.

@@ -292,12 +292,12 @@ int bwd_dq_from_env() {
 // All three paths give bit-identical results (they hand the same rotated
 // operands to the same attention arithmetic), so the choice is about time
 // only: the path with the least modelled time (dispatch_model.h: a cost model
-// of the attention kernel, the in-kernel rotation and the streaming pass,
-// fitted per head dim and MHA/GQA class to kernel times measured on MI355X).
-// The model weighs the whole problem (B, heads, N, D), not N alone: the pass
-// costs bytes, the rotation a share of the attention's time, and an
-// under-filled grid (few heads, short N) keeps the attention time from
-// shrinking with the work.
+// of the attention kernels and the streaming pass, fitted per head dim and
+// MHA/GQA class to kernel times measured on MI355X). The model weighs the
+// whole problem (B, heads, N, D), not N alone: the pass costs bytes, each
+// attention kernel a time per workgroup step times its launch's makespan
+// (rounds of workgroups over the CUs), so an under-filled grid (few heads,
+// short N) keeps the attention time from shrinking with the work.
 size_t path_workspace(int path, int B, int Hq, int Hkv, int N, int D) {
     const size_t q = (size_t)B * Hq * N * D * 2, k = (size_t)B * Hkv * N * D * 2;
     const size_t q16 = (q + 255) & ~(size_t)255;  // K' starts 256-byte aligned

@@ -209,20 +209,21 @@ class Oracle:
         return dq, dk, dv, lse, delta
 
     def rope_attention_bwd(self, q_bits, k_bits, v_bits, do_bits, dtype: str, base: float,
-                           variant: str = "rounded"):
+                           variant: str = "rounded", pairing: str = "adjacent"):
         """Gradients of RoPE then causal attention with respect to the
         unrotated q, k and to v, from bf16/fp16 bit patterns.
 
         The attention gradients are taken at the rotated operands (``variant``
         as in rope_attention); RoPE's gradient is its inverse rotation, the
-        turn by -p theta_i. Returns (dq, dk, dv, delta, lse).
+        turn by -p theta_i of the same pairs (``pairing`` as in rope()).
+        Returns (dq, dk, dv, delta, lse).
         """
         q = self.decode(q_bits, dtype)
         k = self.decode(k_bits, dtype)
         v = self.decode(v_bits, dtype)
         do = self.decode(do_bits, dtype)
-        qr = self.rope_bhnd(q, base)
-        kr = self.rope_bhnd(k, base)
+        qr = self.rope_bhnd(q, base, pairing)
+        kr = self.rope_bhnd(k, base, pairing)
         if variant == "rounded":
             qr = self.decode(self.encode(qr, dtype), dtype)
             kr = self.decode(self.encode(kr, dtype), dtype)
@@ -230,7 +231,8 @@ class Oracle:
             raise ValueError("variant must be 'exact' or 'rounded'")
         dqr, dkr, dv, lse, delta = self.attention_bwd(qr, kr, v, do)
         neg = -np.arange(q.shape[-2], dtype=np.int64)
-        return self.rope(dqr, neg, base), self.rope(dkr, neg, base), dv, delta, lse
+        return (self.rope(dqr, neg, base, pairing), self.rope(dkr, neg, base, pairing), dv, delta,
+                lse)
 
 
 def _ptr(a, ctype):
@@ -285,5 +287,7 @@ def attention_bwd(q, k, v, dout):
     return default().attention_bwd(q, k, v, dout)
 
 
-def rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant="rounded"):
-    return default().rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant)
+def rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant="rounded",
+                       pairing="adjacent"):
+    return default().rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant,
+                                        pairing)

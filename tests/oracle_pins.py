@@ -448,10 +448,10 @@ def pin_attention_bwd_special_cases(orc):
     assert np.max(np.abs(dv0[:, :, 1:])) == 0.0
 
 
-def pin_rope_attention_bwd_finite_differences(orc):
+def _rope_attention_bwd_fd(orc, pairing, seed):
     # gradients with respect to the unrotated q and k (the inverse rotation),
     # against central differences of the RoPE-then-attention forward
-    rng = _rng(22)
+    rng = _rng(seed)
     B, Hq, Hkv, N, D, base = 1, 2, 1, 12, 8, 10000.0
 
     def bf16_bits(shape):
@@ -462,11 +462,12 @@ def pin_rope_attention_bwd_finite_differences(orc):
                                               (B, Hq, N, D)))
     q, k, v, do = (orc.decode(b, "bf16") for b in (qb, kb, vb, dob))
     dq, dk, dv, delta, lse = orc.rope_attention_bwd(qb, kb, vb, dob, "bf16", base,
-                                                    variant="exact")
+                                                    variant="exact", pairing=pairing)
     pos = np.arange(N)
 
     def loss(q_, k_, v_):
-        o, _ = orc.attention(orc.rope(q_, pos, base), orc.rope(k_, pos, base), v_)
+        o, _ = orc.attention(orc.rope(q_, pos, base, pairing), orc.rope(k_, pos, base, pairing),
+                             v_)
         return float(np.sum(do * o))
 
     h = 1e-6
@@ -479,6 +480,15 @@ def pin_rope_attention_bwd_finite_differences(orc):
             args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
             fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
             assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def pin_rope_attention_bwd_finite_differences(orc):
+    _rope_attention_bwd_fd(orc, "adjacent", 22)
+
+
+def pin_rope_half_attention_bwd_finite_differences(orc):
+    # the half-split pairing's gradient: the inverse turn of pairs (i, i + D/2)
+    _rope_attention_bwd_fd(orc, "half", 26)
 
 
 # --------------------------------------------------------------------------

@@ -407,14 +407,21 @@ def variants(torch, rac, w, qd, kd, vd, ev, reps):
 def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):
     """The backward of both paths on the bench workload, after the timed region
     (not part of `value`): fused (attn_rope_causal_bwd) and pre-rotation
-    (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd). TFLOP/s count the
-    algorithmic backward work, 2.5 x the forward's (five N^2 products: S, dP,
-    dV, dK, dQ); the two-pass kernels rebuild S and dP once more."""
+    (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd), and both again with
+    the half-split RoPE pairing (from the half-split forward's out and lse).
+    TFLOP/s count the algorithmic backward work, 2.5 x the forward's (five N^2
+    products: S, dP, dV, dK, dQ); the two-pass kernels rebuild S and dP once
+    more."""
     gen = torch.Generator(device=qd.device).manual_seed(20260913)
     dout = torch.randn(qd.shape, generator=gen, device=qd.device, dtype=torch.float32).to(qd.dtype)
     base = w["base"]
+    out_h, lse_h = rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half")
     fns = {"fused": lambda: rac.attn_rope_causal_bwd(qd, kd, vd, out, lse, dout, base),
-           "prerotate": lambda: rac.prerotate_path_bwd(qd, kd, vd, out, lse, dout, base)}
+           "prerotate": lambda: rac.prerotate_path_bwd(qd, kd, vd, out, lse, dout, base),
+           "fused_half": lambda: rac.attn_rope_causal_bwd_ex(qd, kd, vd, out_h, lse_h, dout, base,
+                                                             "half"),
+           "prerotate_half": lambda: rac.prerotate_path_bwd(qd, kd, vd, out_h, lse_h, dout, base,
+                                                            "half")}
     res = {"flops_per_call": 2.5 * attn_flops(w), "dout": "N(0,1) from a seeded torch generator"}
     for key, fn in fns.items():
         warm(fn, 3, WARM_SECONDS, torch.cuda.synchronize)

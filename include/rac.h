@@ -25,9 +25,10 @@
  *                         whichever of the three paths is fastest for the
  *                         shape on MI355X (the report's paragraph 5: the
  *                         choice is measured per architecture and shape).
- *   rope_prerotate_ex, attn_rope_causal_fwd_ex
- *                         the pass and the fused kernel with the half-split
- *                         RoPE pairing (i, i + D/2) as an alternative.
+ *   rope_prerotate_ex, attn_rope_causal_fwd_ex, attn_rope_causal_bwd_ex,
+ *   rope_prerotate_bwd_ex the pass, the fused kernel and their gradients with
+ *                         the half-split RoPE pairing (i, i + D/2) as an
+ *                         alternative.
  *   attn_alibi_causal_fwd causal attention with the ALiBi distance penalty
  *                         after the QK product, alone or with fused RoPE.
  *
@@ -333,6 +334,33 @@ int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out
  */
 int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
                        int Hkv, int N, int D, double rope_base, int dtype, void* stream);
+
+/*
+ * The backward with a choice of RoPE pairing (RAC_PAIR_ADJACENT or
+ * RAC_PAIR_HALF), for the forward of attn_rope_causal_fwd_ex and of
+ * rope_prerotate_ex: "rotate half" checkpoints (the Llama layout) train
+ * through it. The gradient of the turn is the inverse turn of the same pairs
+ * (for the half-split pairing, element d with d + D/2: x_d = y_d cos +
+ * y_{d+D/2} sin, x_{d+D/2} = y_{d+D/2} cos - y_d sin, in fp32, one rounding).
+ *
+ * attn_rope_causal_bwd_ex: as attn_rope_causal_bwd. With RAC_PAIR_HALF the
+ *   two passes run on q and k rotated once by the half-split streaming pass
+ *   (the same 2 * B * (Hq + Hkv) * N * D bytes of stream-ordered scratch),
+ *   write dq and dk in the rotated frame, and a third streaming pass turns
+ *   them back in place; B * (Hq + Hkv) <= 524280 (RAC_ERR_ARG beyond: the
+ *   pass's grid), and RAC_BWD_ROT has no effect. Its results are those of
+ *   rope_prerotate_ex, attn_causal_bwd and rope_prerotate_bwd_ex in turn,
+ *   bit for bit. RAC_PAIR_ADJACENT is attn_rope_causal_bwd.
+ * rope_prerotate_bwd_ex: as rope_prerotate_bwd, with the pairing.
+ * Any other pairing value: RAC_ERR_ARG.
+ */
+int attn_rope_causal_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* delta, int B, int Hq, int Hkv, int N, int D, double rope_base,
+                            int pairing, int dtype, void* stream);
+int rope_prerotate_bwd_ex(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B,
+                          int Hq, int Hkv, int N, int D, double rope_base, int pairing, int dtype,
+                          void* stream);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 const char* rac_last_error(void);

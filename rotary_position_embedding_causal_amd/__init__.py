@@ -38,7 +38,8 @@ EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_p
             "attn_rope_causal_bwd", "attn_causal_bwd", "rope_prerotate_bwd",
             "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
             "rac_last_error", "rac_release_tables", "rac_time_next_kernel",
-            "attn_rope_causal_fwd_noalloc", "rac_stream_copy")
+            "attn_rope_causal_fwd_noalloc", "rac_stream_copy", "attn_rope_causal_bwd_ex",
+            "rope_prerotate_bwd_ex")
 RAC_NOALLOC_MAX_N = 32768
 RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
 PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.attn_causal_bwd.restype = i
     L.rope_prerotate_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp]
     L.rope_prerotate_bwd.restype = i
+    L.attn_rope_causal_bwd_ex.argtypes = [vp] * 10 + [i] * 5 + [d, i, i, vp]
+    L.attn_rope_causal_bwd_ex.restype = i
+    L.rope_prerotate_bwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp]
+    L.rope_prerotate_bwd_ex.restype = i
     L.rope_prerotate_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp]
     L.rope_prerotate_ex.restype = i
     L.attn_rope_causal_fwd_ex.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, i, vp]
@@ -409,6 +414,19 @@ def attn_rope_causal_bwd(q, k, v, out, lse, dout, rope_base: float):
     return dq, dk, dv, delta
 
 
+def attn_rope_causal_bwd_ex(q, k, v, out, lse, dout, rope_base: float, pairing="adjacent"):
+    """Backward of attn_rope_causal_fwd_ex with a choice of RoPE pairing ("adjacent" or
+    "half"). Returns (dq, dk, dv, delta)."""
+    (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta) = _bwd_tensors(q, k, v, out, lse, dout)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_rope_causal_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                           B, Hq, Hkv, N, D, float(rope_base), _pairing(pairing),
+                                           dt, _stream(q.device))
+    check(rc, "attn_rope_causal_bwd_ex")
+    return dq, dk, dv, delta
+
+
 def attn_causal_bwd(q, k, v, out, lse, dout):
     """Backward of attn_causal_fwd (q, k already rotated). Returns (dq, dk, dv, delta)."""
     (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta) = _bwd_tensors(q, k, v, out, lse, dout)
@@ -422,6 +440,12 @@ def attn_causal_bwd(q, k, v, out, lse, dout):
 
 def rope_prerotate_bwd(dq_rot, dk_rot, rope_base: float, dq=None, dk=None):
     """Backward of rope_prerotate: (dq, dk) = R(-p) (dq_rot, dk_rot); dq=dq_rot for in place."""
+    return rope_prerotate_bwd_ex(dq_rot, dk_rot, rope_base, "adjacent", dq, dk)
+
+
+def rope_prerotate_bwd_ex(dq_rot, dk_rot, rope_base: float, pairing="adjacent", dq=None,
+                          dk=None):
+    """Backward of rope_prerotate_ex with a choice of RoPE pairing. Returns (dq, dk)."""
     B, Hq, Hkv, N, D, dt = _check_qkv(dq_rot, dk_rot, None)
     dq = torch.empty_like(dq_rot) if dq is None else dq
     dk = torch.empty_like(dk_rot) if dk is None else dk
@@ -430,16 +454,17 @@ def rope_prerotate_bwd(dq_rot, dk_rot, rope_base: float, dq=None, dk=None):
                 or dst.device != src.device:
             raise ValueError("dq/dk must be contiguous tensors like dq_rot/dk_rot")
     with torch.cuda.device(dq_rot.device):
-        rc = lib().rope_prerotate_bwd(_ptr(dq_rot), _ptr(dk_rot), _ptr(dq), _ptr(dk), B, Hq, Hkv,
-                                      N, D, float(rope_base), dt, _stream(dq_rot.device))
-    check(rc, "rope_prerotate_bwd")
+        rc = lib().rope_prerotate_bwd_ex(_ptr(dq_rot), _ptr(dk_rot), _ptr(dq), _ptr(dk), B, Hq,
+                                         Hkv, N, D, float(rope_base), _pairing(pairing), dt,
+                                         _stream(dq_rot.device))
+    check(rc, "rope_prerotate_bwd_ex")
     return dq, dk
 
 
-def prerotate_path_bwd(q, k, v, out, lse, dout, rope_base: float):
-    """Backward of the pre-rotation path: rope_prerotate (the rotated operands the forward
-    used), attn_causal_bwd on them, rope_prerotate_bwd. Returns (dq, dk, dv, delta)."""
-    q_rot, k_rot = rope_prerotate(q, k, rope_base)
+def prerotate_path_bwd(q, k, v, out, lse, dout, rope_base: float, pairing="adjacent"):
+    """Backward of the pre-rotation path: rope_prerotate_ex (the rotated operands the forward
+    used), attn_causal_bwd on them, rope_prerotate_bwd_ex. Returns (dq, dk, dv, delta)."""
+    q_rot, k_rot = rope_prerotate_ex(q, k, rope_base, pairing)
     dq_rot, dk_rot, dv, delta = attn_causal_bwd(q_rot, k_rot, v, out, lse, dout)
-    dq, dk = rope_prerotate_bwd(dq_rot, dk_rot, rope_base, dq=dq_rot, dk=dk_rot)
+    dq, dk = rope_prerotate_bwd_ex(dq_rot, dk_rot, rope_base, pairing, dq=dq_rot, dk=dk_rot)
     return dq, dk, dv, delta

@@ -369,21 +369,37 @@ int check_bwd_ptrs(const rac::BwdArgs& a) {
     return RAC_OK;
 }
 
+// Launches a streaming pass (pre-rotation or its inverse) from inside a
+// backward call, which leaves the kernel timer armed for the next forward or
+// pass call.
+template <typename Launch>
+hipError_t untimed(Launch launch) {
+    const hipEvent_t timer_start = g_timer_start, timer_stop = g_timer_stop;
+    g_timer_start = g_timer_stop = nullptr;
+    const hipError_t e = launch();
+    g_timer_start = timer_start;
+    g_timer_stop = timer_stop;
+    return e;
+}
+
 int attn_bwd_common(const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
                     int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype, int rot,
-                    void* stream, const char* what) {
+                    void* stream, const char* what, bool half = false) {
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
     if (rot == rac::ROT_QK && (rc = check_base(rope_base)) != RAC_OK) return rc;
+    const bool pass_fits = (int64_t)B * (Hq + (int64_t)Hkv) <= 8LL * 65535;
+    if (half && !pass_fits)
+        return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280 for the half-split pairing");
     if (empty) return ok();
     rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype,
                    bwd_shape_from_env(), bwd_dq_from_env()};
     if ((rc = check_bwd_ptrs(a)) != RAC_OK) return rc;
     if (rot == rac::ROT_QK && (rc = get_table(D, rope_base, N, &a.table)) != RAC_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (rot != rac::ROT_QK || bwd_rotation_in_kernel())
+    if (rot != rac::ROT_QK || (!half && bwd_rotation_in_kernel()))
         return hip_status(rac::launch_attn_bwd(a, rot, st), what);
     // Both passes read every query and key tile many times (each key tile once
     // per query tile that sees it, and the reverse), so the rotated operands
@@ -391,25 +407,33 @@ int attn_bwd_common(const void* q, const void* k, const void* v, const void* out
     // kernels then read them as they are and turn dq and dk back by R(-p) in
     // their epilogues, exactly as when rotating in the kernel (the same
     // operands, the same arithmetic).
+    // With the half-split pairing the kernels run plain on the rotated
+    // operands and write the gradients in the rotated frame, which a second
+    // streaming pass turns back by R(-p) in place (the epilogues' in-register
+    // turn handles adjacent pairs only).
     const size_t qbytes = (size_t)B * Hq * N * D * 2, kbytes = (size_t)B * Hkv * N * D * 2;
     const size_t q16 = (qbytes + 255) & ~(size_t)255;
     char* scratch = nullptr;
-    if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)  // the pass's grid: rotate in the kernel
+    if (!pass_fits)  // the pass's grid: rotate in the kernel
         return hip_status(rac::launch_attn_bwd(a, rot, st), what);
     hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), q16 + kbytes, st);
     if (e != hipSuccess) return hip_status(e, "attn_rope_causal_bwd scratch allocation");
-    // backward launches leave the kernel timer armed for the next forward or pass call
-    const hipEvent_t timer_start = g_timer_start, timer_stop = g_timer_stop;
-    g_timer_start = g_timer_stop = nullptr;
-    e = rac::launch_rope_prerotate(q, k, scratch, scratch + q16, a.table, B, Hq, Hkv, N, D, dtype,
-                                   st);
-    g_timer_start = timer_start;
-    g_timer_stop = timer_stop;
+    e = untimed([&] {
+        return half ? rac::launch_rope_prerotate_half(q, k, scratch, scratch + q16, a.table, B,
+                                                      Hq, Hkv, N, D, dtype, st)
+                    : rac::launch_rope_prerotate(q, k, scratch, scratch + q16, a.table, B, Hq,
+                                                 Hkv, N, D, dtype, st);
+    });
     if (e == hipSuccess) {
         a.q = scratch;
         a.k = scratch + q16;
-        e = rac::launch_attn_bwd(a, rac::ROT_QK_OUT, st);
+        e = rac::launch_attn_bwd(a, half ? rac::ROT_NONE : rac::ROT_QK_OUT, st);
     }
+    if (e == hipSuccess && half)
+        e = untimed([&] {
+            return rac::launch_rope_unrotate_half(dq, dk, dq, dk, a.table, B, Hq, Hkv, N, D,
+                                                  dtype, st);
+        });
     const hipError_t f = hipFreeAsync(scratch, st);
     return hip_status(e != hipSuccess ? e : f, what);
 }
@@ -559,31 +583,55 @@ int rope_prerotate(const void* q, const void* k, void* q_rot, void* k_rot, int B
                              dtype, stream);
 }
 
-int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
-                       int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+int rope_prerotate_bwd_ex(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B,
+                          int Hq, int Hkv, int N, int D, double rope_base, int pairing, int dtype,
+                          void* stream) {
     const TimerScope timer_scope;
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
     if ((rc = check_base(rope_base)) != RAC_OK) return rc;
+    if ((rc = check_pairing(pairing)) != RAC_OK) return rc;
     if ((int64_t)B * (Hq + (int64_t)Hkv) > 8LL * 65535)
         return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280");
     if (empty) return ok();
     if ((rc = check_pass_ptrs(dq_rot, dk_rot, dq, dk, B, Hq, Hkv, N, D)) != RAC_OK) return rc;
     const float* table = nullptr;
     if ((rc = get_table(D, rope_base, N, &table)) != RAC_OK) return rc;
-    return hip_status(rac::launch_rope_unrotate(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D,
-                                                dtype, static_cast<hipStream_t>(stream)),
-                      "rope_prerotate_bwd launch");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(
+        pairing == RAC_PAIR_HALF
+            ? rac::launch_rope_unrotate_half(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D,
+                                             dtype, st)
+            : rac::launch_rope_unrotate(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D, dtype,
+                                        st),
+        "rope_prerotate_bwd launch");
 }
 
+int rope_prerotate_bwd(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B, int Hq,
+                       int Hkv, int N, int D, double rope_base, int dtype, void* stream) {
+    return rope_prerotate_bwd_ex(dq_rot, dk_rot, dq, dk, B, Hq, Hkv, N, D, rope_base,
+                                 RAC_PAIR_ADJACENT, dtype, stream);
+}
+
+
+int attn_rope_causal_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* delta, int B, int Hq, int Hkv, int N, int D, double rope_base,
+                            int pairing, int dtype, void* stream) {
+    const int rc = check_pairing(pairing);
+    if (rc != RAC_OK) return rc;
+    return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                           rope_base, dtype, rac::ROT_QK, stream, "attn_rope_causal_bwd launch",
+                           pairing == RAC_PAIR_HALF);
+}
 
 int attn_rope_causal_bwd(const void* q, const void* k, const void* v, const void* out,
                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
                          float* delta, int B, int Hq, int Hkv, int N, int D, double rope_base,
                          int dtype, void* stream) {
-    return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D,
-                           rope_base, dtype, rac::ROT_QK, stream, "attn_rope_causal_bwd launch");
+    return attn_rope_causal_bwd_ex(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                                   rope_base, RAC_PAIR_ADJACENT, dtype, stream);
 }
 
 int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out,

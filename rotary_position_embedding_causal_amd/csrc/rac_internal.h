@@ -104,4 +104,9 @@ hipError_t launch_rope_unrotate(const void* dq_rot, const void* dk_rot, void* dq
                                 const float* table, int B, int Hq, int Hkv, int N, int D,
                                 int dtype, hipStream_t stream);
 
+// The inverse turn with the half-split pairing.
+hipError_t launch_rope_unrotate_half(const void* dq_rot, const void* dk_rot, void* dq, void* dk,
+                                     const float* table, int B, int Hq, int Hkv, int N, int D,
+                                     int dtype, hipStream_t stream);
+
 }  // namespace rac

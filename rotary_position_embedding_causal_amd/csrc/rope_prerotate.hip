@@ -87,11 +87,36 @@ __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_kernel(
     }
 }
 
+// The inverse turn of rope_rotate_half8: each pair (a', b') = (lo[j], hi[j])
+// goes back by R(-p), a = a' c + b' s and b = b' c - a' s, in fp32 with one
+// fused multiply-add each, then one rounding to the storage format.
+template <int DT>
+__device__ __forceinline__ void rope_unrotate_half8(u32x4 lo, u32x4 hi, const f32x4 (&cs)[4],
+                                                    u32x4& lo_out, u32x4& hi_out) {
+    typedef Fmt<DT> F;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float x[2], y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int j = 2 * t + e;  // frequency d0 + j
+            const float c = cs[j >> 1][2 * (j & 1)], sn = cs[j >> 1][2 * (j & 1) + 1];
+            const float a = e ? F::hi(lo[t]) : F::lo(lo[t]);
+            const float b = e ? F::hi(hi[t]) : F::lo(hi[t]);
+            x[e] = __builtin_fmaf(a, c, b * sn);
+            y[e] = __builtin_fmaf(b, c, -(a * sn));
+        }
+        lo_out[t] = F::pack2(x[0], x[1]);
+        hi_out[t] = F::pack2(y[0], y[1]);
+    }
+}
+
 // The half-split pairing: a lane owns chunk c < D/16 of a row and its
 // partner chunk c + D/16 (elements d and d + D/2 pair), with the 16 table
-// floats of frequencies 8c .. 8c+7, for PR_HEADS slabs.
+// floats of frequencies 8c .. 8c+7, for PR_HEADS slabs. INV: turn by -p
+// (the gradient of the pass).
 // (in-place use as for rope_prerotate_kernel)
-template <int DT, int D, int PR_HEADS>
+template <int DT, int D, int PR_HEADS, bool INV>
 __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_half_kernel(
     const uint16_t* q, const uint16_t* k, uint16_t* q_rot, uint16_t* k_rot,
     const float* __restrict__ table, int N, int64_t q_slabs, int64_t total_slabs) {
@@ -125,7 +150,10 @@ __global__ __launch_bounds__(PR_THREADS) void rope_prerotate_half_kernel(
             uint16_t* dst = slab < q_slabs ? q_rot + slab * slab_elems
                                            : k_rot + (slab - q_slabs) * slab_elems;
             u32x4 a, b;
-            rope_rotate_half8<DT>(lo[s], hi[s], cs, a, b);
+            if (INV)
+                rope_unrotate_half8<DT>(lo[s], hi[s], cs, a, b);
+            else
+                rope_rotate_half8<DT>(lo[s], hi[s], cs, a, b);
             __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(dst + lo_off));
             __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(dst + hi_off));
         }
@@ -237,19 +265,19 @@ hipError_t launch_rope_unrotate(const void* dq_rot, const void* dk_rot, void* dq
     return launch_any<true>(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D, dtype, stream);
 }
 
-template <int DT, int D, int H>
+template <int DT, int D, int H, bool INV>
 static hipError_t launch_half_heads(const void* q, const void* k, void* q_rot, void* k_rot,
                                     const float* table, int N, int64_t q_slabs, int64_t total,
                                     unsigned gx, hipStream_t stream) {
     dim3 grid(gx, (unsigned)((total + H - 1) / H));
-    return launch_kernel(rope_prerotate_half_kernel<DT, D, H>, grid, dim3(PR_THREADS), stream,
+    return launch_kernel(rope_prerotate_half_kernel<DT, D, H, INV>, grid, dim3(PR_THREADS), stream,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<uint16_t*>(q_rot), static_cast<uint16_t*>(k_rot), table, N,
                          q_slabs, total);
 }
 
 // Same grid policy as the adjacent pairing, with one lane per chunk pair.
-template <int DT, int D>
+template <int DT, int D, bool INV>
 static hipError_t launch_half(const void* q, const void* k, void* q_rot, void* k_rot,
                               const float* table, int B, int Hq, int Hkv, int N,
                               hipStream_t stream) {
@@ -258,21 +286,34 @@ static hipError_t launch_half(const void* q, const void* k, void* q_rot, void* k
     const int64_t total = q_slabs + (int64_t)B * Hkv;
     const unsigned gx = (unsigned)((lanes + PR_THREADS - 1) / PR_THREADS);
     switch (prerotate_heads(total)) {
-        case 8: return launch_half_heads<DT, D, 8>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        case 4: return launch_half_heads<DT, D, 4>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        case 2: return launch_half_heads<DT, D, 2>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
-        default: return launch_half_heads<DT, D, 1>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 8: return launch_half_heads<DT, D, 8, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 4: return launch_half_heads<DT, D, 4, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        case 2: return launch_half_heads<DT, D, 2, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
+        default: return launch_half_heads<DT, D, 1, INV>(q, k, q_rot, k_rot, table, N, q_slabs, total, gx, stream);
     }
+}
+
+template <bool INV>
+static hipError_t launch_half_any(const void* q, const void* k, void* q_rot, void* k_rot,
+                                  const float* table, int B, int Hq, int Hkv, int N, int D,
+                                  int dtype, hipStream_t stream) {
+    if (dtype == DT_BF16)
+        return D == 64 ? launch_half<DT_BF16, 64, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                       : launch_half<DT_BF16, 128, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return D == 64 ? launch_half<DT_FP16, 64, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
+                   : launch_half<DT_FP16, 128, INV>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
 }
 
 hipError_t launch_rope_prerotate_half(const void* q, const void* k, void* q_rot, void* k_rot,
                                       const float* table, int B, int Hq, int Hkv, int N, int D,
                                       int dtype, hipStream_t stream) {
-    if (dtype == DT_BF16)
-        return D == 64 ? launch_half<DT_BF16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
-                       : launch_half<DT_BF16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
-    return D == 64 ? launch_half<DT_FP16, 64>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream)
-                   : launch_half<DT_FP16, 128>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, stream);
+    return launch_half_any<false>(q, k, q_rot, k_rot, table, B, Hq, Hkv, N, D, dtype, stream);
+}
+
+hipError_t launch_rope_unrotate_half(const void* dq_rot, const void* dk_rot, void* dq, void* dk,
+                                     const float* table, int B, int Hq, int Hkv, int N, int D,
+                                     int dtype, hipStream_t stream) {
+    return launch_half_any<true>(dq_rot, dk_rot, dq, dk, table, B, Hq, Hkv, N, D, dtype, stream);
 }
 
 }  // namespace rac

@@ -282,13 +282,15 @@ def test_auto_plan_empty_and_grid_limits():
         rac.auto_plan(1, 4, 3, 64, 64, 0, 0)
 
 
-def bwd(fused=True, **kw):
+def bwd(fused=True, pairing=None, **kw):
     a = dict(q=Q, k=K, v=V, out=O, lse=L, do=ctypes.c_void_p(P * 6), dq=ctypes.c_void_p(P * 7),
              dk=ctypes.c_void_p(P * 8), dv=ctypes.c_void_p(P * 9), delta=ctypes.c_void_p(P * 10),
              B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
     a.update(kw)
     args = [a[x] for x in ("q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "delta", "B",
                            "Hq", "Hkv", "N", "D")]
+    if pairing is not None:
+        return rac.lib().attn_rope_causal_bwd_ex(*args, a["base"], pairing, a["dtype"], None)
     if fused:
         return rac.lib().attn_rope_causal_bwd(*args, a["base"], a["dtype"], None)
     return rac.lib().attn_causal_bwd(*args, a["dtype"], None)
@@ -303,13 +305,30 @@ BAD_BWD = BAD[:10]
 def test_backward_rejects_bad_arguments(kw, code):
     assert bwd(True, **kw) == code
     assert bwd(False, **kw) == code
+    assert bwd(pairing=0, **kw) == code
+    assert bwd(pairing=1, **kw) == code
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "delta"])
 def test_backward_requires_every_pointer(name):
     assert bwd(True, **{name: None}) == rac.RAC_ERR_ARG
     assert bwd(False, **{name: None}) == rac.RAC_ERR_ARG
+    assert bwd(pairing=1, **{name: None}) == rac.RAC_ERR_ARG
     assert bwd(True, **{name: ctypes.c_void_p(P * 11 + 8)}) == rac.RAC_ERR_ALIGN
+    assert bwd(pairing=1, **{name: ctypes.c_void_p(P * 11 + 8)}) == rac.RAC_ERR_ALIGN
+
+
+def test_backward_pairing_rules():
+    for pairing in (-1, 2, 7):
+        assert bwd(pairing=pairing) == rac.RAC_ERR_ARG
+        assert "pairing" in rac.last_error()
+    # the half-split backward runs through the streaming pass, whose grid
+    # holds B * (Hq + Hkv) <= 524280 slabs
+    assert bwd(pairing=1, B=65535, Hq=8, Hkv=8) == rac.RAC_ERR_ARG
+    assert "524280" in rac.last_error()
+    assert bwd(pairing=1, dq=ctypes.c_void_p(P * 1 + 64)) == rac.RAC_ERR_ARG  # dq over q
+    assert bwd(pairing=1, base=0.0) == rac.RAC_ERR_ARG
+    assert bwd(pairing=1, B=0) == rac.RAC_OK and bwd(pairing=0, B=0) == rac.RAC_OK
 
 
 def test_backward_overlap_and_empty_rules():
@@ -322,15 +341,24 @@ def test_backward_overlap_and_empty_rules():
     assert bwd(False, B=0) == rac.RAC_OK
 
 
-def test_rope_prerotate_bwd_argument_rules():
-    f = rac.lib().rope_prerotate_bwd
+@pytest.mark.parametrize("pairing", [None, 0, 1])
+def test_rope_prerotate_bwd_argument_rules(pairing):
+    if pairing is None:
+        f = rac.lib().rope_prerotate_bwd
+    else:
+        def f(*a):
+            return rac.lib().rope_prerotate_bwd_ex(*a[:10], pairing, *a[10:])
     assert f(Q, K, None, L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, ctypes.c_void_p(P + 16), L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, ctypes.c_void_p(P * 3 + 8), L, 1, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ALIGN
     assert f(Q, K, O, L, 1, 4, 2, 64, 96, 1e4, 0, None) == rac.RAC_ERR_UNSUPPORTED
     assert f(Q, K, O, L, 1, 4, 2, 64, 64, -1.0, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, O, L, 1, 4, 3, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
+    assert f(Q, K, O, L, 65535, 8, 8, 64, 64, 1e4, 0, None) == rac.RAC_ERR_ARG
     assert f(Q, K, O, L, 0, 4, 2, 64, 64, 1e4, 0, None) == rac.RAC_OK
+    if pairing is not None:
+        assert rac.lib().rope_prerotate_bwd_ex(Q, K, O, L, 1, 4, 2, 64, 64, 1e4, 5, 0,
+                                               None) == rac.RAC_ERR_ARG
 
 
 def fused_ex(pairing=1, **kw):

@@ -2,7 +2,8 @@
 against the fp64 oracle's gradients on the same seeded inputs.
 
 Cases: the fused backward (attn_rope_causal_bwd) and the pre-rotation path's
-backward (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd) on small shapes
+backward (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd), with adjacent
+and with half-split RoPE pairs (the _ex entry points), on small shapes
 spanning several tiles with ragged tails, GQA ratios 1-8, D = 64 and 128,
 bf16 and fp16; the inverse rotation pass on its own; determinism; and one key/
 value group of the Llama-3-8B-shaped layer at full length (N = 2048 and 8192)
@@ -198,6 +199,112 @@ def test_full_length_one_group(name, key):
     assert_grad(to_f64(dv[:, g:g + 1]), rdv, "%s dv" % name)
 
 
+# ---- the half-split pairing (i, i + D/2) ----------------------------------
+
+def _case_half(B, Hq, Hkv, N, D, dt, base, key):
+    q, k, v = inputs.qkv(B, Hq, Hkv, N, D, dt, key=key)
+    do = inputs.draw((B, Hq, N, D), dt, key, 3)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half")
+    return (q, k, v, do), (qd, kd, vd, dod, o, lse)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+@pytest.mark.parametrize("path", ["fused", "prerotate"])
+def test_half_split_backward_matches_oracle(shape, path):
+    """The gradients through the half-split pairing's RoPE against the
+    oracle's (its inverse turn of pairs (i, i + D/2)), both oracle variants."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    print("half-split backward %s %s" % (path, _id(shape)), flush=True)
+    (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case_half(B, Hq, Hkv, N, D, dt, base,
+                                                          (411, N, D))
+    if path == "fused":
+        dq, dk, dv, delta = rac.attn_rope_causal_bwd_ex(qd, kd, vd, o, lse, dod, base, "half")
+    else:
+        dq, dk, dv, delta = rac.prerotate_path_bwd(qd, kd, vd, o, lse, dod, base, "half")
+    torch.cuda.synchronize()
+    for variant in ("rounded", "exact"):
+        rdq, rdk, rdv, rdelta, _ = oracle.rope_attention_bwd(
+            inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), dt, base, variant,
+            "half")
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad(to_f64(got), ref, "half %s %s vs %s oracle" % (path, name, variant))
+        assert_grad(delta.cpu().double().numpy(), rdelta, "half %s delta" % path)
+
+
+@pytest.mark.parametrize("shape", SHAPES[:4] + SHAPES[6:], ids=_id)
+def test_half_split_backward_paths_agree_bit_for_bit(shape, bwd_shape):
+    """The fused half-split backward is the pre-rotation path's three calls
+    (the same passes and kernels in the same order), so every output is
+    bit for bit the same, and it is deterministic; under every key-parallel
+    workgroup shape."""
+    B, Hq, Hkv, N, D, dt, base = shape
+    _, (qd, kd, vd, dod, o, lse) = _case_half(B, Hq, Hkv, N, D, dt, base, (412, N, D))
+    f1 = rac.attn_rope_causal_bwd_ex(qd, kd, vd, o, lse, dod, base, "half")
+    f2 = rac.attn_rope_causal_bwd_ex(qd, kd, vd, o, lse, dod, base, "half")
+    p = rac.prerotate_path_bwd(qd, kd, vd, o, lse, dod, base, "half")
+    a = rac.attn_rope_causal_bwd_ex(qd, kd, vd, o, lse, dod, base, "adjacent")
+    b = rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base)
+    torch.cuda.synchronize()
+    for x, y, z, name in zip(f1, f2, p, ("dq", "dk", "dv", "delta")):
+        assert torch.equal(x, y) and torch.equal(x, z), name
+    for x, y in zip(a, b):  # the _ex entry with adjacent pairs is the plain one
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 300, 128, "bf16", 500000.0),
+                                   (2, 2, 2, 4096, 64, "fp16", 10000.0)], ids=_id)
+def test_rope_prerotate_bwd_ex_half_is_the_inverse_rotation(shape):
+    B, Hq, Hkv, N, D, dt, base = shape
+    gq = inputs.draw((B, Hq, N, D), dt, (413, N), 0)
+    gk = inputs.draw((B, Hkv, N, D), dt, (413, N), 1)
+    dq, dk = rac.rope_prerotate_bwd_ex(gq.to(DEV), gk.to(DEV), base, "half")
+    g2 = gq.to(DEV).clone()
+    rac.rope_prerotate_bwd_ex(g2, gk.to(DEV), base, "half", dq=g2,
+                              dk=torch.empty_like(gk, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(g2, dq)  # in place
+    neg = -np.arange(N)
+    for src, got in ((gq, dq), (gk, dk)):
+        y = oracle.rope(oracle.decode(inputs.bits(src), dt), neg, base, "half")
+        ref = oracle.encode(y, dt)
+        g = bits(got)
+        exact = float(np.mean(g == ref))
+        assert exact >= 0.999, "bit-exact fraction %.5f" % exact
+        x = oracle.decode(inputs.bits(src), dt)
+        h = D // 2
+        pair = np.abs(x[..., :h]) + np.abs(x[..., h:])
+        pair = np.concatenate([pair, pair], axis=-1)
+        gv = oracle.decode(g, dt)
+        spacing = np.spacing(np.abs(gv).astype(np.float16 if dt == "fp16" else np.float32))
+        ulp = spacing.astype(np.float64) * (65536.0 if dt == "bf16" else 1.0)
+        assert np.all(np.abs(gv - y) <= ulp + 8 * 2.0 ** -24 * pair)
+
+
+def test_half_split_backward_full_length_one_group():
+    """The Llama-3-8B-shaped layer at N = 2048 with the half-split pairing
+    (the layout its checkpoints use), one key/value group against the
+    oracle, as test_full_length_one_group."""
+    name, key = "llama3_8b_gqa_n2048", 414
+    w = inputs.WORKLOADS[name]
+    B, Hq, Hkv, N, D, dt, base = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"], w["base"]
+    q, k, v = inputs.workload_qkv(name)
+    do = inputs.draw((B, Hq, N, D), dt, (key,), 3)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half")
+    dq, dk, dv, _ = rac.attn_rope_causal_bwd_ex(qd, kd, vd, o, lse, dod, base, "half")
+    torch.cuda.synchronize()
+    group = Hq // Hkv
+    g = 3
+    hs = slice(g * group, (g + 1) * group)
+    rdq, rdk, rdv, _, _ = oracle.rope_attention_bwd(
+        inputs.bits(q)[:, hs], inputs.bits(k)[:, g:g + 1], inputs.bits(v)[:, g:g + 1],
+        inputs.bits(do)[:, hs], dt, base, "rounded", "half")
+    assert_grad(to_f64(dq[:, hs]), rdq, "%s half dq" % name)
+    assert_grad(to_f64(dk[:, g:g + 1]), rdk, "%s half dk" % name)
+    assert_grad(to_f64(dv[:, g:g + 1]), rdv, "%s half dv" % name)
+
+
 def test_empty_inputs():
     for shape in ((0, 2, 8, 64), (1, 2, 0, 64)):
         x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
@@ -205,4 +312,7 @@ def test_empty_inputs():
         dq, dk, dv, delta = rac.attn_rope_causal_bwd(x, x, x, x, l, x, 10000.0)
         dq2, dk2, dv2, _ = rac.attn_causal_bwd(x, x, x, x, l, x)
         a, b = rac.rope_prerotate_bwd(x, x, 10000.0)
+        dq3, _, _, _ = rac.attn_rope_causal_bwd_ex(x, x, x, x, l, x, 10000.0, "half")
+        c, _ = rac.rope_prerotate_bwd_ex(x, x, 10000.0, "half")
         assert dq.shape == shape and dv2.shape == shape and a.shape == shape
+        assert dq3.shape == shape and c.shape == shape

@@ -66,6 +66,8 @@ class Oracle:
         lib.oracle_attn_alibi_rows.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [f64p] * 4 + [ctypes.c_int] * 5 + [f64p] * 5
         lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_alibi_bwd.argtypes = [f64p] * 4 + [ctypes.c_int] * 5 + [f64p] * 6
+        lib.oracle_attn_alibi_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -183,10 +185,12 @@ class Oracle:
         return o, lse, qr, kr
 
 
-    def attention_bwd(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray):
+    def attention_bwd(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                      slopes=None):
         """Gradients of the causal attention above, fp64, from the definition.
 
-        q, dout [B, Hq, N, D]; k, v [B, Hkv, N, D]. Returns (dq, dk, dv, lse,
+        q, dout [B, Hq, N, D]; k, v [B, Hkv, N, D]; ``slopes`` (Hq values) adds
+        the ALiBi penalty of attention(..., slopes). Returns (dq, dk, dv, lse,
         delta): the gradients with respect to q, k and v (dk, dv summed over
         the query heads of each GQA group), and per query row L_i and
         Delta_i = sum_j P_ij dP_ij.
@@ -202,34 +206,47 @@ class Oracle:
         lse = np.empty(q.shape[:-1], dtype=np.float64)
         delta = np.empty(q.shape[:-1], dtype=np.float64)
         p = lambda a: _ptr(a, ctypes.c_double)  # noqa: E731
-        rc = self.lib.oracle_attn_bwd(p(q), p(k), p(v), p(dout), B, Hq, Hkv, N, D, p(dq), p(dk),
-                                      p(dv), p(lse), p(delta))
+        if slopes is None:
+            rc = self.lib.oracle_attn_bwd(p(q), p(k), p(v), p(dout), B, Hq, Hkv, N, D, p(dq),
+                                          p(dk), p(dv), p(lse), p(delta))
+        else:
+            sl = np.ascontiguousarray(slopes, dtype=np.float64).reshape(-1)
+            if sl.shape != (Hq,):
+                raise ValueError("slopes must hold one value per query head")
+            rc = self.lib.oracle_attn_alibi_bwd(p(q), p(k), p(v), p(dout), B, Hq, Hkv, N, D,
+                                                p(sl), p(dq), p(dk), p(dv), p(lse), p(delta))
         if rc != 0:
             raise ValueError("oracle_attn_bwd: bad arguments")
         return dq, dk, dv, lse, delta
 
     def rope_attention_bwd(self, q_bits, k_bits, v_bits, do_bits, dtype: str, base: float,
-                           variant: str = "rounded", pairing: str = "adjacent"):
+                           variant: str = "rounded", pairing: str = "adjacent", slopes=None):
         """Gradients of RoPE then causal attention with respect to the
         unrotated q, k and to v, from bf16/fp16 bit patterns.
 
         The attention gradients are taken at the rotated operands (``variant``
         as in rope_attention); RoPE's gradient is its inverse rotation, the
         turn by -p theta_i of the same pairs (``pairing`` as in rope()).
-        Returns (dq, dk, dv, delta, lse).
+        ``base=None`` skips the rotation, ``slopes`` adds the ALiBi penalty
+        (as in rope_attention). Returns (dq, dk, dv, delta, lse).
         """
         q = self.decode(q_bits, dtype)
         k = self.decode(k_bits, dtype)
         v = self.decode(v_bits, dtype)
         do = self.decode(do_bits, dtype)
-        qr = self.rope_bhnd(q, base, pairing)
-        kr = self.rope_bhnd(k, base, pairing)
+        if base is None:
+            qr, kr = q, k
+        else:
+            qr = self.rope_bhnd(q, base, pairing)
+            kr = self.rope_bhnd(k, base, pairing)
         if variant == "rounded":
             qr = self.decode(self.encode(qr, dtype), dtype)
             kr = self.decode(self.encode(kr, dtype), dtype)
         elif variant != "exact":
             raise ValueError("variant must be 'exact' or 'rounded'")
-        dqr, dkr, dv, lse, delta = self.attention_bwd(qr, kr, v, do)
+        dqr, dkr, dv, lse, delta = self.attention_bwd(qr, kr, v, do, slopes)
+        if base is None:
+            return dqr, dkr, dv, delta, lse
         neg = -np.arange(q.shape[-2], dtype=np.int64)
         return (self.rope(dqr, neg, base, pairing), self.rope(dkr, neg, base, pairing), dv, delta,
                 lse)
@@ -283,11 +300,11 @@ def rope_attention(q_bits, k_bits, v_bits, dtype, base, rows=None, variant="roun
                                     slopes)
 
 
-def attention_bwd(q, k, v, dout):
-    return default().attention_bwd(q, k, v, dout)
+def attention_bwd(q, k, v, dout, slopes=None):
+    return default().attention_bwd(q, k, v, dout, slopes)
 
 
 def rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant="rounded",
-                       pairing="adjacent"):
+                       pairing="adjacent", slopes=None):
     return default().rope_attention_bwd(q_bits, k_bits, v_bits, do_bits, dtype, base, variant,
-                                        pairing)
+                                        pairing, slopes)

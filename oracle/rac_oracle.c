@@ -49,7 +49,9 @@
  *   dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - Delta_i) with
  *   Delta_i = sum_j P_ij dP_ij (the softmax Jacobian), dq_i = tau sum_j dS_ij
  *   k_j and dk_j = tau sum_i dS_ij q_i; dk and dv of a key/value head sum
- *   over the query heads that read it. RoPE's gradient is the inverse
+ *   over the query heads that read it. With ALiBi (oracle_attn_alibi_bwd)
+ *   s_ij carries the penalty, which depends on no input, so only P changes.
+ *   RoPE's gradient is the inverse
  *   rotation (turn by -p theta_i), i.e. oracle_rope at negated positions. The
  *   digest's method section describes its own backward as a two-pass
  *   recomputation from the stored L_i; this oracle recomputes everything from
@@ -301,10 +303,17 @@ int oracle_attn_alibi_rows(const double* q, const double* k, const double* v,
 
 /* ---- causal attention, backward ------------------------------------------ */
 
+/* The ALiBi penalty of query head h for query i and key j (0 without
+ * slopes): the term oracle_attn_alibi_rows subtracts from the scaled score. */
+static double alibi_penalty(const double* slopes, int64_t h, int64_t i, int64_t j) {
+    return slopes ? slopes[h] * (double)(i - j) : 0.0;
+}
+
 /* The scores of query row `row` (flattened (b*Hq + h)*N + i) against the
- * visible keys j = 0..i of its key head, s[j] = tau q_i . k_j; returns i. */
+ * visible keys j = 0..i of its key head, s[j] = tau q_i . k_j minus the
+ * ALiBi penalty when slopes are given; returns i. */
 static int64_t row_scores(const double* q, const double* k, int Hq, int Hkv, int N, int D,
-                          int64_t row, double tau, double* s) {
+                          int64_t row, double tau, const double* slopes, double* s) {
     const int group = Hq / Hkv;
     int64_t i = row % N;
     int64_t bh = row / N;
@@ -315,7 +324,7 @@ static int64_t row_scores(const double* q, const double* k, int Hq, int Hkv, int
     for (int64_t j = 0; j <= i; ++j) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d) dot += qi[d] * kb[j * D + d];
-        s[j] = tau * dot;
+        s[j] = tau * dot - alibi_penalty(slopes, h, i, j);
     }
     return i;
 }
@@ -325,10 +334,12 @@ static int64_t row_scores(const double* q, const double* k, int Hq, int Hkv, int
  * log-sum-exp lse and Delta [B,Hq,N]. Three passes, each recomputing the
  * scores: (1) per query row, L_i and Delta_i; (2) per query row, dq_i;
  * (3) per key row j of each key head, dk_j and dv_j over the query rows
- * i >= j of every query head of its group. Returns 0, or -1 on bad
- * arguments. */
-int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
-                    int B, int Hq, int Hkv, int N, int D,
+ * i >= j of every query head of its group. With slopes (one per query
+ * head) the scores carry the ALiBi penalty of oracle_attn_alibi_rows; the
+ * penalty does not depend on q, k or v, so the gradients keep their form
+ * and only P changes. Returns 0, or -1 on bad arguments. */
+static int attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    int B, int Hq, int Hkv, int N, int D, const double* slopes,
                     double* dq, double* dk, double* dv, double* lse, double* delta) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv != 0) return -1;
     const int64_t qrows = (int64_t)B * Hq * N;
@@ -343,7 +354,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
 #pragma omp for schedule(dynamic, 16)
         for (int64_t row = 0; row < qrows; ++row) {
             if (!s) { bad = 1; continue; }
-            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, s);
+            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, slopes, s);
             int64_t bh = row / N;
             int64_t g = (bh % Hq) / group, b = bh / Hq;
             const double* vb = v + (b * Hkv + g) * (int64_t)N * D;
@@ -373,7 +384,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
 #pragma omp for schedule(dynamic, 16)
         for (int64_t row = 0; row < qrows; ++row) {
             if (!s) { bad = 1; continue; }
-            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, s);
+            int64_t i = row_scores(q, k, Hq, Hkv, N, D, row, tau, slopes, s);
             int64_t bh = row / N;
             int64_t g = (bh % Hq) / group, b = bh / Hq;
             const double* kb = k + (b * Hkv + g) * (int64_t)N * D;
@@ -412,7 +423,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
                     dot += qi[d] * kj[d];
                     dp += doi[d] * vj[d];
                 }
-                double p = exp(tau * dot - lse[row]);
+                double p = exp(tau * dot - alibi_penalty(slopes, h, i, j) - lse[row]);
                 double ds = p * (dp - delta[row]);
                 for (int d = 0; d < D; ++d) {
                     dkj[d] += tau * ds * qi[d];
@@ -422,6 +433,20 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
         }
     }
     return 0;
+}
+
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    int B, int Hq, int Hkv, int N, int D,
+                    double* dq, double* dk, double* dv, double* lse, double* delta) {
+    return attn_bwd(q, k, v, dout, B, Hq, Hkv, N, D, NULL, dq, dk, dv, lse, delta);
+}
+
+/* The backward of oracle_attn_alibi_rows (slopes: Hq values, required). */
+int oracle_attn_alibi_bwd(const double* q, const double* k, const double* v, const double* dout,
+                          int B, int Hq, int Hkv, int N, int D, const double* slopes,
+                          double* dq, double* dk, double* dv, double* lse, double* delta) {
+    if (!slopes) return -1;
+    return attn_bwd(q, k, v, dout, B, Hq, Hkv, N, D, slopes, dq, dk, dv, lse, delta);
 }
 
 int oracle_num_threads(void) {

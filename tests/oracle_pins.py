@@ -448,11 +448,12 @@ def pin_attention_bwd_special_cases(orc):
     assert np.max(np.abs(dv0[:, :, 1:])) == 0.0
 
 
-def _rope_attention_bwd_fd(orc, pairing, seed):
+def _rope_attention_bwd_fd(orc, pairing, seed, slopes=None, base=10000.0):
     # gradients with respect to the unrotated q and k (the inverse rotation),
-    # against central differences of the RoPE-then-attention forward
+    # against central differences of the RoPE-then-attention forward (with
+    # the ALiBi penalty when slopes are given, without RoPE when base is None)
     rng = _rng(seed)
-    B, Hq, Hkv, N, D, base = 1, 2, 1, 12, 8, 10000.0
+    B, Hq, Hkv, N, D = 1, 2, 1, 12, 8
 
     def bf16_bits(shape):
         x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
@@ -462,12 +463,15 @@ def _rope_attention_bwd_fd(orc, pairing, seed):
                                               (B, Hq, N, D)))
     q, k, v, do = (orc.decode(b, "bf16") for b in (qb, kb, vb, dob))
     dq, dk, dv, delta, lse = orc.rope_attention_bwd(qb, kb, vb, dob, "bf16", base,
-                                                    variant="exact", pairing=pairing)
+                                                    variant="exact", pairing=pairing,
+                                                    slopes=slopes)
     pos = np.arange(N)
 
+    def rot(x):
+        return x if base is None else orc.rope(x, pos, base, pairing)
+
     def loss(q_, k_, v_):
-        o, _ = orc.attention(orc.rope(q_, pos, base, pairing), orc.rope(k_, pos, base, pairing),
-                             v_)
+        o, _ = orc.attention(rot(q_), rot(k_), v_, slopes=slopes)
         return float(np.sum(do * o))
 
     h = 1e-6
@@ -489,6 +493,29 @@ def pin_rope_attention_bwd_finite_differences(orc):
 def pin_rope_half_attention_bwd_finite_differences(orc):
     # the half-split pairing's gradient: the inverse turn of pairs (i, i + D/2)
     _rope_attention_bwd_fd(orc, "half", 26)
+
+
+def pin_alibi_attention_bwd_finite_differences(orc):
+    # the ALiBi backward: P carries the penalty (one slope per query head,
+    # steep enough to matter over 12 positions), with and without RoPE
+    slopes = np.array([0.5, 0.125])
+    _rope_attention_bwd_fd(orc, "adjacent", 27, slopes=slopes, base=None)
+    _rope_attention_bwd_fd(orc, "adjacent", 28, slopes=slopes)
+    _rope_attention_bwd_fd(orc, "half", 29, slopes=slopes)
+
+
+def pin_alibi_bwd_zero_slopes_is_plain_backward(orc):
+    rng = _rng(30)
+    q, k, v, do = (rng.standard_normal(s) for s in ((1, 4, 9, 8), (1, 2, 9, 8), (1, 2, 9, 8),
+                                                     (1, 4, 9, 8)))
+    plain = orc.attention_bwd(q, k, v, do)
+    alibi = orc.attention_bwd(q, k, v, do, slopes=np.zeros(4))
+    for a, b in zip(plain, alibi):
+        assert np.array_equal(a, b)
+    # and the forward's L is the backward's
+    _, lse = orc.attention(q, k, v, slopes=np.array([0.3, 0.0, 0.7, 1.5]))
+    assert np.max(np.abs(orc.attention_bwd(q, k, v, do, slopes=np.array([0.3, 0.0, 0.7, 1.5]))[3]
+                         - lse)) < 1e-12
 
 
 # --------------------------------------------------------------------------

@@ -64,6 +64,13 @@ MUTANTS = {
                               "const double distance = (double)(qpos - kpos + 1);"),
     "alibi_gqa_modulo": ("const int64_t kvh = batch * Hkv + qhead / heads_per_kv;",
                          "const int64_t kvh = batch * Hkv + qhead % Hkv;"),
+    "alibi_bwd_penalty_sign": ("return slopes ? slopes[h] * (double)(i - j) : 0.0;",
+                               "return slopes ? slopes[h] * (double)(j - i) : 0.0;"),
+    "alibi_bwd_key_pass_drops_penalty": (
+        "double p = exp(tau * dot - alibi_penalty(slopes, h, i, j) - lse[row]);",
+        "double p = exp(tau * dot - lse[row]);"),
+    "alibi_bwd_scaled_penalty": ("s[j] = tau * dot - alibi_penalty(slopes, h, i, j);",
+                                 "s[j] = tau * (dot - alibi_penalty(slopes, h, i, j));"),
     "alibi_mask_strict": ("for (int64_t kpos = 0; kpos <= qpos; ++kpos) {\n                const double w",
                           "for (int64_t kpos = 0; kpos < qpos; ++kpos) {\n                const double w"),
 }

@@ -407,8 +407,10 @@ def variants(torch, rac, w, qd, kd, vd, ev, reps):
 def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):
     """The backward of both paths on the bench workload, after the timed region
     (not part of `value`): fused (attn_rope_causal_bwd) and pre-rotation
-    (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd), and both again with
-    the half-split RoPE pairing (from the half-split forward's out and lse).
+    (rope_prerotate, attn_causal_bwd, rope_prerotate_bwd), both again with the
+    half-split RoPE pairing (from the half-split forward's out and lse), and
+    the fused backward with the ALiBi penalty (slopes 2^(-8(h+1)/Hq)) after
+    adjacent-pair RoPE.
     TFLOP/s count the algorithmic backward work, 2.5 x the forward's (five N^2
     products: S, dP, dV, dK, dQ); the two-pass kernels rebuild S and dP once
     more."""
@@ -416,12 +418,17 @@ def backward(torch, rac, w, qd, kd, vd, out, lse, ev, reps):
     dout = torch.randn(qd.shape, generator=gen, device=qd.device, dtype=torch.float32).to(qd.dtype)
     base = w["base"]
     out_h, lse_h = rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half")
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w["Hq"]) for h in range(w["Hq"])],
+                          dtype=torch.float32, device=qd.device)
+    out_a, lse_a = rac.attn_alibi_causal_fwd(qd, kd, vd, slopes, rope_base=base)
     fns = {"fused": lambda: rac.attn_rope_causal_bwd(qd, kd, vd, out, lse, dout, base),
            "prerotate": lambda: rac.prerotate_path_bwd(qd, kd, vd, out, lse, dout, base),
            "fused_half": lambda: rac.attn_rope_causal_bwd_ex(qd, kd, vd, out_h, lse_h, dout, base,
                                                              "half"),
            "prerotate_half": lambda: rac.prerotate_path_bwd(qd, kd, vd, out_h, lse_h, dout, base,
-                                                            "half")}
+                                                            "half"),
+           "fused_alibi": lambda: rac.attn_alibi_causal_bwd(qd, kd, vd, out_a, lse_a, dout, slopes,
+                                                            rope_base=base)}
     res = {"flops_per_call": 2.5 * attn_flops(w), "dout": "N(0,1) from a seeded torch generator"}
     for key, fn in fns.items():
         warm(fn, 3, WARM_SECONDS, torch.cuda.synchronize)

@@ -29,8 +29,10 @@
  *   rope_prerotate_bwd_ex the pass, the fused kernel and their gradients with
  *                         the half-split RoPE pairing (i, i + D/2) as an
  *                         alternative.
- *   attn_alibi_causal_fwd causal attention with the ALiBi distance penalty
- *                         after the QK product, alone or with fused RoPE.
+ *   attn_alibi_causal_fwd, attn_alibi_causal_bwd
+ *                         causal attention with the ALiBi distance penalty
+ *                         after the QK product, alone or with fused RoPE, and
+ *                         its gradients.
  *
  * The two paths and the choice between them are the subject of "AttnFuse Makes
  * RoPE a First-Class Attention Compilation Operation" (tdteach paper-news,
@@ -361,6 +363,23 @@ int attn_rope_causal_bwd_ex(const void* q, const void* k, const void* v, const v
 int rope_prerotate_bwd_ex(const void* dq_rot, const void* dk_rot, void* dq, void* dk, int B,
                           int Hq, int Hkv, int N, int D, double rope_base, int pairing, int dtype,
                           void* stream);
+
+/*
+ * Backward of attn_alibi_causal_fwd: the gradients with respect to q, k (the
+ * unrotated ones when a RoPE pairing is given) and v. The penalty depends on
+ * no input, so the gradients keep the form of attn_rope_causal_bwd's and only
+ * the rebuilt probabilities carry it: P = exp(q_i . k_j / sqrt(D) -
+ * slopes[h] (i - j) - lse_i), the penalty entering the base-2 exponent as
+ * slopes[h] log2(e) (j - i) in fp32. Arguments, layouts, scratch and rules
+ * as attn_rope_causal_bwd_ex, plus slopes and pairing as in
+ * attn_alibi_causal_fwd (slopes must not overlap dq, dk, dv or delta); with
+ * RoPE, B * (Hq + Hkv) <= 524280 (the streaming pass forms the rotated
+ * operands; RAC_BWD_ROT has no effect).
+ */
+int attn_alibi_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          float* delta, int B, int Hq, int Hkv, int N, int D, const float* slopes,
+                          double rope_base, int pairing, int dtype, void* stream);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 const char* rac_last_error(void);

@@ -39,7 +39,7 @@ EXPORTED = ("attn_rope_causal_fwd", "rope_prerotate", "attn_causal_fwd", "rope_p
             "rope_prerotate_ex", "attn_rope_causal_fwd_ex", "attn_alibi_causal_fwd",
             "rac_last_error", "rac_release_tables", "rac_time_next_kernel",
             "attn_rope_causal_fwd_noalloc", "rac_stream_copy", "attn_rope_causal_bwd_ex",
-            "rope_prerotate_bwd_ex")
+            "rope_prerotate_bwd_ex", "attn_alibi_causal_bwd")
 RAC_NOALLOC_MAX_N = 32768
 RAC_PAIR_ADJACENT, RAC_PAIR_HALF, RAC_ROPE_NONE = 0, 1, 2
 PAIRINGS = {"adjacent": RAC_PAIR_ADJACENT, "half": RAC_PAIR_HALF, "none": RAC_ROPE_NONE}
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.attn_rope_causal_bwd_ex.restype = i
     L.rope_prerotate_bwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp]
     L.rope_prerotate_bwd_ex.restype = i
+    L.attn_alibi_causal_bwd.argtypes = [vp] * 10 + [i] * 5 + [vp, d, i, i, vp]
+    L.attn_alibi_causal_bwd.restype = i
     L.rope_prerotate_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp]
     L.rope_prerotate_ex.restype = i
     L.attn_rope_causal_fwd_ex.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, d, i, i, vp]
@@ -424,6 +426,23 @@ def attn_rope_causal_bwd_ex(q, k, v, out, lse, dout, rope_base: float, pairing="
                                            B, Hq, Hkv, N, D, float(rope_base), _pairing(pairing),
                                            dt, _stream(q.device))
     check(rc, "attn_rope_causal_bwd_ex")
+    return dq, dk, dv, delta
+
+
+def attn_alibi_causal_bwd(q, k, v, out, lse, dout, slopes, rope_base=None, pairing="adjacent"):
+    """Backward of attn_alibi_causal_fwd (same slopes, rope_base and pairing). Returns
+    (dq, dk, dv, delta)."""
+    (B, Hq, Hkv, N, D, dt), (dq, dk, dv, delta) = _bwd_tensors(q, k, v, out, lse, dout)
+    if slopes.shape != (Hq,) or slopes.dtype != torch.float32 or not slopes.is_contiguous() \
+            or slopes.device != q.device:
+        raise ValueError("slopes must be a contiguous fp32 [Hq] tensor on q's device")
+    pr = RAC_ROPE_NONE if rope_base is None else _pairing(pairing)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_alibi_causal_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                         B, Hq, Hkv, N, D, _ptr(slopes),
+                                         float(rope_base or 0.0), pr, dt, _stream(q.device))
+    check(rc, "attn_alibi_causal_bwd")
     return dq, dk, dv, delta
 
 

@@ -287,15 +287,20 @@ struct Wave {
 // column = query row `row`, element j = key key0 + 8(j/4) + 4hh + j%4), with
 // P = 2^(s * scale_log2 - l2) rebuilt from the forward's log-sum-exp. MASK:
 // keys after the row get P = 0 (only blocks on the diagonal need it; keys
-// past the sequence end are after every row).
-template <bool MASK>
+// past the sequence end are after every row). ALIBI: the exponent also
+// carries the penalty, sl2 (key - row) in base-2 units (sl2 = the head's
+// slope times log2 e).
+template <bool MASK, bool ALIBI>
 __device__ __forceinline__ f32x16 ds_block(const f32x16& s, const f32x16& dp, float scale_log2,
-                                           float l2, float dl, int key0, int hh, int row) {
+                                           float l2, float dl, int key0, int hh, int row,
+                                           float sl2) {
     f32x16 ds;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, -l2));
-        if (MASK && key0 + 8 * (j >> 2) + 4 * hh + (j & 3) > row) p = 0.f;
+        const int key = key0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        const float off = ALIBI ? __builtin_fmaf(sl2, (float)(key - row), -l2) : -l2;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], scale_log2, off));
+        if (MASK && key > row) p = 0.f;
         ds[j] = p * (dp[j] - dl);
     }
     return ds;
@@ -306,10 +311,12 @@ __device__ __forceinline__ f32x16 ds_block(const f32x16& s, const f32x16& dp, fl
 // r0 + 8(j/4) + 4hh + j%4 of the tile, whose base-2 L and Delta sit in
 // rl[row] and rl[BT + row]); P = 2^(s * scale_log2 - L). MASK: query rows
 // before the key, or past the sequence end (q_first + row >= N), get P = 0.
-template <bool MASK, bool DK>
+// q_first: the block's first query row. ALIBI: the exponent also carries the
+// penalty sl2 (key - query row), as in ds_block.
+template <bool MASK, bool DK, bool ALIBI>
 __device__ __forceinline__ void kv_p_block(f32x16& x, const f32x16& dp, const float* rl,
                                            int q_first, int r0, int hh, int key, int N,
-                                           float scale_log2) {
+                                           float scale_log2, float sl2) {
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
         const int r = r0 + 8 * gq + 4 * hh;  // the lane's 4 query rows in the tile
@@ -319,9 +326,10 @@ __device__ __forceinline__ void kv_p_block(f32x16& x, const f32x16& dp, const fl
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int j = 4 * gq + jj;
-            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, -lq[jj]));
+            const int qrow = q_first + 8 * gq + 4 * hh + jj;
+            const float off = ALIBI ? __builtin_fmaf(sl2, (float)(key - qrow), -lq[jj]) : -lq[jj];
+            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, off));
             if (MASK) {
-                const int qrow = q_first + 8 * gq + 4 * hh + jj;
                 if (qrow < key || qrow >= N) pj = 0.f;
             }
             x[j] = DK ? pj * (dp[j] - dq4[jj]) : pj;  // dS or P
@@ -349,10 +357,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    float* __restrict__ delta, const float* __restrict__ table, int Hq, int Hkv, int N,
-    int n_qtiles, float scale_log2, float scale) {
-    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
-    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
+    float* __restrict__ delta, const float* __restrict__ table,
+    const float* __restrict__ slopes, int Hq, int Hkv, int N, int n_qtiles, float scale_log2,
+    float scale) {
+    constexpr bool ALIBI = (RM & MOD_ALIBI) != 0;           // distance penalty on the scores
+    constexpr int ROT = RM & ~MOD_ALIBI;
+    constexpr bool ROPE = ROT == ROT_QK;                     // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || ROT == ROT_QK_OUT;    // turn dq, dk back
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 4> S;
     constexpr int TILE = BT * D;
@@ -368,6 +379,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const int g = h / (Hq / Hkv);
     const int qw0 = qt * BR + 32 * wave;
     const int row = qw0 + n;
+    const float sl2 = ALIBI ? slopes[h] * LOG2E : 0.f;
     const int64_t qhead = ((int64_t)b * Hq + h) * N;
     const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
     const uint16_t* kbase = k + kvhead * D;
@@ -423,8 +435,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
             f32x16 s = W::score(Ks, 32 * kb, qf, n, hh);
             const f32x16 dp = W::score(Vs, 32 * kb, dof, n, hh);
             // only tiles on the diagonal mask (a wave-uniform branch)
-            const f32x16 ds = diag ? ds_block<true>(s, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row)
-                                   : ds_block<false>(s, dp, scale_log2, l2, dl, 0, 0, 0);
+            const f32x16 ds =
+                diag ? ds_block<true, ALIBI>(s, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row, sl2)
+                     : ds_block<false, ALIBI>(s, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row,
+                                              sl2);
             u32x4 y[2];
             W::pack(ds, y);
             W::pv(acc, Ks, 32 * kb, y, lane);
@@ -453,10 +467,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    float* __restrict__ delta, const float* __restrict__ table, int Hq, int Hkv, int N,
-    int n_qtiles, float scale_log2, float scale) {
-    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
-    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
+    float* __restrict__ delta, const float* __restrict__ table,
+    const float* __restrict__ slopes, int Hq, int Hkv, int N, int n_qtiles, float scale_log2,
+    float scale) {
+    constexpr bool ALIBI = (RM & MOD_ALIBI) != 0;           // distance penalty on the scores
+    constexpr int ROT = RM & ~MOD_ALIBI;
+    constexpr bool ROPE = ROT == ROT_QK;                     // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || ROT == ROT_QK_OUT;    // turn dq, dk back
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 4> S;
     constexpr int TILE = BT * D;
@@ -473,6 +490,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pair_kernel(
     const int lt = slot < hv ? slot : -1;   // the light tile, if any
     const int b = bh / Hq, h = bh % Hq;
     const int g = h / (Hq / Hkv);
+    const float sl2 = ALIBI ? slopes[h] * LOG2E : 0.f;
     const int64_t qhead = ((int64_t)b * Hq + h) * N;
     const int64_t kvhead = ((int64_t)b * Hkv + g) * N;
     const uint16_t* kbase = k + kvhead * D;
@@ -562,8 +580,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pair_kernel(
             const f32x16 dp = W::score(Vs, 32 * kb, dof, n, hh);
             // only tiles on the diagonal mask (a wave-uniform branch)
             const f32x16 ds = diag
-                ? ds_block<true>(sc, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row)
-                : ds_block<false>(sc, dp, scale_log2, l2, dl, 0, 0, 0);
+                ? ds_block<true, ALIBI>(sc, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row, sl2)
+                : ds_block<false, ALIBI>(sc, dp, scale_log2, l2, dl, k0 + 32 * kb, hh, row, sl2);
             u32x4 y[2];
             W::pack(ds, y);
             W::pv(acc, Ks, 32 * kb, y, lane);
@@ -624,10 +642,13 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, float* __restrict__ part, const float* __restrict__ table, int Hq,
-    int Hkv, int N, int n_ktiles, float scale_log2, float scale) {
-    constexpr bool ROPE = RM == ROT_QK;                      // rotate the loaded q, k
-    constexpr bool ROPE_OUT = ROPE || RM == ROT_QK_OUT;     // turn dq, dk back
+    uint16_t* __restrict__ dv, float* __restrict__ part, const float* __restrict__ table,
+    const float* __restrict__ slopes, int Hq, int Hkv, int N, int n_ktiles, float scale_log2,
+    float scale) {
+    constexpr bool ALIBI = (RM & MOD_ALIBI) != 0;           // distance penalty on the scores
+    constexpr int ROT = RM & ~MOD_ALIBI;
+    constexpr bool ROPE = ROT == ROT_QK;                     // rotate the loaded q, k
+    constexpr bool ROPE_OUT = ROPE || ROT == ROT_QK_OUT;    // turn dq, dk back
     constexpr int KW = 32 * RW;  // keys per workgroup
     typedef Wave<DT, D> W;
     typedef Streamer<DT, D, ROPE, 2 * RW> S;
@@ -703,6 +724,7 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
             if (s + 1 < rounds) start(s + 1);
             if (!live) continue;
             const int q0 = tq * BT;
+            const float sl2 = ALIBI ? slopes[qh] * LOG2E : 0.f;  // the tile's query head
             if (kw0 >= N) continue;           // the wave has no keys
             if (q0 + BT - 1 < kw0) continue;  // every query of the tile precedes the wave's keys
             // masking only where the tile crosses the wave's keys or the
@@ -715,9 +737,11 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
                 f32x16 dp{};  // read only with DK
                 if (DK) dp = W::score(dOs, 32 * qb, vf, n, hh);
                 if (mask)
-                    kv_p_block<true, DK>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N, scale_log2);
+                    kv_p_block<true, DK, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N,
+                                                scale_log2, sl2);
                 else
-                    kv_p_block<false, DK>(x, dp, rl, 0, 32 * qb, hh, 0, 0, scale_log2);
+                    kv_p_block<false, DK, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N,
+                                                 scale_log2, sl2);
                 u32x4 y[2];
                 W::pack(x, y);
                 W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
@@ -838,11 +862,11 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
         (a.dq_shape == BWD_DQ_PAIR || q_units <= 2 * NUM_CUS))
         attn_bwd_dq_pair_kernel<DT, D, RM>
             <<<dim3((unsigned)((n_qtiles + 1) / 2 * (int64_t)a.Hq * a.B)), 512, 0, stream>>>(
-                q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq,
+                q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.slopes, a.Hq,
                 a.Hkv, a.N, n_qtiles, scale_log2, scale);
     else
         attn_bwd_dq_kernel<DT, D, RM><<<dim3((unsigned)q_units), 256, 0, stream>>>(
-            q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.Hq,
+            q, k, v, out, a.lse, dout, static_cast<uint16_t*>(a.dq), a.delta, a.table, a.slopes, a.Hq,
             a.Hkv, a.N, n_qtiles, scale_log2, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -865,11 +889,12 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
                            stream);
         if (e != hipSuccess) return e;
         attn_bwd_dkdv_kernel<DT, D, RM, 2, 2, 2><<<dim3((unsigned)(2 * k_units)), 512, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, dk, dv, part, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            q, k, v, a.lse, dout, a.delta, dk, dv, part, a.table, a.slopes, a.Hq, a.Hkv, a.N, n_ktiles,
             scale_log2, scale);
         e = hipGetLastError();
         if (e == hipSuccess) {
-            kv_reduce_kernel<DT, RM == ROT_QK || RM == ROT_QK_OUT><<<dim3((unsigned)((quads + 255) / 256)), 256, 0,
+            constexpr int ROT = RM & ~MOD_ALIBI;
+            kv_reduce_kernel<DT, ROT == ROT_QK || ROT == ROT_QK_OUT><<<dim3((unsigned)((quads + 255) / 256)), 256, 0,
                                                  stream>>>(part, dk, dv, a.table, kv_rows, a.N,
                                                            a.D, scale);
             e = hipGetLastError();
@@ -879,16 +904,16 @@ static hipError_t launch_typed(const BwdArgs& a, hipStream_t stream) {
     }
     if (rw == 4)
         attn_bwd_dkdv_kernel<DT, D, RM, 4, 1, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.slopes, a.Hq, a.Hkv, a.N, n_ktiles,
             scale_log2, scale);
     else if (a.shape == BWD_SHAPE_K64X2 || a.shape == BWD_SHAPE_K64X2H ||
              (a.shape != BWD_SHAPE_K64 && k_units <= 2 * NUM_CUS))
         attn_bwd_dkdv_kernel<DT, D, RM, 2, 2, 1><<<dim3((unsigned)k_units), 512, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.slopes, a.Hq, a.Hkv, a.N, n_ktiles,
             scale_log2, scale);
     else
         attn_bwd_dkdv_kernel<DT, D, RM, 2, 1, 1><<<dim3((unsigned)k_units), 256, 0, stream>>>(
-            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.Hq, a.Hkv, a.N, n_ktiles,
+            q, k, v, a.lse, dout, a.delta, dk, dv, nullptr, a.table, a.slopes, a.Hq, a.Hkv, a.N, n_ktiles,
             scale_log2, scale);
     return hipGetLastError();
 }
@@ -900,14 +925,21 @@ static hipError_t launch_dt(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace bwd
 
+template <int DT>
+static hipError_t launch_rot(const BwdArgs& a, int rot, hipStream_t stream) {
+    if (a.slopes != nullptr) {  // ALiBi: on operands rotated beforehand, or none
+        if (rot == ROT_QK_OUT) return bwd::launch_dt<DT, ROT_QK_OUT | MOD_ALIBI>(a, stream);
+        if (rot == ROT_NONE) return bwd::launch_dt<DT, ROT_NONE | MOD_ALIBI>(a, stream);
+        return hipErrorInvalidValue;
+    }
+    return rot == ROT_QK       ? bwd::launch_dt<DT, ROT_QK>(a, stream)
+           : rot == ROT_QK_OUT ? bwd::launch_dt<DT, ROT_QK_OUT>(a, stream)
+                               : bwd::launch_dt<DT, ROT_NONE>(a, stream);
+}
+
 hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream) {
-    if (a.dtype == DT_BF16)
-        return rot == ROT_QK       ? bwd::launch_dt<DT_BF16, ROT_QK>(a, stream)
-               : rot == ROT_QK_OUT ? bwd::launch_dt<DT_BF16, ROT_QK_OUT>(a, stream)
-                                   : bwd::launch_dt<DT_BF16, ROT_NONE>(a, stream);
-    return rot == ROT_QK       ? bwd::launch_dt<DT_FP16, ROT_QK>(a, stream)
-           : rot == ROT_QK_OUT ? bwd::launch_dt<DT_FP16, ROT_QK_OUT>(a, stream)
-                               : bwd::launch_dt<DT_FP16, ROT_NONE>(a, stream);
+    return a.dtype == DT_BF16 ? launch_rot<DT_BF16>(a, rot, stream)
+                              : launch_rot<DT_FP16>(a, rot, stream);
 }
 
 }  // namespace rac

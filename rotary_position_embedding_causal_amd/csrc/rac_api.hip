@@ -382,10 +382,14 @@ hipError_t untimed(Launch launch) {
     return e;
 }
 
+// The backward entry points: rot ROT_QK (RoPE fused; half: the half-split
+// pairing) or ROT_NONE; alibi: slopes carry the ALiBi penalty (validated
+// here: non-null, aligned, clear of the outputs).
 int attn_bwd_common(const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
                     int B, int Hq, int Hkv, int N, int D, double rope_base, int dtype, int rot,
-                    void* stream, const char* what, bool half = false) {
+                    void* stream, const char* what, bool half = false, bool alibi = false,
+                    const float* slopes = nullptr) {
     bool empty = false;
     int rc = check_shape(B, Hq, Hkv, N, D, dtype, &empty);
     if (rc != RAC_OK) return rc;
@@ -393,13 +397,26 @@ int attn_bwd_common(const void* q, const void* k, const void* v, const void* out
     const bool pass_fits = (int64_t)B * (Hq + (int64_t)Hkv) <= 8LL * 65535;
     if (half && !pass_fits)
         return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280 for the half-split pairing");
+    if (alibi && rot == rac::ROT_QK && !pass_fits)
+        return fail(RAC_ERR_ARG, "B*(Hq+Hkv) must be <= 524280 for RoPE with ALiBi");
     if (empty) return ok();
     rac::BwdArgs a{q, k, v, out, lse, dout, dq, dk, dv, delta, nullptr, B, Hq, Hkv, N, D, dtype,
                    bwd_shape_from_env(), bwd_dq_from_env()};
     if ((rc = check_bwd_ptrs(a)) != RAC_OK) return rc;
+    if (alibi) {
+        if (!slopes) return fail(RAC_ERR_ARG, "slopes must be non-null");
+        if (reinterpret_cast<uintptr_t>(slopes) % 4 != 0)
+            return fail(RAC_ERR_ALIGN, "slopes must be 4-byte aligned");
+        const int64_t sb = (int64_t)Hq * 4;
+        const int64_t qb = (int64_t)B * Hq * N * D * 2, kb = (int64_t)B * Hkv * N * D * 2;
+        if (overlap(slopes, sb, dq, qb) || overlap(slopes, sb, dk, kb) ||
+            overlap(slopes, sb, dv, kb) || overlap(slopes, sb, delta, (int64_t)B * Hq * N * 4))
+            return fail(RAC_ERR_ARG, "slopes must not overlap dq, dk, dv or delta");
+        a.slopes = slopes;
+    }
     if (rot == rac::ROT_QK && (rc = get_table(D, rope_base, N, &a.table)) != RAC_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (rot != rac::ROT_QK || (!half && bwd_rotation_in_kernel()))
+    if (rot != rac::ROT_QK || (!half && !alibi && bwd_rotation_in_kernel()))
         return hip_status(rac::launch_attn_bwd(a, rot, st), what);
     // Both passes read every query and key tile many times (each key tile once
     // per query tile that sees it, and the reverse), so the rotated operands
@@ -639,6 +656,19 @@ int attn_causal_bwd(const void* q, const void* k, const void* v, const void* out
                     float* delta, int B, int Hq, int Hkv, int N, int D, int dtype, void* stream) {
     return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D, 1.0,
                            dtype, rac::ROT_NONE, stream, "attn_causal_bwd launch");
+}
+
+int attn_alibi_causal_bwd(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          float* delta, int B, int Hq, int Hkv, int N, int D, const float* slopes,
+                          double rope_base, int pairing, int dtype, void* stream) {
+    const bool rope = pairing != RAC_ROPE_NONE;
+    int rc = RAC_OK;
+    if (rope && (rc = check_pairing(pairing)) != RAC_OK) return rc;
+    return attn_bwd_common(q, k, v, out, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                           rope ? rope_base : 1.0, dtype, rope ? rac::ROT_QK : rac::ROT_NONE,
+                           stream, "attn_alibi_causal_bwd launch", pairing == RAC_PAIR_HALF, true,
+                           slopes);
 }
 
 int rope_prerotate_k(const void* k, void* k_rot, int B, int Hkv, int N, int D, double rope_base,

@@ -71,6 +71,7 @@ struct BwdArgs {
     int dtype;
     int shape = 0;       // BWD_SHAPE_* (the dK/dV pass)
     int dq_shape = 0;    // BWD_DQ_* (the dQ pass)
+    const float* slopes = nullptr;  // ALiBi: one slope per query head, or none
 };
 
 // dK/dV pass workgroup shapes: automatic, 128 keys (8 waves), 64 keys (4
@@ -82,7 +83,8 @@ enum { BWD_DQ_AUTO = 0, BWD_DQ_TILE = 1, BWD_DQ_PAIR = 2 };
 // Causal attention backward (ROT_QK: RoPE fused, gradients with respect to
 // the unrotated q and k; ROT_QK_OUT: q and k already rotated, gradients with
 // respect to the unrotated ones; ROT_NONE: inputs already rotated, gradients
-// with respect to them).
+// with respect to them). With a.slopes the scores carry the ALiBi penalty
+// (ROT_NONE and ROT_QK_OUT only).
 hipError_t launch_attn_bwd(const BwdArgs& a, int rot, hipStream_t stream);
 
 // q_rot = RoPE(q), k_rot = RoPE(k).

@@ -94,11 +94,21 @@ G_MAXABS_REL = 2e-2
 G_RELL2 = 1e-2
 
 
-def assert_grad(got, ref, what=""):
+# Peaked softmax (a steep ALiBi slope): dS = P (dP - Delta) cancels where a
+# row's P is nearly one-hot, and Delta = rowsum(dO * O) is formed from the
+# stored, rounded O, as the two-pass backward defines it, so O's rounding
+# reaches dq and dk amplified (fp16's 8x finer rounding cuts the error 8x).
+# rel-L2 bound for dq, dk in bf16 when the penalty is at least one unit of
+# score per position.
+G_RELL2_PEAKED = 2.5e-2
+
+
+def assert_grad(got, ref, what="", rel_bound=G_RELL2):
     d = got - ref
     scale = max(1.0, float(np.max(np.abs(ref))))
     mx = float(np.max(np.abs(d)))
     rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
-    assert mx <= G_MAXABS_REL * scale and (rel <= G_RELL2 or np.linalg.norm(ref) < 1e-30), \
-        "%s: max|d|=%.3e (bound %.3e) relL2=%.3e" % (what, mx, G_MAXABS_REL * scale, rel)
+    assert mx <= G_MAXABS_REL * scale and (rel <= rel_bound or np.linalg.norm(ref) < 1e-30), \
+        "%s: max|d|=%.3e (bound %.3e) relL2=%.3e (bound %.1e)" % (
+            what, mx, G_MAXABS_REL * scale, rel, rel_bound)
     return mx, rel

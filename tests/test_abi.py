@@ -453,6 +453,43 @@ def test_alibi_argument_rules():
     assert rac.last_error() == ""
 
 
+def alibi_bwd(pairing=2, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, do=ctypes.c_void_p(P * 6), dq=ctypes.c_void_p(P * 7),
+             dk=ctypes.c_void_p(P * 8), dv=ctypes.c_void_p(P * 9), delta=ctypes.c_void_p(P * 10),
+             slopes=ctypes.c_void_p(P * 11), B=1, Hq=4, Hkv=2, N=64, D=64, base=1e4, dtype=0)
+    a.update(kw)
+    args = [a[x] for x in ("q", "k", "v", "out", "lse", "do", "dq", "dk", "dv", "delta", "B",
+                           "Hq", "Hkv", "N", "D", "slopes", "base")]
+    return rac.lib().attn_alibi_causal_bwd(*args, pairing, a["dtype"], None)
+
+
+@pytest.mark.parametrize("pairing", [0, 1, 2])
+@pytest.mark.parametrize("kw,code", BAD_BWD, ids=[str(b[0]) for b in BAD_BWD])
+def test_alibi_backward_rejects_bad_arguments(kw, code, pairing):
+    assert alibi_bwd(pairing, **kw) == code
+
+
+def test_alibi_backward_argument_rules():
+    assert alibi_bwd(slopes=None) == rac.RAC_ERR_ARG
+    assert "slopes" in rac.last_error()
+    assert alibi_bwd(slopes=ctypes.c_void_p(P * 11 + 2)) == rac.RAC_ERR_ALIGN
+    assert alibi_bwd(slopes=ctypes.c_void_p(P * 7 + 64)) == rac.RAC_ERR_ARG    # inside dq
+    assert alibi_bwd(slopes=ctypes.c_void_p(P * 10 + 16)) == rac.RAC_ERR_ARG   # inside delta
+    assert alibi_bwd(dq=ctypes.c_void_p(P * 1 + 64)) == rac.RAC_ERR_ARG        # dq over q
+    assert alibi_bwd(do=None) == rac.RAC_ERR_ARG
+    assert alibi_bwd(3) == rac.RAC_ERR_ARG and "pairing" in rac.last_error()
+    assert alibi_bwd(-1) == rac.RAC_ERR_ARG
+    assert alibi_bwd(0, base=0.0) == rac.RAC_ERR_ARG and "rope_base" in rac.last_error()
+    assert alibi_bwd(1, base=float("nan")) == rac.RAC_ERR_ARG
+    # with RoPE the streaming pass forms the rotated operands: its grid
+    for pairing in (0, 1):
+        assert alibi_bwd(pairing, B=65535, Hq=8, Hkv=8) == rac.RAC_ERR_ARG
+        assert "524280" in rac.last_error()
+    assert alibi_bwd(2, base=0.0, B=0) == rac.RAC_OK
+    assert alibi_bwd(2, N=0, slopes=None, q=None) == rac.RAC_OK
+    assert rac.last_error() == ""
+
+
 def test_kernel_timer_arguments():
     """rac_time_next_kernel stores or clears an event pair (no HIP call); a
     lone event is an argument error."""

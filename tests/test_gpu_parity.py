@@ -430,11 +430,13 @@ def test_empty_inputs():
 # ---------------------------------------------------------------------------
 
 # every sweep point: the launch shape changes with the size (for the D = 64
-# MHA sweep the pair launch at N = 2048, 4096 and 8192, the tile launch at
-# 1024, 6144 and from 16384)
+# MHA sweep the pair launch at N = 1536 - 4096 and 8192, the tile launch at
+# 1024, 6144 and from 16384; for D = 128 MHA the pair launch also at 3072,
+# 1.5 rounds of it)
 FULL = ["llama3_8b_gqa_n2048", "llama3_8b_gqa_b4_n4096", "llama3_8b_gqa_n8192",
-        "mha_d64_fp16_n1024", "mha_d64_fp16_n2048", "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
-        "mha_d64_fp16_n16384", "mha_d64_fp16_n32768",
+        "mha_d64_fp16_n1024", "mha_d64_fp16_n1536", "mha_d64_fp16_n2048", "mha_d64_fp16_n3072",
+        "mha_d64_fp16_n4096", "mha_d64_fp16_n6144", "mha_d64_fp16_n8192",
+        "mha_d64_fp16_n16384", "mha_d64_fp16_n32768", "mha_d128_bf16_n3072",
         # the largest shape of each other crossover family, and its batched rows
         "mha_d128_bf16_n16384", "mha_d128_bf16_b8_n1024", "gqa4_d64_bf16_n16384",
         "llama3_8b_gqa_n16384", "gqa4_d128_fp16_n8192", "gqa8_d128_bf16_n8192"]

@@ -660,7 +660,12 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     const int tid = threadIdx.x;
     const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qg = wave_wg / (2 * RW);   // query group
-    const int wave = wave_wg % (2 * RW);  // wave inside its group
+    // wave inside its group (its role and keys). Waves w and w + 4 of the
+    // workgroup share a SIMD, so with two 4-wave groups the second group's
+    // roles are swapped: every SIMD then runs one dV and one dK wave, instead
+    // of two dK waves (S, dP, dS and dK: 1.5x the matrix work) on two SIMDs.
+    const int wave = (QS == 2 && RW == 2 && (qg & 1)) ? (wave_wg + RW) % (2 * RW)
+                                                      : wave_wg % (2 * RW);
     const bool dk_role = wave >= RW;
     const int lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int bg, slot;

@@ -67,12 +67,22 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-// Position of logical 16-byte chunk c of tile row `row` (XOR swizzle: the
-// score-pattern reads take one chunk column of 16 consecutive rows at once,
-// so rows spread over all chunk positions). Both tiles of a pass use it.
+// Position of logical 16-byte chunk c of tile row `row`: c ^ swz(row). Every
+// streamed tile is read in both patterns, so the swizzle serves both:
+//   * score pattern: 16 lanes read one chunk column of 16 consecutive rows,
+//     so swz must take distinct values over any 16 consecutive rows (with
+//     D = 64 two rows share a 256-byte bank period: over the 8 rows of each
+//     parity);
+//   * transpose (PV) pattern: a 16-lane group reads chunks 4i + {lc, lc + 1}
+//     of 4 consecutive rows 4k .. 4k+3, so the 4 rows must land on disjoint
+//     chunk positions (D = 128: swz's bits 2-3 take the row's low two bits;
+//     D = 64: rows 4k and 4k + 2, of one parity, differ in swz's bit 1).
+// (A swizzle for the score pattern alone, row & 15, left the transpose
+// reads two-way bank-conflicted.)
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3)
+                    : 2 * ((row >> 1) & 1) + 4 * ((row >> 2) & 1) + ((row >> 3) & 1);
 }
 
 constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw (unformatted) 32-bit data

@@ -503,17 +503,21 @@ struct WaveAttn {
                 return;
             }
         }
-        // row maximum: a shallow tree over the lane's 32 scores, then the other
-        // lane half's value (v_permlane32_swap leaves {x[l], x[l^32]} in its
-        // two results)
-        float m8[8];
+        // row maximum over the lane's 32 scores in 16 three-input maxima (four
+        // chains of seven scores, then the chains and the last four scores),
+        // then the other lane half's value (v_permlane32_swap leaves
+        // {x[l], x[l^32]} in its two results)
+        auto sc = [&](int i) { return s[b][i >> 4][i & 15]; };
+        float m4[4];
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int kb = g >> 2, j = 4 * (g & 3);
-            m8[g] = fmaxf(fmaxf(s[b][kb][j], s[b][kb][j + 1]), fmaxf(s[b][kb][j + 2], s[b][kb][j + 3]));
+        for (int g = 0; g < 4; ++g) {
+            float c = fmaxf(fmaxf(sc(7 * g), sc(7 * g + 1)), sc(7 * g + 2));
+            c = fmaxf(fmaxf(c, sc(7 * g + 3)), sc(7 * g + 4));
+            m4[g] = fmaxf(fmaxf(c, sc(7 * g + 5)), sc(7 * g + 6));
         }
-        float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        const float ma = fmaxf(fmaxf(m4[0], m4[1]), sc(28));
+        const float mb = fmaxf(fmaxf(m4[2], m4[3]), sc(29));
+        float mx = fmaxf(fmaxf(fmaxf(ma, mb), sc(30)), sc(31));
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                              false, false);

@@ -13,7 +13,9 @@ Also printed in the same JSON line:
     TFLOP/s from a pair of HIP events that each of its launches in the timed
     region records at the kernel's own start and end (rac.time_next_kernel,
     hipExtLaunchKernel on the launch stream), against the dense bf16 MFMA
-    peak; warm (the timed steps) and cold (after a 512 MiB flush);
+    peak; warm (the timed steps) and cold (after a 512 MiB flush); and
+    against that peak scaled to the GFX clock sampled (amd-smi) while the
+    kernel runs back to back (`frac_at_sclk`);
   * paths: per-kernel times taken the same way (warm, and cold after a
     512 MiB cache flush) and their sums per path, TFLOP/s, % of MFMA peak,
     rope_prerotate GB/s vs 8 TB/s and vs a plain copy of the same bytes
@@ -129,6 +131,77 @@ def warm(fn, calls, min_seconds, sync):
             fn()
         done += max(1, min(calls, 10))
         sync()
+
+
+NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
+
+
+def parse_gfx_clocks(text):
+    """The GFX clocks (MHz) in the JSON that `amd-smi metric -c --json` prints:
+    one value per XCD ("gfx_0" ...) of every GPU listed, leaving out XCDs
+    caught below their lowest clock level (min_clk, else 500 MHz), which are
+    in deep sleep at that instant rather than running slower. Empty if none."""
+    try:
+        data = json.loads(text)
+    except ValueError:
+        return []
+    gpus = data.get("gpu_data", []) if isinstance(data, dict) else data
+    mhz = []
+
+    def value(c, key):
+        v = c.get(key, {})
+        v = v.get("value") if isinstance(v, dict) else v
+        return float(v) if isinstance(v, (int, float)) else None
+
+    for g in gpus if isinstance(gpus, list) else []:
+        clocks = g.get("clock", {}) if isinstance(g, dict) else {}
+        for key, c in sorted(clocks.items()):
+            if key.startswith("gfx_") and isinstance(c, dict):
+                v, lo = value(c, "clk"), value(c, "min_clk")
+                if v is not None and v >= (lo if lo else 500.0):
+                    mhz.append(v)
+    return mhz
+
+
+def gfx_clock_under(fn, sync, seconds=1.0):
+    """Per-XCD GFX clocks while fn runs back to back for about `seconds`: a
+    helper thread samples `amd-smi metric -c --json` (a child process that
+    reads the driver's metrics) while this thread keeps the GPU busy.
+    Returns the median, min and max MHz over all samples and XCDs, or None
+    when amd-smi is unavailable or reports nothing."""
+    import subprocess
+    import threading
+    samples, done = [], threading.Event()
+
+    def sampler():
+        while not done.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            if r.returncode != 0:
+                return
+            samples.append(parse_gfx_clocks(r.stdout))
+            done.wait(0.05)
+
+    warm(fn, 20, 0.1, sync)  # clocks up before the first sample
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and th.is_alive():
+        for _ in range(100):
+            fn()
+        sync()
+    done.set()
+    th.join()
+    mhz = sorted(m for smp in samples for m in smp)
+    if not mhz:
+        return None
+    return {"median_mhz": _median(mhz), "min_mhz": mhz[0], "max_mhz": mhz[-1],
+            "readings": len(mhz), "samples": len(samples),
+            "source": "amd-smi metric -c (per-XCD GFX clock, XCDs in deep sleep left out), "
+                      "sampled while the kernel runs back to back"}
 
 
 def attn_flops(w):
@@ -274,6 +347,9 @@ def main():
     peak = MFMA_PEAK_TFLOPS[w["dtype"]]
     achieved = fl / (t_fused * 1e-3) / 1e12
 
+    # the GFX clock while the roofline kernel runs: its peak at that clock
+    sclk = gfx_clock_under(fused, torch.cuda.synchronize)
+
     # ---- cold-cache kernel times (512 MiB flush before each rep) ----
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -356,6 +432,10 @@ def main():
                      "cold": "median of 20 launches, each after a 512 MiB cache flush"},
         "paths": paths,
     }
+    if sclk is not None:
+        # the published peak scaled to the clock measured under this kernel
+        result["roofline"]["sclk"] = sclk
+        result["roofline"]["frac_at_sclk"] = achieved / (peak * sclk["median_mhz"] / NOMINAL_SCLK_MHZ)
 
     result["variants"] = variants(torch, rac, w, qd, kd, vd, ev, args.steps)
     result["backward"] = backward(torch, rac, w, qd, kd, vd, out_f, lse_f, ev, args.steps)

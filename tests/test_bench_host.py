@@ -63,3 +63,17 @@ def test_crossover_reports_the_winner_when_the_sign_never_changes():
     assert pre["n_star"] is None and pre["winner_if_no_crossing"] == "prerotate"
     fus = bench.locate_crossover(_rows([(2048, -0.3), (4096, -0.01)]), "f", "p")
     assert fus["n_star"] is None and fus["winner_if_no_crossing"] == "fused"
+
+
+def test_gfx_clocks_are_read_per_xcd_from_the_amd_smi_json():
+    text = json.dumps({"gpu_data": [{"gpu": 0, "clock": {
+        "gfx_0": {"clk": {"value": 2170, "unit": "MHz"}, "max_clk": {"value": 2400}},
+        "gfx_1": {"clk": {"value": 2118, "unit": "MHz"}},
+        "mem_0": {"clk": {"value": 2000, "unit": "MHz"}},
+        "gfx_2": {"clk": {"value": "N/A"}},
+        "gfx_3": {"clk": {"value": 95}, "min_clk": {"value": 500}},
+        "gfx_4": {"clk": {"value": 450}}}}]})
+    # gfx_3 and gfx_4 sit below the lowest clock level: asleep, not slow
+    assert bench.parse_gfx_clocks(text) == [2170.0, 2118.0]
+    assert bench.parse_gfx_clocks("not json") == []
+    assert bench.parse_gfx_clocks(json.dumps({"gpu_data": []})) == []

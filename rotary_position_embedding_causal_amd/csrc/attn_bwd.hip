@@ -347,6 +347,19 @@ __device__ __forceinline__ void kv_p_block(f32x16& x, const f32x16& dp, const fl
     }
 }
 
+// dS = P * (dP - Delta) in place for one 32 x 32 score block of the dK/dV
+// pass, from the block's P as kv_p_block<MASK, false, ALIBI> left it (zero
+// where masked): the same product, so the same bits, as kv_p_block with DK.
+__device__ __forceinline__ void kv_ds_from_p(f32x16& x, const f32x16& dp, const float* rl, int r0,
+                                             int hh) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(rl + BT + r0 + 8 * gq + 4 * hh);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) x[4 * gq + jj] = x[4 * gq + jj] * (dp[4 * gq + jj] - dq4[jj]);
+    }
+}
+
 // 1-D work-unit index, XCD-aware order (the hardware deals workgroup ids
 // round-robin over 8 XCDs; consecutive units on one XCD share a head), then
 // (outer, tile) with the heaviest tile first.
@@ -628,12 +641,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pair_kernel(
 // dK/dV pass: one workgroup per (b, key/value head, 32*RW-key tile),
 // heaviest first; it walks the 64-row query tiles at or after its keys for
 // every query head of the group. Its 2*RW waves take two roles on the same
-// keys and the same streamed tiles: waves 0 .. RW-1 accumulate dV (they need
-// only S and P), waves RW .. 2RW-1 accumulate dK (S, dP and dS). Split this
-// way each wave holds one D-wide accumulator and at most two stationary
-// operands, so two waves fit on a SIMD (wave w and w + 4 share one), where a
-// wave holding both accumulators would run alone; S is computed by both
-// roles.
+// keys and the same streamed tiles: waves 0 .. RW-1 accumulate dV (S, P),
+// waves RW .. 2RW-1 accumulate dK (dP, and dS from the P that the dV wave on
+// the same keys hands over through LDS). Split this way each wave holds one
+// D-wide accumulator and one stationary operand, so two waves fit on a SIMD
+// (wave w and w + 4 share one), where a wave holding both accumulators would
+// run alone; and S is computed once.
 // With QS > 1 the workgroup holds QS such groups of 2*RW waves on the same
 // keys: group c takes the query tiles c, c + QS, c + 2QS, ... of the walk,
 // each with its own stream buffers, and at the end the groups' partial dK
@@ -666,6 +679,9 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     // per query group: Q0 dO0 Q1 dO1, and per buffer 64 scaled L and 64 Delta values
     __shared__ __attribute__((aligned(16))) uint16_t smem[QS * 4 * TILE];
     __shared__ __attribute__((aligned(16))) float rows_lds[QS][2][2 * BT];
+    // P of one 32-query block, handed from each dV wave to the dK wave on the
+    // same keys: [query group][key block][4][64 lanes][4], fp32
+    __shared__ __attribute__((aligned(16))) f32x4 p_lds[QS][RW][4][64];
 
     const int tid = threadIdx.x;
     const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -716,11 +732,16 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
 
     // The whole loop of one role (the same barriers in the same order for
     // both, so the workgroup stays in step), compiled separately per role.
+    // Per 32-query block the dV wave computes S and P and hands P to the dK
+    // wave on its keys through LDS; the dK wave computes dP meanwhile and
+    // then dS from that P (so S is computed once per block, by the dV wave).
+    // Every wave passes the same barriers, with or without work.
     auto run = [&](auto dk_tag) {
         constexpr bool DK = decltype(dk_tag)::value;
-        typename W::vec8 kf[W::QCH], vf[W::QCH];
-        W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
-        if (DK) W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
+        typename W::vec8 kf[W::QCH], vf[W::QCH];  // stationary K (dV waves) or V (dK waves)
+        if constexpr (!DK) W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
+        if constexpr (DK) W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
+        f32x4* pex = &p_lds[qg][wave % RW][0][lane];  // this pair's P, this lane's slots
         f32x16 acc[W::DBLK];  // dK^T (DK) or dV^T
 #pragma unroll
         for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
@@ -737,29 +758,53 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
             if (live) st.finish(Qs, rl, true, wave, lane);
             __syncthreads();  // round s complete; the other buffers are no longer read
             if (s + 1 < rounds) start(s + 1);
-            if (!live) continue;
             const int q0 = tq * BT;
-            const float sl2 = ALIBI ? slopes[qh] * LOG2E : 0.f;  // the tile's query head
-            if (kw0 >= N) continue;           // the wave has no keys
-            if (q0 + BT - 1 < kw0) continue;  // every query of the tile precedes the wave's keys
+            const float sl2 = ALIBI && live ? slopes[qh] * LOG2E : 0.f;  // the tile's query head
+            // work unless the group is idle, the wave has no keys or every
+            // query of the tile precedes them (uniform over the wave pair)
+            const bool work = live && kw0 < N && q0 + BT - 1 >= kw0;
             // masking only where the tile crosses the wave's keys or the
             // sequence end (a wave-uniform branch)
             const bool mask = q0 < kw0 + 31 || q0 + BT > N;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                // S (and for dK, dP) for queries q0 + 32qb .. +31 (lane column = key)
-                f32x16 x = W::score(Qs, 32 * qb, kf, n, hh);
-                f32x16 dp{};  // read only with DK
-                if (DK) dp = W::score(dOs, 32 * qb, vf, n, hh);
-                if (mask)
-                    kv_p_block<true, DK, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N,
-                                                scale_log2, sl2);
-                else
-                    kv_p_block<false, DK, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key, N,
-                                                 scale_log2, sl2);
+                // queries q0 + 32qb .. +31 (lane column = key)
+                f32x16 x, dp{};  // dp: dK waves only
                 u32x4 y[2];
-                W::pack(x, y);
-                W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
+                if (work) {
+                    if constexpr (!DK) {
+                        x = W::score(Qs, 32 * qb, kf, n, hh);
+                        if (mask)
+                            kv_p_block<true, false, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh, key,
+                                                           N, scale_log2, sl2);
+                        else
+                            kv_p_block<false, false, ALIBI>(x, dp, rl, q0 + 32 * qb, 32 * qb, hh,
+                                                            key, N, scale_log2, sl2);
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            pex[64 * g4] = f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
+                        W::pack(x, y);
+                    } else {
+                        dp = W::score(dOs, 32 * qb, vf, n, hh);
+                    }
+                }
+                __syncthreads();  // P of this block is in LDS
+                if (work) {
+                    if constexpr (DK) {
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const f32x4 t = pex[64 * g4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[4 * g4 + e] = t[e];
+                        }
+                        kv_ds_from_p(x, dp, rl, 32 * qb, hh);
+                        W::pack(x, y);
+                    }
+                    W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
+                }
+                // the dK wave has read this P before the next block's is written
+                // (after the last block, the next round's barrier does it)
+                if (qb == 0) __syncthreads();
             }
         }
         if constexpr (QS > 1) {

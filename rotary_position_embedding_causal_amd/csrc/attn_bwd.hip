@@ -680,8 +680,14 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
     __shared__ __attribute__((aligned(16))) uint16_t smem[QS * 4 * TILE];
     __shared__ __attribute__((aligned(16))) float rows_lds[QS][2][2 * BT];
     // P of one 32-query block, handed from each dV wave to the dK wave on the
-    // same keys: [query group][key block][4][64 lanes][4], fp32
-    __shared__ __attribute__((aligned(16))) f32x4 p_lds[QS][RW][4][64];
+    // same keys: [block parity][query group][key block][4][64 lanes][4], fp32;
+    // one buffer per block of a tile where LDS allows (then no barrier is
+    // needed before the second block's P is written), else one shared
+    constexpr int STREAM_BYTES = QS * 4 * TILE * 2 + QS * 2 * 2 * BT * 4;
+    constexpr int P_BYTES = QS * RW * 4 * 64 * 16;
+    constexpr int WG_PER_CU = RW * QS == 2 ? 2 : 1;
+    constexpr int PB = WG_PER_CU * (STREAM_BYTES + 2 * P_BYTES) <= 160 * 1024 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) f32x4 p_lds[PB][QS][RW][4][64];
 
     const int tid = threadIdx.x;
     const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -741,7 +747,6 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
         typename W::vec8 kf[W::QCH], vf[W::QCH];  // stationary K (dV waves) or V (dK waves)
         if constexpr (!DK) W::load_rows(kf, k + kvhead * D, ROPE ? table : nullptr, kw0, N, n, hh);
         if constexpr (DK) W::load_rows(vf, v + kvhead * D, nullptr, kw0, N, n, hh);
-        f32x4* pex = &p_lds[qg][wave % RW][0][lane];  // this pair's P, this lane's slots
         f32x16 acc[W::DBLK];  // dK^T (DK) or dV^T
 #pragma unroll
         for (int i = 0; i < W::DBLK; ++i) acc[i] = f32x16{};
@@ -769,6 +774,7 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 // queries q0 + 32qb .. +31 (lane column = key)
+                f32x4* pex = &p_lds[qb % PB][qg][wave % RW][0][lane];  // this pair's P, this lane's
                 f32x16 x, dp{};  // dp: dK waves only
                 u32x4 y[2];
                 if (work) {
@@ -802,9 +808,10 @@ __global__ __launch_bounds__(128 * RW * QS, RW * QS == 2 ? 2 : 1) void attn_bwd_
                     }
                     W::pv(acc, DK ? Qs : dOs, 32 * qb, y, lane);  // dK^T += Q^T dS, dV^T += dO^T P
                 }
-                // the dK wave has read this P before the next block's is written
-                // (after the last block, the next round's barrier does it)
-                if (qb == 0) __syncthreads();
+                // with one buffer, the dK wave has read this P before the next
+                // block's is written (after the last block, and with two
+                // buffers, the next round's barrier does it)
+                if (PB == 1 && qb == 0) __syncthreads();
             }
         }
         if constexpr (QS > 1) {

@@ -250,8 +250,19 @@ struct Wave {
     // lane's elements d = 32i + 8gq + 4hh + (0..3). With `table`, the pairs
     // are first turned back by the row's position, R(-p):
     //   x0 = y0 c + y1 s,  x1 = y1 c - y0 s.
+    // The table entries are all loaded before the first store: the output and
+    // the table never overlap, but the compiler cannot know it and would wait
+    // for each load after the previous store.
     __device__ __forceinline__ static void write(const f32x16 (&acc)[DBLK], float scale,
                                                  uint16_t* orow, const float* trow, int hh) {
+        f32x4 tab[DBLK][4];
+        if (trow) {
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    tab[i][gq] = *reinterpret_cast<const f32x4*>(trow + 32 * i + 8 * gq + 4 * hh);
+        }
 #pragma unroll
         for (int i = 0; i < DBLK; ++i)
 #pragma unroll
@@ -261,7 +272,7 @@ struct Wave {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) y[t] = acc[i][4 * gq + t] * scale;
                 if (trow) {
-                    const f32x4 cs = *reinterpret_cast<const f32x4*>(trow + d0);
+                    const f32x4 cs = tab[i][gq];
 #pragma unroll
                     for (int pr = 0; pr < 2; ++pr) {
                         const float c = cs[2 * pr], s = cs[2 * pr + 1];

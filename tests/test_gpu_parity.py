@@ -10,6 +10,8 @@ each other crossover family) in the launch configuration the bench times,
 checked on sampled rows the oracle computes one by one, with the three paths
 and the dispatcher bit-identical.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -477,6 +479,43 @@ def test_full_size_sampled_rows(name):
     assert_lse(gl, rl, name + " LSE")
     mx, rel = o_errors(got, ro)
     print("%s: rows=%d max|dO|=%.3e relL2=%.3e" % (name, got.shape[0], mx, rel), flush=True)
+
+
+def test_longest_sequence_sampled_rows():
+    """N = RAC_MAX_N (2^22), the longest sequence the library accepts, for one
+    fp16 D = 64 head: the fused and pre-rotation paths agree bit for bit and
+    match the oracle on rows at the start, around tile edges, in the middle
+    and at the end (positions up to 2^22 - 1: the table's largest angles, the
+    last key tiles' buffer descriptors, 32768 query tiles in the tile
+    launch). About 3 s of GPU work per path and ~8 GiB of host memory for
+    the oracle's fp64 copies."""
+    B, H, N, D, dt, base = 1, 1, rac.RAC_MAX_N, 64, "fp16", 10000.0
+    t0 = time.time()
+    print("longest-sequence case: N=%d" % N, flush=True)
+    (q, k, v), (qd, kd, vd) = _inputs(B, H, H, N, D, dt, key=(111,))
+    of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    op, lp = rac.prerotate_path(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    print("  GPU paths done at %.1f s" % (time.time() - t0), flush=True)
+    assert torch.equal(of, op) and torch.equal(lf, lp)
+    del op, lp, qd, kd, vd
+    og, lg = to_f64(of), to_f64(lf)
+    del of, lf
+    rng = np.random.default_rng(111)
+    rows = sampled_rows(B, H, N, rng, per_head=6)
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    del q, k, v
+    ref = oracle_rows(qb, kb, vb, dt, base, H, H, rows, "rounded")
+    print("  oracle done at %.1f s" % (time.time() - t0), flush=True)
+    got = np.concatenate([og[b, h, r] for (b, h), r in rows.items()])
+    gl = np.concatenate([lg[b, h, r] for (b, h), r in rows.items()])
+    ro = np.concatenate([ref[bh][0] for bh in rows])
+    rl = np.concatenate([ref[bh][1] for bh in rows])
+    assert_o(got, ro, "N = RAC_MAX_N vs rounded-rotation oracle")
+    assert_lse(gl, rl, "N = RAC_MAX_N LSE")
+    mx, rel = o_errors(got, ro)
+    print("  rows=%d max|dO|=%.3e relL2=%.3e" % (got.shape[0], mx, rel), flush=True)
+    rac.release_tables()  # the 1 GiB table is not kept for the later tests
 
 
 def test_kernel_timer_times_one_launch():

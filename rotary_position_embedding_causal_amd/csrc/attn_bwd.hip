@@ -88,12 +88,12 @@ __device__ __forceinline__ int swz(int row) {
 constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw (unformatted) 32-bit data
 
 // Buffer descriptor of rows t*BT .. N-1 of a [N][row_elems] tensor; rows past
-// N read as zeros.
+// N read as zeros (a tile at or past the end: a record count of zero).
 template <typename E>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const E* base, int row_elems, int t,
                                                             int N) {
     const int64_t r0 = (int64_t)t * BT;
-    const int64_t bytes = (N - r0) * row_elems * (int64_t)sizeof(E);
+    const int64_t bytes = (N > r0 ? N - r0 : 0) * row_elems * (int64_t)sizeof(E);
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + r0 * row_elems), 0,
                                              (int)min(bytes, (int64_t)0x7fffffff),
                                              BUF_RSRC_FLAGS);

@@ -121,7 +121,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Buffer descriptors of one key tile: K, V and (RoPE) cos/sin rows starting
 // at the tile's first key. The descriptor's record count ends at the sequence
 // end, so rows past it read as zeros (their scores are masked by causality and
-// their probabilities are zero) without any per-lane clamping.
+// their probabilities are zero) without any per-lane clamping. A tile that
+// starts at or past the end (the second 64-row half of a query tile of fewer
+// than 65 rows, staged like a key tile) gets a record count of zero: every
+// row reads as zero and nothing past the tensor is touched.
 constexpr int BUF_RSRC_FLAGS = 0x00020000;  // raw (unformatted) 32-bit data
 struct TileRsrc {
     __amdgpu_buffer_rsrc_t k, v, t;
@@ -130,7 +133,7 @@ template <int D>
 __device__ __forceinline__ TileRsrc tile_rsrc(const uint16_t* kbase, const uint16_t* vbase,
                                               const float* table, int t, int N) {
     const int k0 = t * BN;
-    const int64_t rows = N - k0;
+    const int64_t rows = N > k0 ? N - k0 : 0;
     const int kv_bytes = (int)min(rows * D * 2, (int64_t)0x7fffffff);
     const int tab_bytes = (int)min(rows * D * 4, (int64_t)0x7fffffff);
     TileRsrc r;

@@ -305,6 +305,23 @@ def test_half_split_backward_full_length_one_group():
     assert_grad(to_f64(dv[:, g:g + 1]), rdv, "%s half dv" % name)
 
 
+def test_largest_batch_short_sequences():
+    """B = 65535 (the largest batch accepted), GQA 2:1, N = 3: the dQ pass's
+    131070 and the dK/dV pass's 65535 work units, both paths against the
+    oracle's gradients."""
+    B, Hq, Hkv, N, D, dt, base = 65535, 2, 1, 3, 64, "bf16", 10000.0
+    (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (402,))
+    res = {"fused": rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base),
+           "prerotate": rac.prerotate_path_bwd(qd, kd, vd, o, lse, dod, base)}
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rdelta, _ = oracle.rope_attention_bwd(
+        inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), dt, base, "rounded")
+    for path, (dq, dk, dv, delta) in res.items():
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad(to_f64(got), ref, "%s %s at B = 65535" % (path, name))
+        assert_grad(delta.cpu().double().numpy(), rdelta, "%s delta at B = 65535" % path)
+
+
 def test_empty_inputs():
     for shape in ((0, 2, 8, 64), (1, 2, 0, 64)):
         x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)

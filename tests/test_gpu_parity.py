@@ -518,6 +518,44 @@ def test_longest_sequence_sampled_rows():
     rac.release_tables()  # the 1 GiB table is not kept for the later tests
 
 
+def test_largest_batch_short_sequences():
+    """B = 65535 (the largest batch accepted) with two query heads sharing one
+    key/value head and N = 3: 131070 single-tile work units, the most the
+    launch grid takes at this N, and every query tile's staged second half
+    (rows 64-127) lying past the sequence end. The three paths give the same
+    bits and O matches the oracle. A one-key row's LSE is its single score,
+    so a rotated operand that rounds to the other neighbour (reading 11)
+    enters it unaveraged, and among 131070 such rows some do: the LSE is
+    checked on the attention arithmetic alone (attn_causal_fwd on the
+    oracle's own rounded rotation) and the pass's rotation against the
+    oracle's on every element."""
+    B, Hq, Hkv, N, D, dt, base = 65535, 2, 1, 3, 64, "bf16", 10000.0
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(113,))
+    outs = {"fused": rac.attn_rope_causal_fwd(qd, kd, vd, base),
+            "prerotate": rac.prerotate_path(qd, kd, vd, base),
+            "split": rac.split_path(qd, kd, vd, base)}
+    qr, kr = rac.rope_prerotate(qd, kd, base)
+    torch.cuda.synchronize()
+    of, lf = outs["fused"]
+    for path, (o, l) in outs.items():
+        assert torch.equal(o, of) and torch.equal(l, lf), path
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    ro, _, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="rounded")
+    assert_o(to_f64(of), ro, "fused at B = 65535")
+    _check_rotation(bits(qr), qb, np.arange(N), dt, base)
+    _check_rotation(bits(kr), kb, np.arange(N), dt, base)
+    qr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(qb, dt), base), dt)
+    kr_bits = oracle.encode(oracle.rope_bhnd(oracle.decode(kb, dt), base), dt)
+    tdt = inputs.TORCH_DTYPES[dt]
+    o2, l2 = rac.attn_causal_fwd(torch.from_numpy(qr_bits.view(np.int16)).view(tdt).to(DEV),
+                                 torch.from_numpy(kr_bits.view(np.int16)).view(tdt).to(DEV), vd)
+    torch.cuda.synchronize()
+    ro2, rl2 = oracle.attention(oracle.decode(qr_bits, dt), oracle.decode(kr_bits, dt),
+                                oracle.decode(vb, dt))
+    assert_o(to_f64(o2), ro2, "attn_causal_fwd at B = 65535")
+    assert_lse(to_f64(l2), rl2, "attn_causal_fwd LSE at B = 65535")
+
+
 def test_kernel_timer_times_one_launch():
     """rac_time_next_kernel: the armed launch records the events (a positive
     kernel time), computes the same bits as an untimed launch, and disarms

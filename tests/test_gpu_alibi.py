@@ -12,7 +12,7 @@ import torch
 import oracle
 import rotary_position_embedding_causal_amd as rac
 from rotary_position_embedding_causal_amd import inputs
-from parity import assert_lse, assert_o, oracle_rows, sampled_rows, to_f64
+from parity import assert_grad, assert_lse, assert_o, oracle_rows, sampled_rows, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,35 @@ def test_alibi_full_size_sampled_rows():
     gl = np.concatenate([lg[b, h, r] for (b, h), r in rows.items()])
     assert_o(got, ro, name + " alibi")
     assert_lse(gl, rl, name + " alibi LSE")
+
+
+def test_alibi_largest_batch_short_sequences():
+    """B = 65535 (the largest batch accepted), GQA 2:1, N = 3, D = 128: ALiBi
+    alone (O and LSE against the oracle) and after RoPE of either pairing (O
+    against the oracle; a one-key row's LSE would carry a rotated operand's
+    rounding unaveraged), and the backward without RoPE against the
+    oracle's gradients."""
+    B, Hq, Hkv, N, D, dt, base = 65535, 2, 1, 3, 128, "bf16", 10000.0
+    q, k, v = inputs.qkv(B, Hq, Hkv, N, D, dt, key=(430,))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    slopes = geometric_slopes(Hq)
+    for pairing in ("none", "adjacent", "half"):
+        o, l = _run(qd, kd, vd, slopes, base, pairing)
+        torch.cuda.synchronize()
+        ro, rl, _, _ = _oracle(q, k, v, dt, base, pairing, slopes)
+        assert_o(to_f64(o), ro, "alibi %s at B = 65535" % pairing)
+        if pairing == "none":
+            assert_lse(to_f64(l), rl, "alibi LSE at B = 65535")
+    o, l = _run(qd, kd, vd, slopes, base, "none")
+    do = inputs.draw((B, Hq, N, D), dt, (430,), 3)
+    dq, dk, dv, _ = rac.attn_alibi_causal_bwd(qd, kd, vd, o, l, do.to(DEV),
+                                              torch.from_numpy(slopes).to(DEV))
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _, _ = oracle.rope_attention_bwd(
+        inputs.bits(q), inputs.bits(k), inputs.bits(v), inputs.bits(do), dt, None,
+        slopes=slopes.astype(np.float64))
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad(to_f64(got), ref, "alibi %s at B = 65535" % name)
 
 
 def test_alibi_empty_inputs():

@@ -11,7 +11,8 @@ import torch
 import oracle
 import rotary_position_embedding_causal_amd as rac
 from rotary_position_embedding_causal_amd import inputs
-from parity import assert_lse, assert_o, bits, o_errors, oracle_rows, sampled_rows, to_f64
+from parity import (assert_grad, assert_lse, assert_o, bits, o_errors, oracle_rows, sampled_rows,
+                    to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,6 +174,32 @@ def test_half_full_size_sampled_rows():
     gl = np.concatenate([lg[b, h, r] for (b, h), r in rows.items()])
     assert_o(got, np.concatenate([ref[bh][0] for bh in rows]), name + " half")
     assert_lse(gl, np.concatenate([ref[bh][1] for bh in rows]), name + " half LSE")
+
+
+def test_half_largest_batch_short_sequences():
+    """B = 65535 (the largest batch accepted), GQA 2:1, N = 3, D = 128, fp16:
+    the half-split fused kernel and pre-rotation path give the same bits and
+    O matches the oracle; the backward of both paths against the oracle's
+    gradients."""
+    B, Hq, Hkv, N, D, dt, base = 65535, 2, 1, 3, 128, "fp16", 10000.0
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(330,))
+    of, lf = rac.attn_rope_causal_fwd_ex(qd, kd, vd, base, "half")
+    op, lp = rac.prerotate_path(qd, kd, vd, base, pairing="half")
+    torch.cuda.synchronize()
+    assert torch.equal(of, op) and torch.equal(lf, lp)
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    ro, _, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="rounded", pairing="half")
+    assert_o(to_f64(of), ro, "half at B = 65535")
+    do = inputs.draw((B, Hq, N, D), dt, (330,), 3)
+    dod = do.to(DEV)
+    res = {"fused": rac.attn_rope_causal_bwd_ex(qd, kd, vd, of, lf, dod, base, "half"),
+           "prerotate": rac.prerotate_path_bwd(qd, kd, vd, of, lf, dod, base, "half")}
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _, _ = oracle.rope_attention_bwd(qb, kb, vb, inputs.bits(do), dt, base,
+                                                    "rounded", pairing="half")
+    for path, (dq, dk, dv, _) in res.items():
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad(to_f64(got), ref, "half %s %s at B = 65535" % (path, name))
 
 
 def test_half_empty_inputs():

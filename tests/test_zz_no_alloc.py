@@ -1,9 +1,10 @@
 """attn_rope_causal_fwd_noalloc, the entry point for callers that cannot
 allocate device memory, against attn_rope_causal_fwd (the entry point it is a
-variant of): two calls in a row through the C ABI into preallocated outputs,
-the second with a smaller input and another rope_base (its table rows are
-rebuilt in the static array), to the parity bounds (O max-abs 2e-2, rel-L2
-1e-2; LSE 1e-3)."""
+variant of): four calls in a row through the C ABI into preallocated outputs,
+each with a smaller input than the one before -- the first two fill the
+static table to its capacity, at D = 64 and D = 128 -- and the rope_base
+changing along the way (each call rebuilds its table rows in the static
+array), to the parity bounds (O max-abs 2e-2, rel-L2 1e-2; LSE 1e-3)."""
 import ctypes
 
 import numpy as np
@@ -33,7 +34,10 @@ def _noalloc(q, k, v, out, lse, base, stream):
 
 def test_noalloc_matches_fused_two_calls():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
-    cases = [  # (B, Hq, Hkv, N, D, dtype, base, key): the second call smaller
+    cases = [  # (B, Hq, Hkv, N, D, dtype, base, key): each call smaller than the one before
+        # the static table's full capacity: N * D = RAC_NOALLOC_MAX_N * 128 at D = 64 and 128
+        (1, 1, 1, 2 * rac.RAC_NOALLOC_MAX_N, 64, "fp16", 10000.0, (503,)),
+        (1, 2, 1, rac.RAC_NOALLOC_MAX_N, 128, "bf16", 500000.0, (504,)),
         (1, 32, 8, 2048, 128, "bf16", 500000.0, (501,)),
         (2, 4, 2, 300, 64, "fp16", 10000.0, (502,)),
     ]

@@ -17,7 +17,7 @@ import torch
 import oracle
 import rotary_position_embedding_causal_amd as rac
 from rotary_position_embedding_causal_amd import inputs
-from parity import assert_grad, bits, to_f64
+from parity import assert_grad, assert_o, bits, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -320,6 +320,27 @@ def test_largest_batch_short_sequences():
         for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
             assert_grad(to_f64(got), ref, "%s %s at B = 65535" % (path, name))
         assert_grad(delta.cpu().double().numpy(), rdelta, "%s delta at B = 65535" % path)
+
+
+def test_most_query_heads_in_one_group():
+    """Hq = 65535 (the most query heads accepted) sharing one key/value head,
+    N = 3: a GQA group of 65535 heads, odd, so neither pass splits it; the
+    dK/dV pass walks all of them for its one key tile. The forward's O and
+    both backwards against the oracle."""
+    B, Hq, Hkv, N, D, dt, base = 1, 65535, 1, 3, 64, "bf16", 10000.0
+    (q, k, v, do), (qd, kd, vd, dod, o, lse) = _case(B, Hq, Hkv, N, D, dt, base, (403,))
+    res = {"fused": rac.attn_rope_causal_bwd(qd, kd, vd, o, lse, dod, base),
+           "prerotate": rac.prerotate_path_bwd(qd, kd, vd, o, lse, dod, base)}
+    torch.cuda.synchronize()
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    ro, _, _, _ = oracle.rope_attention(qb, kb, vb, dt, base, variant="rounded")
+    assert_o(to_f64(o), ro, "forward with Hq = 65535")
+    rdq, rdk, rdv, rdelta, _ = oracle.rope_attention_bwd(qb, kb, vb, inputs.bits(do), dt, base,
+                                                         "rounded")
+    for path, (dq, dk, dv, delta) in res.items():
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad(to_f64(got), ref, "%s %s with Hq = 65535" % (path, name))
+        assert_grad(delta.cpu().double().numpy(), rdelta, "%s delta with Hq = 65535" % path)
 
 
 def test_empty_inputs():

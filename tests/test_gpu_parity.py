@@ -236,6 +236,29 @@ def test_dispatcher_matches_fused(shape):
     assert_lse(to_f64(lf), rl, "auto")
 
 
+def test_dispatcher_beyond_the_pass_grid():
+    """B = 65535 with eight query heads per key/value head: B * (Hq + Hkv) =
+    589815 heads exceed the streaming pass's grid (8 * 65535), so with any
+    workspace the dispatcher must not take the pre-rotation path; B * Hkv fits,
+    so the split path remains. Every workspace size gives the fused kernel's
+    bits, and those match the oracle's O."""
+    B, Hq, Hkv, N, D, dt, base = 65535, 8, 1, 2, 64, "bf16", 10000.0
+    assert B * (Hq + Hkv) > 8 * 65535 >= B * Hkv
+    (q, k, v), (qd, kd, vd) = _inputs(B, Hq, Hkv, N, D, dt, key=(114,))
+    of, lf = rac.attn_rope_causal_fwd(qd, kd, vd, base)
+    torch.cuda.synchronize()
+    for wbytes in (None, B * Hkv * N * D * 2, B * (Hq + Hkv) * N * D * 2 + 4096):
+        path = rac.auto_plan(B, Hq, Hkv, N, D, qd.dtype, wbytes or 0)[0]
+        assert path != rac.RAC_PATH_PREROTATE, wbytes
+        ws = None if wbytes is None else torch.empty(wbytes, dtype=torch.uint8, device=DEV)
+        oa, la = rac.attn_rope_causal_auto(qd, kd, vd, base, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, of) and torch.equal(la, lf), rac.PATH_NAMES[path]
+    ro, _, _, _ = oracle.rope_attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), dt, base,
+                                        variant="rounded")
+    assert_o(to_f64(of), ro, "fused at B = 65535, Hq = 8")
+
+
 ODD_N = [1, 2, 3, 17, 63, 64, 65, 127, 129, 300]
 
 

@@ -34,7 +34,7 @@ Also printed in the same JSON line:
     workload (rotation + causal attention), in the same unit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-       [--no-cpu] [--only fused|prerotate|rope|attn|split|rope_k|attn_q
+       [--no-cpu] [--only fused|prerotate|rope|attn|split|rope_k|attn_q|bwd|bwd_prerotate
        [--workload NAME]]
        [--copy-calib]
 """
@@ -224,7 +224,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["fused", "prerotate", "rope", "attn", "split", "rope_k",
-                                       "attn_q"], default=None,
+                                       "attn_q", "bwd", "bwd_prerotate"], default=None,
                     help="time one kernel/path alone (for profiler runs)")
     ap.add_argument("--workload", default=MAIN,
                     help="workload of the --only runs (a name from inputs.WORKLOADS)")
@@ -293,9 +293,20 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     if args.only:
-        fn = {"fused": fused, "rope": rope, "attn": attn,
-              "prerotate": lambda: (rope(), attn()), "rope_k": rope_k, "attn_q": attn_q,
-              "split": lambda: (rope_k(), attn_q())}[args.only]
+        fns = {"fused": fused, "rope": rope, "attn": attn,
+               "prerotate": lambda: (rope(), attn()), "rope_k": rope_k, "attn_q": attn_q,
+               "split": lambda: (rope_k(), attn_q())}
+        if args.only.startswith("bwd"):
+            # the backward of the fused path or of the pre-rotation path, from the
+            # fused forward's out and lse and a seeded dO
+            fused()
+            gen = torch.Generator(device=dev).manual_seed(20260913)
+            dout = torch.randn(qd.shape, generator=gen, device=dev,
+                               dtype=torch.float32).to(qd.dtype)
+            fns["bwd"] = lambda: rac.attn_rope_causal_bwd(qd, kd, vd, out_f, lse_f, dout, base)
+            fns["bwd_prerotate"] = lambda: rac.prerotate_path_bwd(qd, kd, vd, out_f, lse_f, dout,
+                                                                  base)
+        fn = fns[args.only]
         warm(fn, args.warmup, 0.0, torch.cuda.synchronize)  # counter runs: few dispatches
         t0 = time.perf_counter()
         for _ in range(args.steps):

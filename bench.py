@@ -306,6 +306,10 @@ def main():
             fns["bwd"] = lambda: rac.attn_rope_causal_bwd(qd, kd, vd, out_f, lse_f, dout, base)
             fns["bwd_prerotate"] = lambda: rac.prerotate_path_bwd(qd, kd, vd, out_f, lse_f, dout,
                                                                   base)
+        if args.only == "attn":
+            rope()  # the plain kernel reads the rotated operands: write them first
+        if args.only == "attn_q":
+            rope_k()
         fn = fns[args.only]
         warm(fn, args.warmup, 0.0, torch.cuda.synchronize)  # counter runs: few dispatches
         t0 = time.perf_counter()
